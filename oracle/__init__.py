@@ -1,0 +1,12 @@
+"""CPU fp64 oracle (test infrastructure; never imported by the product path)."""
+from .attention import (  # noqa: F401
+    CacheModel,
+    attend_row,
+    brute,
+    chunked,
+    decode_cached,
+    decode_recompute,
+    kv_bytes,
+    kv_head_of,
+    naive_causal,
+)

@@ -1,0 +1,175 @@
+"""Seeded synthetic inputs for the KV-cached causal attention workloads.
+
+This module is the one piece shared by the CPU oracle side (``oracle/``, the
+tests) and the GPU side (the tests, ``bench.py``, the smoke check).  It holds
+none of the attention arithmetic: it only draws i.i.d. N(0, 1) samples, rounds
+them to the storage dtype with round-to-nearest-even, picks the heavy key rows
+and the ragged sequence lengths, and describes the workload shapes.
+
+Seeding: every tensor comes from its own ``numpy.random.Generator`` built from
+``SeedSequence(BASE_SEED, spawn_key=(cfg, layer, step + 1, tensor, *extra))``.
+``step = -1`` is the prompt / cache history, ``step = s >= 0`` is decode step
+``s``.  Samples are drawn as float64 in C order of the logical shape and then
+rounded: float32 by IEEE RNE, float16 by numpy's RNE cast, bfloat16 by RNE on
+the float32 bit pattern.  bfloat16 arrays are carried as ``uint16`` bit
+patterns, so that the exact bits can be uploaded to the device unchanged.
+
+Workload shapes follow the pages' workloads: the 8-layer, 512-wide, 16-head
+model of the llm-perf-lab README (KV-cache and attention tables), the
+B=4, H=12, T=2048, D=64 shape of the naive-vs-SDPA comparison (roadmap page,
+project 15) and the 32-layer, D=128, 4096-token capacity example of the
+inference chapter (section 9.3).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+BASE_SEED = 0x6B76_6361  # fixed base of every seed sequence
+
+# tensor ids inside the spawn key
+Q, K, V, HEAVY, LENGTHS = 0, 1, 2, 3, 4
+
+DTYPES = ("f32", "f16", "bf16")
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+
+
+def generator(cfg: int, layer: int, step: int, tensor: int, *extra: int) -> np.random.Generator:
+    """Independent generator for one (config, layer, step, tensor[, extra]) stream."""
+    if step < -1:
+        raise ValueError("step must be >= -1")
+    key = (int(cfg), int(layer), int(step) + 1, int(tensor)) + tuple(int(e) for e in extra)
+    if min(key) < 0:
+        raise ValueError("spawn key entries must be non-negative")
+    return np.random.default_rng(np.random.SeedSequence(BASE_SEED, spawn_key=key))
+
+
+def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (RNE on the bit pattern); returns uint16 bits."""
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    bits = x32.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    rounded = ((bits + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(x32)
+    if nan.any():
+        rounded[nan] = 0x7FC0
+    return rounded
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64/float32 values to the storage dtype (RNE)."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32)
+    if dtype == "f16":
+        return np.asarray(x, dtype=np.float64).astype(np.float16)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of storage values to float64."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a).astype(np.float64)
+
+
+def normal(cfg: int, layer: int, step: int, tensor: int, shape, dtype: str, *extra: int) -> np.ndarray:
+    """i.i.d. N(0,1) tensor of ``shape``, rounded to ``dtype`` storage."""
+    g = generator(cfg, layer, step, tensor, *extra)
+    x = g.standard_normal(size=tuple(shape), dtype=np.float64)
+    return round_to(x, dtype)
+
+
+def heavy_count(n: int, frac: float = 0.01) -> int:
+    """Number of heavy rows among n positions: frac*n rounded half up."""
+    return int(math.floor(frac * n + 0.5))
+
+
+def heavy_rows(cfg: int, layer: int, step: int, b: int, h: int, n: int, frac: float = 0.01) -> np.ndarray:
+    """Sorted positions (out of n) of the K rows that are scaled by 8."""
+    g = generator(cfg, layer, step, HEAVY, b, h)
+    c = heavy_count(n, frac)
+    return np.sort(g.choice(n, size=c, replace=False)).astype(np.int64)
+
+
+def scale_rows(a: np.ndarray, rows: np.ndarray, factor: float, dtype: str) -> np.ndarray:
+    """Multiply whole rows (last axis = D) of a 2-D storage array by a power of two.
+
+    Scaling by 8 is exact in binary floating point for these magnitudes, so the
+    re-rounding below returns the exact product.
+    """
+    out = a.copy()
+    if len(rows):
+        x = to_f64(out[rows], dtype) * factor
+        out[rows] = round_to(x, dtype)
+    return out
+
+
+def ragged_lengths(cfg: int, batch: int, lo: int, hi: int) -> np.ndarray:
+    """Per-sequence context lengths drawn uniformly from the inclusive range [lo, hi]."""
+    g = generator(cfg, 0, -1, LENGTHS)
+    return g.integers(lo, hi, size=batch, endpoint=True).astype(np.int64)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shape and dtype of one workload (one attention layer stack)."""
+
+    cfg: int
+    name: str
+    dtype: str
+    layers: int
+    batch: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    prompt: int            # prefill length T (0: no prefill, cache is filled directly)
+    steps: int             # decode steps after the prompt
+    max_T: int             # cache capacity
+    ctx_lo: int = 0        # ragged decode contexts (keys attended, incl. the appended row)
+    ctx_hi: int = 0
+    heavy_frac: float = 0.0
+    extra_prefill_T: int = 0   # a separate B=1 prefill at this length
+    extra_prefill_batch: int = 1
+    note: str = field(default="", compare=False)
+
+    @property
+    def group(self) -> int:
+        return self.q_heads // self.kv_heads
+
+    @property
+    def scale(self) -> float:
+        """Softmax scale 1/sqrt(D) as the float32 value passed across the C ABI."""
+        return float(np.float32(1.0 / math.sqrt(self.head_dim)))
+
+
+WORKLOADS = {
+    1: Workload(1, "c1_f32_mha_b1h4d64_t128", "f32", 1, 1, 4, 4, 64, 128, 32, 160,
+                note="correctness case: prefill 128 then 32 decode steps"),
+    2: Workload(2, "c2_f16_mha_b4h12d64_t2048", "f16", 1, 4, 12, 12, 64, 2048, 128, 2176,
+                note="naive-vs-SDPA shape with 128 decode steps"),
+    3: Workload(3, "c3_f16_8l_b1h16d32_t4096", "f16", 8, 1, 16, 16, 32, 4096, 128, 4224,
+                extra_prefill_T=8192,
+                note="8L x 512d, 16-head model: prompt 4096 + 128 steps; separate prefill at 8192"),
+    4: Workload(4, "c4_bf16_gqa32x8_32l_b16_ctx4096", "bf16", 32, 16, 32, 8, 128, 0, 1, 4096,
+                ctx_lo=4096, ctx_hi=4096,
+                note="GQA decode, every sequence at context 4096"),
+    5: Workload(5, "c5_f16_mha32_32l_b32_ragged", "f16", 32, 32, 32, 32, 128, 0, 1, 4096,
+                ctx_lo=512, ctx_hi=4096, heavy_frac=0.01, extra_prefill_T=8192,
+                note="ragged batch-32 decode with 1% heavy keys; separate B=1 prefill at 8192"),
+}
+
+
+def decode_contexts(w: Workload) -> np.ndarray:
+    """Keys attended by each sequence's decode query (after its own append)."""
+    if w.ctx_lo == w.ctx_hi:
+        return np.full(w.batch, w.ctx_hi, dtype=np.int64)
+    return ragged_lengths(w.cfg, w.batch, w.ctx_lo, w.ctx_hi)

@@ -1,0 +1,250 @@
+"""Pins of the CPU oracle against facts outside the oracle itself.
+
+Each ``check_*`` takes the functions under test as arguments (defaulting to the
+oracle's own), so that ``test_oracle_mutations.py`` can plant plausible
+mistakes in copies of the oracle and show that some pin catches each one.
+
+What the pins rest on:
+* the inference chapter's worked KV-bytes example (section 9.3), stored in
+  ``tests/golden/kv_bytes_worked_example.json``;
+* closed forms: row 0 of causal attention is v_0 exactly; a zero query (or
+  identical keys) gives the running mean of V; a two-key row is a logistic
+  blend; V = 1 gives outputs of exactly 1 (rows sum to one);
+* brute force: pure-Python ``math.fsum`` loops on tiny shapes;
+* a library routine: PyTorch's CPU float64 scaled_dot_product_attention with
+  is_causal (square prefill only, where its top-left mask coincides);
+* invariants the pages state: chunked == naive for any chunk size (README
+  correctness notes), cached == uncached (README, chapter 9.3), and the
+  structural facts that GQA equals MHA on repeated K/V heads (roadmap project
+  12), that future keys never change a row, and that decode is invariant
+  under permutations of the cached keys.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+from synth_inputs import round_to, to_f64
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _to_lists(a):
+    return a.tolist()
+
+
+# ---------------------------------------------------------------- capacity
+def check_kv_bytes(kv_bytes=oracle.kv_bytes):
+    with open(os.path.join(GOLDEN, "kv_bytes_worked_example.json")) as f:
+        gold = json.load(f)
+    for c in gold["cases"]:
+        got = kv_bytes(c["layers"], c["kv_heads"], c["head_dim"], c["seq_len"],
+                       c["bytes_per_elem"], c["batch"])
+        assert got == c["exact_bytes"], (c, got)
+    # linear in every factor: doubling T or batch doubles the bytes
+    base = kv_bytes(2, 3, 4, 5, 2, 1)
+    assert kv_bytes(2, 3, 4, 10, 2, 1) == 2 * base
+    assert kv_bytes(2, 3, 4, 5, 2, 3) == 3 * base
+    assert kv_bytes(1, 1, 1, 1, 1, 1) == 2
+
+
+# ---------------------------------------------------------------- prefill
+TINY_SHAPES = [  # (B, H, Hkv, T, D)
+    (1, 1, 1, 1, 1), (1, 1, 1, 2, 3), (1, 2, 1, 5, 4), (2, 4, 2, 9, 5),
+    (2, 4, 4, 7, 2), (1, 4, 1, 8, 5), (2, 2, 2, 3, 1),
+]
+
+
+def check_brute(naive=oracle.naive_causal):
+    for n, (B, H, Hkv, T, D) in enumerate(TINY_SHAPES):
+        q = _rand((B, H, T, D), 100 + n)
+        k = _rand((B, Hkv, T, D), 200 + n)
+        v = _rand((B, Hkv, T, D), 300 + n)
+        scale = 1.0 / math.sqrt(D)
+        got = naive(q, k, v, scale)
+        ref = np.array(oracle.brute(_to_lists(q), _to_lists(k), _to_lists(v), scale))
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def check_row0_is_v0(naive=oracle.naive_causal):
+    q = _rand((2, 4, 6, 8), 1)
+    k = _rand((2, 2, 6, 8), 2)
+    v = _rand((2, 2, 6, 8), 3)
+    o = naive(q, k, v, 0.35)
+    for h in range(4):
+        assert np.array_equal(o[:, h, 0], v[:, h // 2, 0]), "row 0 must equal v_0 exactly"
+
+
+def check_zero_query_prefix_mean(naive=oracle.naive_causal):
+    B, H, T, D = 2, 3, 11, 6
+    q = np.zeros((B, H, T, D))
+    k = _rand((B, H, T, D), 4)
+    v = _rand((B, H, T, D), 5)
+    o = naive(q, k, v, 0.5)
+    mean = np.cumsum(v, axis=2) / np.arange(1, T + 1)[None, None, :, None]
+    np.testing.assert_allclose(o, mean, rtol=1e-13, atol=1e-13)
+    # identical keys give the same uniform weights whatever the query
+    k_same = np.broadcast_to(_rand((B, H, 1, D), 6), (B, H, T, D)).copy()
+    o2 = naive(_rand((B, H, T, D), 7), k_same, v, 0.5)
+    np.testing.assert_allclose(o2, mean, rtol=1e-13, atol=1e-13)
+
+
+def check_two_key_logistic(naive=oracle.naive_causal):
+    B, H, T, D = 1, 2, 2, 4
+    q = _rand((B, H, T, D), 8)
+    k = _rand((B, H, T, D), 9)
+    v = _rand((B, H, T, D), 10)
+    scale = 0.7
+    o = naive(q, k, v, scale)
+    for h in range(H):
+        s0 = scale * float(np.dot(q[0, h, 1], k[0, h, 0]))
+        s1 = scale * float(np.dot(q[0, h, 1], k[0, h, 1]))
+        p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        ref = p0 * v[0, h, 0] + (1.0 - p0) * v[0, h, 1]
+        np.testing.assert_allclose(o[0, h, 1], ref, rtol=1e-13, atol=1e-13)
+
+
+def check_rows_sum_to_one(naive=oracle.naive_causal):
+    # with V = 1 every output element is the row's probability sum
+    q = _rand((2, 4, 13, 5), 11, 3.0)
+    k = _rand((2, 2, 13, 5), 12, 3.0)
+    o = naive(q, k, np.ones((2, 2, 13, 5)), 0.9)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-13)
+
+
+def check_large_scores(naive=oracle.naive_causal):
+    # scores near +-1000 overflow exp() unless the row max is subtracted
+    D = 4
+    q = np.zeros((1, 1, 2, D)); q[0, 0, :, 0] = 100.0
+    k = np.zeros((1, 1, 2, D)); k[0, 0, 0, 0] = 10.0; k[0, 0, 1, 0] = 9.9
+    v = _rand((1, 1, 2, D), 13)
+    o = naive(q, k, v, 1.0)
+    assert np.isfinite(o).all()
+    p0 = 1.0 / (1.0 + math.exp(100.0 * 9.9 - 100.0 * 10.0))
+    np.testing.assert_allclose(o[0, 0, 1], p0 * v[0, 0, 0] + (1 - p0) * v[0, 0, 1], rtol=1e-12)
+
+
+def check_causality(naive=oracle.naive_causal):
+    B, H, Hkv, T, D = 2, 4, 2, 10, 6
+    q = _rand((B, H, T, D), 14)
+    k = _rand((B, Hkv, T, D), 15)
+    v = _rand((B, Hkv, T, D), 16)
+    o = naive(q, k, v, 0.4)
+    for cut in (0, 3, 8):
+        k2, v2 = k.copy(), v.copy()
+        k2[:, :, cut + 1:] = _rand(k2[:, :, cut + 1:].shape, 17 + cut, 5.0)
+        v2[:, :, cut + 1:] = _rand(v2[:, :, cut + 1:].shape, 27 + cut, 5.0)
+        o2 = naive(q, k2, v2, 0.4)
+        assert np.array_equal(o[:, :, :cut + 1], o2[:, :, :cut + 1]), "a future key changed a row"
+        assert not np.array_equal(o[:, :, cut + 1:], o2[:, :, cut + 1:])
+
+
+def check_gqa_equals_repeated_mha(naive=oracle.naive_causal):
+    B, H, T, D = 2, 8, 9, 4
+    q = _rand((B, H, T, D), 18)
+    for Hkv in (1, 2, 4, 8):
+        k = _rand((B, Hkv, T, D), 19 + Hkv)
+        v = _rand((B, Hkv, T, D), 29 + Hkv)
+        G = H // Hkv
+        o_gqa = naive(q, k, v, 0.5)
+        o_mha = naive(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), 0.5)
+        np.testing.assert_allclose(o_gqa, o_mha, rtol=0, atol=0)
+
+
+def check_torch_sdpa(naive=oracle.naive_causal):
+    import torch
+    import torch.nn.functional as F
+    for n, (B, H, T, D) in enumerate([(1, 2, 16, 8), (2, 3, 33, 16), (1, 1, 64, 32)]):
+        q = _rand((B, H, T, D), 40 + n)
+        k = _rand((B, H, T, D), 50 + n)
+        v = _rand((B, H, T, D), 60 + n)
+        scale = 1.0 / math.sqrt(D)
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k),
+                                             torch.from_numpy(v), is_causal=True, scale=scale).numpy()
+        np.testing.assert_allclose(naive(q, k, v, scale), ref, rtol=1e-11, atol=1e-12)
+
+
+def check_chunked(chunked=oracle.chunked, naive=oracle.naive_causal):
+    B, H, Hkv, T, D = 2, 4, 2, 23, 8
+    q = _rand((B, H, T, D), 70, 2.0)
+    k = _rand((B, Hkv, T, D), 71, 2.0)
+    v = _rand((B, Hkv, T, D), 72)
+    ref = naive(q, k, v, 0.3)
+    for cq in (1, 2, 3, 7, 64, T - 1, T, T + 5):
+        for ck in (1, 2, 3, 7, 64, T - 1, T, T + 5):
+            np.testing.assert_allclose(chunked(q, k, v, 0.3, cq, ck), ref, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- decode
+def check_decode_single_key(attend_row=oracle.attend_row):
+    K = _rand((1, 8), 80)
+    V = _rand((1, 8), 81)
+    assert np.array_equal(attend_row(_rand(8, 82), K, V, 0.3), V[0])
+
+
+def check_decode_permutation(attend_row=oracle.attend_row):
+    L, D = 37, 16
+    K = _rand((L, D), 83, 2.0)
+    V = _rand((L, D), 84)
+    q = _rand(D, 85)
+    perm = np.random.default_rng(86).permutation(L)
+    np.testing.assert_allclose(attend_row(q, K[perm], V[perm], 0.25), attend_row(q, K, V, 0.25),
+                               rtol=1e-13, atol=1e-14)
+
+
+def check_decode_matches_prefill_rows(decode_cached=oracle.decode_cached, naive=oracle.naive_causal):
+    B, H, Hkv, T, D = 2, 4, 2, 12, 8
+    q = _rand((B, H, T, D), 87)
+    k = _rand((B, Hkv, T, D), 88)
+    v = _rand((B, Hkv, T, D), 89)
+    full = naive(q, k, v, 0.35)
+    for p in (0, 5, T - 1):
+        got = decode_cached(q[:, :, p], k, v, np.full(B, p + 1), 0.35)
+        np.testing.assert_allclose(got, full[:, :, p], rtol=1e-12, atol=1e-13)
+
+
+def check_cached_equals_recompute(decode_cached=oracle.decode_cached,
+                                  decode_recompute=oracle.decode_recompute,
+                                  CacheModel=oracle.CacheModel, dtype="f16"):
+    """Token-by-token decode through the cache equals recomputing the whole prefix,
+    bit for bit, at every step, for batch 1 and batch 2, with a rollback in between."""
+    storage = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
+    for B in (1, 2):
+        H, Hkv, D, T, steps = 4, 2, 8, 6, 7
+        max_T = T + steps
+        rng = np.random.default_rng(90 + B)
+        qh = round_to(rng.standard_normal((B, H, max_T, D)), dtype)
+        kh = round_to(rng.standard_normal((B, Hkv, max_T, D)), dtype)
+        vh = round_to(rng.standard_normal((B, Hkv, max_T, D)), dtype)
+        cache = CacheModel(1, B, Hkv, D, max_T, storage)
+        cache.prefill(0, kh[:, :, :T], vh[:, :, :T])
+        for s in range(steps):
+            pos = T + s
+            if s == 3:
+                # roll back two positions (rejected draft tokens) and re-append them
+                cache.set_lengths(0, cache.lengths[0] - 2)
+                for r in (pos - 2, pos - 1):
+                    cache.append(0, kh[:, :, r:r + 1], vh[:, :, r:r + 1])
+            cache.append(0, kh[:, :, pos:pos + 1], vh[:, :, pos:pos + 1])
+            assert (cache.lengths[0] == pos + 1).all()
+            got = decode_cached(to_f64(qh[:, :, pos], dtype), to_f64(cache.k[0], dtype),
+                                to_f64(cache.v[0], dtype), cache.lengths[0], 0.3)
+            ref = decode_recompute(to_f64(qh[:, :, :pos + 1], dtype), to_f64(kh[:, :, :pos + 1], dtype),
+                                   to_f64(vh[:, :, :pos + 1], dtype), 0.3)
+            assert np.array_equal(got, ref), f"cached != recompute at step {s}, B={B}"
+
+
+ALL_CHECKS = [
+    check_kv_bytes, check_brute, check_row0_is_v0, check_zero_query_prefix_mean,
+    check_two_key_logistic, check_rows_sum_to_one, check_large_scores, check_causality,
+    check_gqa_equals_repeated_mha, check_torch_sdpa, check_chunked, check_decode_single_key,
+    check_decode_permutation, check_decode_matches_prefill_rows, check_cached_equals_recompute,
+]
