@@ -1,0 +1,144 @@
+/*
+ * kvattn.h -- C ABI of libkvattn: exact causal softmax attention over a
+ * preallocated per-layer KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For batch entry b, query head h and a query at absolute
+ * position i, over keys j = 0..i (the diagonal included):
+ *     s_ij = scale * <q[b,h,i,:], k[b,g,j,:]>,   g = h / (H / Hkv)
+ *     o[b,h,i,:] = sum_j softmax_j(s_i.) * v[b,g,j,:]
+ * This is the attention of the roadmap page's project 11 (cached self
+ * attention: scores q k^T / sqrt(D), softmax over keys, times V, past K/V
+ * concatenated on the time axis of a (B, H, T, D) layout) with the causal
+ * mask a decoder-only model needs, and the MQA/GQA head sharing of project 12.
+ * The inference chapter (section 9.3) fixes the two phases: prefill
+ * processes the prompt and builds each layer's K/V cache; decode appends one
+ * position and reads the whole cache.  Only K and V are cached.  Section 9.7:
+ * the tiled (flash-style) computation is the same attention up to ordinary
+ * floating-point rounding, and never writes the T x T matrix to memory.
+ *
+ * Layouts (all row-major and contiguous, element type = the cache dtype):
+ *   q, o in prefill      (B, H, T, D)
+ *   k, v in prefill      (B, Hkv, T, D)
+ *   q, o in decode       (B, H, 1, D)
+ *   k_new, v_new         (B, Hkv, 1, D)
+ *   cache, per layer     K then V, each (B, Hkv, max_T, D), inside one device
+ *                        allocation laid out [layer][K|V][B][Hkv][max_T][D]
+ *   lengths              int32 [layer][B] on the device, mirrored on the host
+ * Pointers named q, k, v, o, k_new, v_new, device_buf are DEVICE pointers;
+ * host_lens is a HOST pointer.  `stream` is a hipStream_t (NULL = the null
+ * stream).
+ *
+ * Supported: dtype F32, F16, BF16; head_dim D in {32, 64, 128}; H % Hkv == 0.
+ * Arithmetic: scores, softmax statistics and output accumulation in fp32; for
+ * F16/BF16 the two products run on the matrix cores with fp32 accumulation.
+ *
+ * Ownership.  The caller owns q/k/v/o/k_new/v_new and the stream.  The library
+ * owns the cache object, its length arrays and its split-K workspace; it owns
+ * the cache payload too unless the caller passes `device_buf`, which must then
+ * stay alive until kvattn_cache_free.  A cache object is not thread-safe, and
+ * all work on one cache must be issued on one stream (the split-K workspace is
+ * shared by every layer of the cache).
+ *
+ * Errors.  0 on success, a negative kvattn_status otherwise.  Every argument is
+ * validated on the host before anything is enqueued, so a failed call leaves
+ * the cache and its lengths unchanged.  All calls only enqueue work on
+ * `stream`; none synchronises except kvattn_cache_free.  A kernel fault shows
+ * up as KVATTN_ERR_HIP on a later call.
+ */
+#ifndef KVATTN_H
+#define KVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KVATTN_F32 = 0, KVATTN_F16 = 1, KVATTN_BF16 = 2 } kvattn_dtype;
+
+typedef enum {
+  KVATTN_OK = 0,
+  KVATTN_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad layer index  */
+  KVATTN_ERR_UNSUPPORTED = -2, /* dtype, head_dim not in {32,64,128}, H % Hkv   */
+  KVATTN_ERR_CAPACITY = -3,    /* append on a full sequence; prefill T > max_T  */
+  KVATTN_ERR_STATE = -4,       /* prefill on a non-empty layer; decode at len 0 */
+  KVATTN_ERR_OOM = -5,         /* device allocation failed / buffer too small   */
+  KVATTN_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed    */
+} kvattn_status;
+
+typedef struct kvattn_cache kvattn_cache; /* opaque, library-owned */
+
+/* Cache payload bytes by the inference chapter's capacity formula (section
+ * 9.3): 2 * layers * kv_heads * head_dim * max_T * bytes(dt) * batch.  The 2
+ * counts K and V; lengths and workspace are not included.  Pure host function;
+ * returns 0 for a non-positive argument or an unknown dtype. */
+size_t kvattn_cache_bytes(int layers, int batch, int kv_heads, int head_dim, int max_T,
+                          kvattn_dtype dt);
+
+/* Create a cache of `layers` layers for `batch` sequences of up to `max_T`
+ * positions (the preallocated cache with O(1) append of the llm-perf-lab
+ * README's kv_cache module).  q_heads is H (needed to size the decode
+ * workspace); kv_heads is Hkv.  If device_buf is NULL the library allocates
+ * the payload; otherwise device_buf (>= kvattn_cache_bytes bytes, 256-byte
+ * aligned) is adopted.  All lengths start at 0 (on the device and the host).
+ * Needs a current HIP device; synchronises that device once. */
+int kvattn_cache_alloc(kvattn_cache **out, int layers, int batch, int q_heads, int kv_heads,
+                       int head_dim, int max_T, kvattn_dtype dt, void *device_buf,
+                       size_t device_buf_bytes);
+
+/* Synchronise the device, release what the library allocated and the object. */
+int kvattn_cache_free(kvattn_cache *c);
+
+/* Device addresses of layer `layer`'s K and V blocks, each (B, Hkv, max_T, D). */
+int kvattn_cache_kv_ptr(const kvattn_cache *c, int layer, void **k, void **v);
+
+/* Set the valid lengths of one layer (layer >= 0) or of every layer (-1) to
+ * host_lens[0..B-1], each in [0, max_T].  Truncation and rollback to an
+ * accepted prefix (the README's speculative loop rolls the cache back);
+ * rows at or past a length are never read.  Enqueued on `stream`; host_lens
+ * is copied before the call returns. */
+int kvattn_cache_set_lengths(kvattn_cache *c, int layer, const int32_t *host_lens, void *stream);
+
+/* Copy the host mirror of one layer's lengths into host_lens[0..B-1].  The
+ * mirror is updated at enqueue time, so it already includes enqueued work. */
+int kvattn_cache_get_lengths(const kvattn_cache *c, int layer, int32_t *host_lens);
+
+/* Prefill of one layer (inference chapter 9.1/9.3): causal attention of the T
+ * prompt queries over the T prompt keys, o = attn(q, k, v), and a bit-exact
+ * copy of k, v into cache rows [0, T); the layer's lengths become T.
+ * q (B,H,T,D), k/v (B,Hkv,T,D) in the cache dtype; o (B,H,T,D) in o_dtype,
+ * which is the cache dtype or F32.  Requires every length of the layer to be
+ * 0 (else STATE) and 1 <= T <= max_T (else CAPACITY / INVALID_ARG).  scale is
+ * normally 1/sqrt(D).  No T x T buffer is ever allocated or written. */
+int kvattn_prefill(kvattn_cache *c, int layer, const void *q, const void *k, const void *v,
+                   void *o, int T, float scale, kvattn_dtype o_dtype, void *stream);
+
+/* Append one position per sequence (inference chapter 9.3: decode appends one
+ * position to the cache): k_new/v_new (B,Hkv,1,D) are copied bit-exactly to
+ * row len[b] of sequence b, then len[b] += 1.  CAPACITY if any len[b] ==
+ * max_T. */
+int kvattn_append(kvattn_cache *c, int layer, const void *k_new, const void *v_new, void *stream);
+
+/* Decode of one layer: query q[b,h] (B,H,1,D) sits at position len[b]-1 and
+ * attends all len[b] cached keys of its KV head (the causal mask aligned to
+ * the bottom right); o (B,H,1,D) in o_dtype (cache dtype or F32).  Lengths are
+ * read from device memory, so the call needs no host synchronisation after an
+ * append.  STATE if any len[b] == 0.  Long contexts are split across
+ * workgroups and merged by log-sum-exp; the split depends only on len[b],
+ * never on the batch, so each sequence's output is independent of the
+ * others. */
+int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scale,
+                  kvattn_dtype o_dtype, void *stream);
+
+/* Static description of a status code. */
+const char *kvattn_status_string(int status);
+
+/* Text of the last HIP error this thread's calls saw ("" if none). */
+const char *kvattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVATTN_H */

@@ -1,0 +1,243 @@
+"""Python binding of libkvattn: exact causal KV-cached attention on MI355X.
+
+Argument marshalling only: every step of prefill, append and decode runs in
+the HIP kernels of ``libkvattn.so`` (built in-tree by
+``kv_cached_causal_amd.build``).  PyTorch supplies device memory and the
+stream.  If the library is missing this module raises at import time: there
+is no CPU fallback.
+
+Layouts are the (B, H, T, D) / (B, Hkv, T, D) contiguous tensors of the C ABI
+(see ``include/kvattn.h``).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["KVCache", "KVAttnError", "cache_bytes", "lib", "LIB_PATH"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvattn.so")
+
+_DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_ELEM = {torch.float32: 4, torch.float16: 2, torch.bfloat16: 2}
+
+_STATUS = {
+    0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "STATE", -5: "OOM", -6: "HIP",
+}
+
+# the exported C symbols and their ctypes signatures
+_SIGS = {
+    "kvattn_cache_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5 + [ctypes.c_int]),
+    "kvattn_cache_alloc": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p)] + [ctypes.c_int] * 7
+                           + [ctypes.c_void_p, ctypes.c_size_t]),
+    "kvattn_cache_free": (ctypes.c_int, [ctypes.c_void_p]),
+    "kvattn_cache_kv_ptr": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p)]),
+    "kvattn_cache_set_lengths": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
+                                                ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]),
+    "kvattn_cache_get_lengths": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int32)]),
+    "kvattn_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 4
+                       + [ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "kvattn_append": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]),
+    "kvattn_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "kvattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kvattn_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvattn.so (once) and declare its signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built: run `python -m kv_cached_causal_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+lib()  # fail loudly at import when the native library is absent
+
+
+class KVAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        detail = lib().kvattn_last_error().decode() if status == -6 else ""
+        msg = f"{where}: {_STATUS.get(status, status)} ({lib().kvattn_status_string(status).decode()})"
+        super().__init__(msg + (f" [{detail}]" if detail else ""))
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise KVAttnError(status, where)
+
+
+def cache_bytes(layers: int, batch: int, kv_heads: int, head_dim: int, max_T: int, dtype) -> int:
+    """Cache payload bytes by the capacity formula (computed by the C library)."""
+    return int(lib().kvattn_cache_bytes(layers, batch, kv_heads, head_dim, max_T, _DT[dtype]))
+
+
+def _stream_ptr(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class KVCache:
+    """A preallocated per-layer KV cache on one GPU.
+
+    Device memory for the payload is a PyTorch allocation handed to the C
+    library (``buffer=True``), so that ``k_view``/``v_view`` can expose it as
+    tensors; with ``buffer=False`` the library allocates it with hipMalloc.
+    """
+
+    def __init__(self, layers: int, batch: int, q_heads: int, kv_heads: int, head_dim: int,
+                 max_T: int, dtype=torch.float16, device=None, buffer: bool = True):
+        if dtype not in _DT:
+            raise TypeError(f"unsupported dtype {dtype}")
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.layers, self.batch, self.q_heads, self.kv_heads = layers, batch, q_heads, kv_heads
+        self.head_dim, self.max_T, self.dtype = head_dim, max_T, dtype
+        self.nbytes = cache_bytes(layers, batch, kv_heads, head_dim, max_T, dtype)
+        self._handle = ctypes.c_void_p()
+        self._buf = None
+        with torch.cuda.device(self.device):
+            if buffer:
+                if self.nbytes == 0:
+                    raise KVAttnError(-1, "KVCache")
+                self._buf = torch.empty(self.nbytes, dtype=torch.uint8, device=self.device)
+                torch.cuda.synchronize(self.device)
+                dev_ptr, dev_bytes = _ptr(self._buf), self.nbytes
+            else:
+                dev_ptr, dev_bytes = None, 0
+            _check(lib().kvattn_cache_alloc(ctypes.byref(self._handle), layers, batch, q_heads, kv_heads,
+                                            head_dim, max_T, _DT[dtype], dev_ptr, dev_bytes),
+                   "kvattn_cache_alloc")
+
+    # ------------------------------------------------------------------ views
+    def _layer_ptrs(self, layer: int):
+        k, v = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(lib().kvattn_cache_kv_ptr(self._handle, layer, ctypes.byref(k), ctypes.byref(v)),
+               "kvattn_cache_kv_ptr")
+        return k.value, v.value
+
+    def _view(self, layer: int, which: int) -> torch.Tensor:
+        if self._buf is None:
+            raise RuntimeError("views need a PyTorch-allocated cache buffer")
+        if not 0 <= layer < self.layers:
+            raise IndexError(layer)
+        block = self.nbytes // (2 * self.layers)
+        off = (2 * layer + which) * block
+        t = self._buf[off:off + block].view(self.dtype)
+        return t.view(self.batch, self.kv_heads, self.max_T, self.head_dim)
+
+    def k_view(self, layer: int) -> torch.Tensor:
+        """Layer's K block (B, Hkv, max_T, D) as a tensor over the cache memory."""
+        return self._view(layer, 0)
+
+    def v_view(self, layer: int) -> torch.Tensor:
+        return self._view(layer, 1)
+
+    # ------------------------------------------------------------------ lengths
+    def set_lengths(self, lengths, layer: int = -1) -> None:
+        arr = (ctypes.c_int32 * self.batch)(*[int(x) for x in lengths])
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_cache_set_lengths(self._handle, layer, arr, _stream_ptr(self.device)),
+                   "kvattn_cache_set_lengths")
+
+    def lengths(self, layer: int) -> list:
+        arr = (ctypes.c_int32 * self.batch)()
+        _check(lib().kvattn_cache_get_lengths(self._handle, layer, arr), "kvattn_cache_get_lengths")
+        return list(arr)
+
+    # ------------------------------------------------------------------ checks
+    def _tensor(self, t: torch.Tensor, shape, name: str, dtype=None) -> None:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a tensor")
+        if t.device != self.device:
+            raise ValueError(f"{name} is on {t.device}, cache on {self.device}")
+        if t.dtype != (dtype or self.dtype):
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype or self.dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    def _scale(self, scale):
+        return float(1.0 / math.sqrt(self.head_dim)) if scale is None else float(scale)
+
+    # ------------------------------------------------------------------ the path
+    def prefill(self, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                out: torch.Tensor | None = None, scale: float | None = None, out_dtype=None) -> torch.Tensor:
+        """Causal attention over the prompt; copies k, v into cache rows [0, T)."""
+        B, H, Hkv, D = self.batch, self.q_heads, self.kv_heads, self.head_dim
+        T = q.shape[2] if q.dim() == 4 else -1
+        self._tensor(q, (B, H, T, D), "q")
+        self._tensor(k, (B, Hkv, T, D), "k")
+        self._tensor(v, (B, Hkv, T, D), "v")
+        od = out_dtype or self.dtype
+        if out is None:
+            out = torch.empty((B, H, T, D), dtype=od, device=self.device)
+        self._tensor(out, (B, H, T, D), "out", od)
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_prefill(self._handle, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(out), T,
+                                        self._scale(scale), _DT[od], _stream_ptr(self.device)),
+                   "kvattn_prefill")
+        return out
+
+    def append(self, layer: int, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+        """Copy one K/V row per sequence to position len[b]; len[b] += 1."""
+        shape = (self.batch, self.kv_heads, 1, self.head_dim)
+        self._tensor(k_new, shape, "k_new")
+        self._tensor(v_new, shape, "v_new")
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_append(self._handle, layer, _ptr(k_new), _ptr(v_new), _stream_ptr(self.device)),
+                   "kvattn_append")
+
+    def decode(self, layer: int, q: torch.Tensor, out: torch.Tensor | None = None,
+               scale: float | None = None, out_dtype=None) -> torch.Tensor:
+        """One query per (b, h) over the len[b] cached keys."""
+        shape = (self.batch, self.q_heads, 1, self.head_dim)
+        self._tensor(q, shape, "q")
+        od = out_dtype or self.dtype
+        if out is None:
+            out = torch.empty(shape, dtype=od, device=self.device)
+        self._tensor(out, shape, "out", od)
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_decode(self._handle, layer, _ptr(q), _ptr(out), self._scale(scale), _DT[od],
+                                       _stream_ptr(self.device)),
+                   "kvattn_decode")
+        return out
+
+    # ------------------------------------------------------------------ lifetime
+    def close(self) -> None:
+        if self._handle and self._handle.value:
+            _check(lib().kvattn_cache_free(self._handle), "kvattn_cache_free")
+            self._handle = ctypes.c_void_p()
+        self._buf = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

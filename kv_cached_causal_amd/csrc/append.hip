@@ -1,0 +1,63 @@
+// Append one K/V position per sequence, and set lengths.
+//
+// Inference chapter, section 9.3: during decode the new token's K and V are
+// appended to each layer's cache; the llm-perf-lab README's cache module
+// preallocates storage so that this append is O(1).  The copy moves raw bits
+// (16-byte integer loads and stores), never converting through float, so the
+// cache holds exactly the caller's bytes.
+#include "common.hpp"
+
+namespace kvattn {
+
+// One workgroup per sequence b: copies the Hkv rows of k_new/v_new to row
+// len[b] of the cache, then (after every thread has read len[b]) bumps it.
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int b = blockIdx.x;
+  const int pos = a.len[b];
+  const int vec_per_row = a.row_bytes >> 4;
+  const int n_vec = a.kv_heads * vec_per_row;
+  for (int i = threadIdx.x; i < n_vec; i += blockDim.x) {
+    const int h = i / vec_per_row;
+    const int w = i - h * vec_per_row;
+    const size_t src = ((size_t)(b * a.kv_heads + h) * a.row_bytes) + (size_t)w * 16;
+    const size_t dst = (((size_t)(b * a.kv_heads + h) * a.max_T + pos) * a.row_bytes) + (size_t)w * 16;
+    const uint4 kv = *reinterpret_cast<const uint4 *>(a.k_new + src);
+    const uint4 vv = *reinterpret_cast<const uint4 *>(a.v_new + src);
+    *reinterpret_cast<uint4 *>(a.k_layer + dst) = kv;
+    *reinterpret_cast<uint4 *>(a.v_layer + dst) = vv;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.len[b] = pos + 1;
+}
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
+  append_kernel<<<dim3(a.batch), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// Lengths travel by value in the kernel arguments, so the caller's host array
+// need not outlive the call and no host-to-device copy is enqueued.
+constexpr int kLenChunk = 256;
+struct LenChunk {
+  int32_t v[kLenChunk];
+};
+
+__global__ void set_lengths_kernel(int32_t *dst, int batch, int offset, int n, LenChunk c) {
+  const int i = threadIdx.x;
+  if (i < n) dst[(size_t)blockIdx.x * batch + offset + i] = c.v[i];
+}
+
+hipError_t launch_set_lengths(int32_t *dst, int layers, int batch, const int32_t *host_lens,
+                              hipStream_t s) {
+  for (int off = 0; off < batch; off += kLenChunk) {
+    LenChunk c;
+    const int n = batch - off < kLenChunk ? batch - off : kLenChunk;
+    for (int i = 0; i < n; ++i) c.v[i] = host_lens[off + i];
+    set_lengths_kernel<<<dim3(layers), dim3(kLenChunk), 0, s>>>(dst, batch, off, n, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace kvattn

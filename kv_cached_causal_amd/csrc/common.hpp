@@ -1,0 +1,74 @@
+// Internal helpers shared by the libkvattn kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvattn.h"
+
+namespace kvattn {
+
+typedef _Float16 half_t;
+typedef __bf16 bf16_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- launch args
+struct AppendArgs {
+  char *k_layer;        // layer's K block (B, Hkv, max_T, D)
+  char *v_layer;        // layer's V block
+  const char *k_new;    // (B, Hkv, 1, D)
+  const char *v_new;
+  int32_t *len;         // layer's lengths [B]
+  int batch, kv_heads, max_T, row_bytes;
+};
+
+struct DecodeArgs {
+  const void *k_layer;  // (B, Hkv, max_T, D)
+  const void *v_layer;
+  const void *q;        // (B, H, 1, D)
+  void *o;              // (B, H, 1, D) in o_dtype
+  float *ws;            // (B, H, n_splits, D + 2) fp32: m (log2 domain), l, u[D]
+  const int32_t *len;   // layer's lengths [B]
+  int batch, q_heads, kv_heads, head_dim, max_T, chunk, n_splits;
+  float scale_log2;     // scale * log2(e)
+  kvattn_dtype dt, o_dt;
+};
+
+struct PrefillArgs {
+  const void *q;        // (B, H, T, D)
+  const void *k;        // (B, Hkv, T, D)
+  const void *v;
+  void *o;              // (B, H, T, D) in o_dtype
+  void *cache_k;        // layer's K block (B, Hkv, max_T, D)
+  void *cache_v;
+  int32_t *len;         // layer's lengths [B]
+  int batch, q_heads, kv_heads, head_dim, T, max_T;
+  float scale_log2;
+  kvattn_dtype dt, o_dt;
+};
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+hipError_t launch_set_lengths(int32_t *dst, int layers, int batch, const int32_t *host_lens,
+                              hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+
+// decode split size in keys: a function of the head dim only, never of the batch
+inline int decode_chunk(int head_dim) { return head_dim <= 32 ? 512 : 256; }
+
+// ---------------------------------------------------------------- device side
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t word4(const uint4 &x, int i) {
+  return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
+}
+
+}  // namespace kvattn

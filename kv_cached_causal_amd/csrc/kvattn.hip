@@ -1,0 +1,320 @@
+// The C ABI of libkvattn: cache object, host-side validation, launches.
+//
+// The cache is one device allocation laid out [layer][K|V][B][Hkv][max_T][D],
+// sized by the inference chapter's capacity formula (section 9.3), plus a
+// lengths array [layer][B] (int32, device) with a host mirror, and a split-K
+// workspace for decode.  Every entry point validates all of its arguments on
+// the host before it enqueues anything, so a failed call never mutates the
+// cache or its mirror.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "common.hpp"
+#include "kvattn.h"
+
+using namespace kvattn;
+
+struct kvattn_cache {
+  int layers, batch, q_heads, kv_heads, head_dim, max_T;
+  kvattn_dtype dt;
+  int elem;               // bytes per element
+  size_t payload_bytes;   // = kvattn_cache_bytes(...)
+  size_t layer_bytes;     // K block + V block of one layer
+  char *base;             // payload (device)
+  bool owns_base;
+  int32_t *d_len;         // [layers][batch] (device)
+  std::vector<int32_t> h_len;  // host mirror
+  float *d_ws;            // decode split-K workspace (device)
+  int chunk, n_splits;
+  int device;
+};
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e, const char *where) {
+  std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", where, hipGetErrorString(e));
+  return KVATTN_ERR_HIP;
+}
+
+int elem_bytes(kvattn_dtype dt) {
+  switch (dt) {
+    case KVATTN_F32: return 4;
+    case KVATTN_F16: return 2;
+    case KVATTN_BF16: return 2;
+  }
+  return 0;
+}
+
+bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
+
+bool valid_out_dtype(const kvattn_cache *c, kvattn_dtype o) { return o == c->dt || o == KVATTN_F32; }
+
+int check_layer(const kvattn_cache *c, int layer) {
+  if (!c) return KVATTN_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= c->layers) return KVATTN_ERR_INVALID_ARG;
+  return KVATTN_OK;
+}
+
+int check_device(const kvattn_cache *c) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != c->device) {
+    std::snprintf(g_last_error, sizeof g_last_error,
+                  "cache lives on device %d but device %d is current", c->device, dev);
+    return KVATTN_ERR_STATE;
+  }
+  return KVATTN_OK;
+}
+
+char *layer_k(const kvattn_cache *c, int layer) { return c->base + (size_t)layer * c->layer_bytes; }
+char *layer_v(const kvattn_cache *c, int layer) {
+  return layer_k(c, layer) + c->layer_bytes / 2;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvattn_cache_bytes(int layers, int batch, int kv_heads, int head_dim, int max_T,
+                          kvattn_dtype dt) {
+  const int e = elem_bytes(dt);
+  if (layers <= 0 || batch <= 0 || kv_heads <= 0 || head_dim <= 0 || max_T <= 0 || e == 0) return 0;
+  return (size_t)2 * layers * kv_heads * head_dim * (size_t)max_T * e * batch;
+}
+
+int kvattn_cache_alloc(kvattn_cache **out, int layers, int batch, int q_heads, int kv_heads,
+                       int head_dim, int max_T, kvattn_dtype dt, void *device_buf,
+                       size_t device_buf_bytes) {
+  if (!out) return KVATTN_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (layers <= 0 || batch <= 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 || max_T <= 0)
+    return KVATTN_ERR_INVALID_ARG;
+  if (elem_bytes(dt) == 0 || !supported_dim(head_dim) || q_heads % kv_heads != 0)
+    return KVATTN_ERR_UNSUPPORTED;
+  const size_t bytes = kvattn_cache_bytes(layers, batch, kv_heads, head_dim, max_T, dt);
+  if (device_buf) {
+    if (device_buf_bytes < bytes) return KVATTN_ERR_OOM;
+    if (((uintptr_t)device_buf & 255u) != 0) return KVATTN_ERR_INVALID_ARG;
+  }
+
+  kvattn_cache *c = new (std::nothrow) kvattn_cache();
+  if (!c) return KVATTN_ERR_OOM;
+  c->layers = layers;
+  c->batch = batch;
+  c->q_heads = q_heads;
+  c->kv_heads = kv_heads;
+  c->head_dim = head_dim;
+  c->max_T = max_T;
+  c->dt = dt;
+  c->elem = elem_bytes(dt);
+  c->payload_bytes = bytes;
+  c->layer_bytes = bytes / layers;
+  c->chunk = decode_chunk(head_dim);
+  c->n_splits = (max_T + c->chunk - 1) / c->chunk;
+  c->h_len.assign((size_t)layers * batch, 0);
+
+  hipError_t e = hipGetDevice(&c->device);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "hipGetDevice");
+  }
+  if (device_buf) {
+    c->base = (char *)device_buf;
+    c->owns_base = false;
+  } else {
+    e = hipMalloc((void **)&c->base, bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      delete c;
+      std::snprintf(g_last_error, sizeof g_last_error, "hipMalloc(%zu): %s", bytes,
+                    hipGetErrorString(e));
+      return KVATTN_ERR_OOM;
+    }
+    c->owns_base = true;
+  }
+  const size_t len_bytes = sizeof(int32_t) * (size_t)layers * batch;
+  const size_t ws_bytes = sizeof(float) * (size_t)batch * q_heads * c->n_splits * (head_dim + 2);
+  e = hipMalloc((void **)&c->d_len, len_bytes);
+  if (e == hipSuccess) e = hipMalloc((void **)&c->d_ws, ws_bytes);
+  if (e == hipSuccess) e = hipMemset(c->d_len, 0, len_bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    int rc = hip_fail(e, "cache side buffers");
+    (void)hipGetLastError();
+    if (c->d_len) (void)hipFree(c->d_len);
+    if (c->d_ws) (void)hipFree(c->d_ws);
+    if (c->owns_base) (void)hipFree(c->base);
+    delete c;
+    return e == hipErrorOutOfMemory ? KVATTN_ERR_OOM : rc;
+  }
+  *out = c;
+  return KVATTN_OK;
+}
+
+int kvattn_cache_free(kvattn_cache *c) {
+  if (!c) return KVATTN_ERR_INVALID_ARG;
+  hipError_t e = hipDeviceSynchronize();
+  hipError_t e1 = hipFree(c->d_len);
+  hipError_t e2 = hipFree(c->d_ws);
+  hipError_t e3 = c->owns_base ? hipFree(c->base) : hipSuccess;
+  delete c;
+  if (e != hipSuccess) return hip_fail(e, "kvattn_cache_free sync");
+  if (e1 != hipSuccess) return hip_fail(e1, "hipFree(lengths)");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipFree(workspace)");
+  if (e3 != hipSuccess) return hip_fail(e3, "hipFree(payload)");
+  return KVATTN_OK;
+}
+
+int kvattn_cache_kv_ptr(const kvattn_cache *c, int layer, void **k, void **v) {
+  int rc = check_layer(c, layer);
+  if (rc) return rc;
+  if (!k || !v) return KVATTN_ERR_INVALID_ARG;
+  *k = layer_k(c, layer);
+  *v = layer_v(c, layer);
+  return KVATTN_OK;
+}
+
+int kvattn_cache_set_lengths(kvattn_cache *c, int layer, const int32_t *host_lens, void *stream) {
+  if (!c || !host_lens) return KVATTN_ERR_INVALID_ARG;
+  if (layer != -1 && (layer < 0 || layer >= c->layers)) return KVATTN_ERR_INVALID_ARG;
+  for (int b = 0; b < c->batch; ++b)
+    if (host_lens[b] < 0 || host_lens[b] > c->max_T) return KVATTN_ERR_CAPACITY;
+  int rc = check_device(c);
+  if (rc) return rc;
+  const int first = layer < 0 ? 0 : layer;
+  const int count = layer < 0 ? c->layers : 1;
+  hipError_t e = launch_set_lengths(c->d_len + (size_t)first * c->batch, count, c->batch, host_lens,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "set_lengths launch");
+  for (int l = first; l < first + count; ++l)
+    std::memcpy(&c->h_len[(size_t)l * c->batch], host_lens, sizeof(int32_t) * c->batch);
+  return KVATTN_OK;
+}
+
+int kvattn_cache_get_lengths(const kvattn_cache *c, int layer, int32_t *host_lens) {
+  int rc = check_layer(c, layer);
+  if (rc) return rc;
+  if (!host_lens) return KVATTN_ERR_INVALID_ARG;
+  std::memcpy(host_lens, &c->h_len[(size_t)layer * c->batch], sizeof(int32_t) * c->batch);
+  return KVATTN_OK;
+}
+
+int kvattn_prefill(kvattn_cache *c, int layer, const void *q, const void *k, const void *v,
+                   void *o, int T, float scale, kvattn_dtype o_dtype, void *stream) {
+  int rc = check_layer(c, layer);
+  if (rc) return rc;
+  if (!q || !k || !v || !o) return KVATTN_ERR_INVALID_ARG;
+  if (T <= 0 || !(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
+  if (!valid_out_dtype(c, o_dtype)) return KVATTN_ERR_UNSUPPORTED;
+  if (T > c->max_T) return KVATTN_ERR_CAPACITY;
+  const int32_t *hl = &c->h_len[(size_t)layer * c->batch];
+  for (int b = 0; b < c->batch; ++b)
+    if (hl[b] != 0) return KVATTN_ERR_STATE;
+  rc = check_device(c);
+  if (rc) return rc;
+
+  PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.cache_k = layer_k(c, layer);
+  a.cache_v = layer_v(c, layer);
+  a.len = c->d_len + (size_t)layer * c->batch;
+  a.batch = c->batch;
+  a.q_heads = c->q_heads;
+  a.kv_heads = c->kv_heads;
+  a.head_dim = c->head_dim;
+  a.T = T;
+  a.max_T = c->max_T;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dt = c->dt;
+  a.o_dt = o_dtype;
+  hipError_t e = launch_prefill(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  for (int b = 0; b < c->batch; ++b) c->h_len[(size_t)layer * c->batch + b] = T;
+  return KVATTN_OK;
+}
+
+int kvattn_append(kvattn_cache *c, int layer, const void *k_new, const void *v_new, void *stream) {
+  int rc = check_layer(c, layer);
+  if (rc) return rc;
+  if (!k_new || !v_new) return KVATTN_ERR_INVALID_ARG;
+  int32_t *hl = &c->h_len[(size_t)layer * c->batch];
+  for (int b = 0; b < c->batch; ++b)
+    if (hl[b] >= c->max_T) return KVATTN_ERR_CAPACITY;
+  rc = check_device(c);
+  if (rc) return rc;
+  AppendArgs a;
+  a.k_layer = layer_k(c, layer);
+  a.v_layer = layer_v(c, layer);
+  a.k_new = (const char *)k_new;
+  a.v_new = (const char *)v_new;
+  a.len = c->d_len + (size_t)layer * c->batch;
+  a.batch = c->batch;
+  a.kv_heads = c->kv_heads;
+  a.max_T = c->max_T;
+  a.row_bytes = c->head_dim * c->elem;
+  hipError_t e = launch_append(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  for (int b = 0; b < c->batch; ++b) hl[b] += 1;
+  return KVATTN_OK;
+}
+
+int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scale,
+                  kvattn_dtype o_dtype, void *stream) {
+  int rc = check_layer(c, layer);
+  if (rc) return rc;
+  if (!q || !o) return KVATTN_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
+  if (!valid_out_dtype(c, o_dtype)) return KVATTN_ERR_UNSUPPORTED;
+  const int32_t *hl = &c->h_len[(size_t)layer * c->batch];
+  for (int b = 0; b < c->batch; ++b)
+    if (hl[b] <= 0) return KVATTN_ERR_STATE;
+  rc = check_device(c);
+  if (rc) return rc;
+  DecodeArgs a;
+  a.k_layer = layer_k(c, layer);
+  a.v_layer = layer_v(c, layer);
+  a.q = q;
+  a.o = o;
+  a.ws = c->d_ws;
+  a.len = c->d_len + (size_t)layer * c->batch;
+  a.batch = c->batch;
+  a.q_heads = c->q_heads;
+  a.kv_heads = c->kv_heads;
+  a.head_dim = c->head_dim;
+  a.max_T = c->max_T;
+  a.chunk = c->chunk;
+  a.n_splits = c->n_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dt = c->dt;
+  a.o_dt = o_dtype;
+  hipError_t e = launch_decode(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return KVATTN_OK;
+}
+
+const char *kvattn_status_string(int status) {
+  switch (status) {
+    case KVATTN_OK: return "ok";
+    case KVATTN_ERR_INVALID_ARG: return "invalid argument";
+    case KVATTN_ERR_UNSUPPORTED: return "unsupported dtype, head_dim or head layout";
+    case KVATTN_ERR_CAPACITY: return "cache capacity exceeded";
+    case KVATTN_ERR_STATE: return "cache state does not allow this call";
+    case KVATTN_ERR_OOM: return "device memory allocation failed";
+    case KVATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *kvattn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

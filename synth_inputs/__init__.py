@@ -173,3 +173,59 @@ def decode_contexts(w: Workload) -> np.ndarray:
     if w.ctx_lo == w.ctx_hi:
         return np.full(w.batch, w.ctx_hi, dtype=np.int64)
     return ragged_lengths(w.cfg, w.batch, w.ctx_lo, w.ctx_hi)
+
+
+# --------------------------------------------------------------------------
+# per-phase inputs of a workload
+# --------------------------------------------------------------------------
+def _apply_heavy(w: Workload, k: np.ndarray, layer: int, step: int, b: int, n_total: int,
+                 first_pos: int) -> np.ndarray:
+    """Scale by 8 the heavy rows (chosen among n_total positions) that fall in
+    k's positions [first_pos, first_pos + k.shape[-2]), per KV head."""
+    if w.heavy_frac <= 0:
+        return k
+    out = k.copy()
+    n_here = k.shape[-2]
+    for h in range(k.shape[0]):
+        rows = heavy_rows(w.cfg, layer, step, b, h, n_total, w.heavy_frac)
+        rows = rows[(rows >= first_pos) & (rows < first_pos + n_here)] - first_pos
+        out[h] = scale_rows(out[h], rows, 8.0, w.dtype)
+    return out
+
+
+def prefill_inputs(w: Workload, layer: int, T: int, batch: int | None = None, variant: int = 0):
+    """Prompt q (B,H,T,D), k, v (B,Hkv,T,D) for one layer, storage dtype.
+
+    variant 0 is the workload's own prompt; variant 1 its separate long prefill.
+    """
+    B = w.batch if batch is None else batch
+    q = normal(w.cfg, layer, -1, Q, (B, w.q_heads, T, w.head_dim), w.dtype, variant)
+    k = normal(w.cfg, layer, -1, K, (B, w.kv_heads, T, w.head_dim), w.dtype, variant)
+    v = normal(w.cfg, layer, -1, V, (B, w.kv_heads, T, w.head_dim), w.dtype, variant)
+    if w.heavy_frac > 0:
+        for b in range(B):
+            k[b] = _apply_heavy(w, k[b], layer, 1000 + variant, b, T, 0)
+    return q, k, v
+
+
+def decode_history(w: Workload, layer: int, b: int, L: int):
+    """Cached rows [0, L-1) of sequence b before its decode step: k, v (Hkv, L-1, D)."""
+    k = normal(w.cfg, layer, -1, K, (w.kv_heads, L - 1, w.head_dim), w.dtype, 2, b)
+    v = normal(w.cfg, layer, -1, V, (w.kv_heads, L - 1, w.head_dim), w.dtype, 2, b)
+    return _apply_heavy(w, k, layer, 0, b, L, 0), v
+
+
+def decode_step_inputs(w: Workload, layer: int, step: int, contexts=None):
+    """q (B,H,1,D) and the appended k_new, v_new (B,Hkv,1,D) of one decode step.
+
+    With ``contexts`` (keys attended per sequence after the append), the heavy
+    rows of position L_b - 1 are applied to k_new.
+    """
+    q = normal(w.cfg, layer, step, Q, (w.batch, w.q_heads, 1, w.head_dim), w.dtype)
+    k = normal(w.cfg, layer, step, K, (w.batch, w.kv_heads, 1, w.head_dim), w.dtype)
+    v = normal(w.cfg, layer, step, V, (w.batch, w.kv_heads, 1, w.head_dim), w.dtype)
+    if contexts is not None and w.heavy_frac > 0:
+        for b in range(w.batch):
+            L = int(contexts[b])
+            k[b] = _apply_heavy(w, k[b], layer, 0, b, L, L - 1)
+    return q, k, v

@@ -1,0 +1,95 @@
+"""The C-ABI library loads, exports every declared symbol and validates on the host (no GPU)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import kv_cached_causal_amd as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvattn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("kvattn_cache_alloc", "kvattn_prefill", "kvattn_append", "kvattn_decode",
+                     "kvattn_cache_bytes", "kvattn_cache_free", "kvattn_cache_set_lengths"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kv.lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_signatures_cover_header():
+    assert set(declared_functions()) == set(kv._SIGS)
+
+
+def test_cache_bytes_matches_worked_example():
+    with open(os.path.join(ROOT, "tests", "golden", "kv_bytes_worked_example.json")) as f:
+        gold = json.load(f)
+    import torch
+    for c in gold["cases"]:
+        got = kv.cache_bytes(c["layers"], c["batch"], c["kv_heads"], c["head_dim"], c["seq_len"], torch.float16)
+        assert got == c["exact_bytes"]
+
+
+def test_cache_bytes_rejects_nonsense():
+    lib = kv.lib()
+    assert lib.kvattn_cache_bytes(0, 1, 1, 64, 16, 1) == 0
+    assert lib.kvattn_cache_bytes(1, 1, 1, 64, -5, 1) == 0
+    assert lib.kvattn_cache_bytes(1, 1, 1, 64, 16, 7) == 0
+    # config sizes: 8 GiB GQA bf16, 64 GiB ragged fp16 decode cache
+    assert lib.kvattn_cache_bytes(32, 16, 8, 128, 4096, 2) == 8 << 30
+    assert lib.kvattn_cache_bytes(32, 32, 32, 128, 4096, 1) == 64 << 30
+
+
+def _alloc(*args):
+    h = ctypes.c_void_p()
+    rc = kv.lib().kvattn_cache_alloc(ctypes.byref(h), *args)
+    return rc, h
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 4, 4, 64, 16, 1, None, 0), -1),       # no layers
+    ((1, 1, 4, 4, 64, 0, 1, None, 0), -1),        # no capacity
+    ((1, 1, 4, 4, 48, 16, 1, None, 0), -2),       # unsupported head_dim
+    ((1, 1, 6, 4, 64, 16, 1, None, 0), -2),       # H % Hkv != 0
+    ((1, 1, 4, 4, 64, 16, 9, None, 0), -2),       # unknown dtype
+    ((1, 1, 4, 4, 64, 16, 1, ctypes.c_void_p(256), 10), -5),   # adopted buffer too small
+    ((1, 1, 4, 4, 64, 16, 1, ctypes.c_void_p(4), 1 << 20), -1),  # misaligned buffer
+])
+def test_alloc_validation_before_any_device_call(args, status):
+    rc, h = _alloc(*args)
+    assert rc == status and not h.value
+
+
+def test_null_cache_is_rejected_everywhere():
+    lib = kv.lib()
+    p = ctypes.c_void_p(0)
+    assert lib.kvattn_cache_free(None) == -1
+    assert lib.kvattn_prefill(None, 0, p, p, p, p, 8, 0.1, 1, None) == -1
+    assert lib.kvattn_append(None, 0, p, p, None) == -1
+    assert lib.kvattn_decode(None, 0, p, p, 0.1, 1, None) == -1
+    assert lib.kvattn_cache_set_lengths(None, 0, (ctypes.c_int32 * 1)(0), None) == -1
+    assert lib.kvattn_cache_get_lengths(None, 0, (ctypes.c_int32 * 1)()) == -1
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.kvattn_cache_kv_ptr(None, 0, ctypes.byref(k), ctypes.byref(v)) == -1
+    assert lib.kvattn_cache_alloc(None, 1, 1, 1, 1, 64, 8, 1, None, 0) == -1
+
+
+def test_status_strings():
+    lib = kv.lib()
+    for s in range(-6, 1):
+        assert lib.kvattn_status_string(s)
+    assert lib.kvattn_status_string(-99) == b"unknown status"
