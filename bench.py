@@ -1,0 +1,384 @@
+"""Benchmark of the KV-cached causal attention hot path on one MI355X.
+
+One step = one pass of the whole path on the 32-layer, 32-head, D=128 fp16
+workload with 1% of K rows scaled by 8:
+  * prefill: a B=1 causal prefill of an 8192-token prompt through all 32
+    layers (each layer writes its K/V into the cache), then
+  * decode: one decode step of a batch of 32 sequences with ragged contexts
+    drawn uniformly from [512, 4096], through all 32 layers (append one K/V
+    row, then attend the whole cache).
+Inputs are seeded synthetic N(0,1) tensors generated on the device and
+resident in HBM before timing starts.  The same run also times a decode step
+of the 32-layer bf16 GQA workload (32 query / 8 KV heads, batch 16, context
+4096).
+
+Printed: one JSON line.  `value` is the decode step's algorithmic HBM bytes
+per second (K and V read once per KV head, plus q, o and the appended row);
+the prefill's algorithmic TFLOP/s (4*B*H*D*T(T+1)/2 per layer) sits in
+`prefill`.  Kernel durations come from HIP events on the launch stream.
+`cpu_baseline` times the CPU fp64 oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import synth_inputs as si  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, TFLOP/s
+METRIC = "decode attn HBM GB/s and prefill attn TFLOP/s (% of MI355X roofline)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--skip-gqa", action="store_true")
+    p.add_argument("--only", choices=["prefill", "decode", "gqa"], default=None,
+                   help="time one phase only (for profiling runs)")
+    return p.parse_args()
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "kv_cached_causal_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key, src_hash):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        e = t[kernel_key]
+        if e.get("source_hash") == src_hash:
+            return e["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        pass
+    return None
+
+
+def fill_normal_(t: torch.Tensor, gen: torch.Generator, chunk=1 << 26):
+    flat = t.view(-1)
+    for i in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - i)
+        flat[i:i + n] = torch.randn(n, generator=gen, device=t.device, dtype=torch.float32).to(t.dtype)
+
+
+def heavy_scale_(k_block: torch.Tensor, L, frac, gen: torch.Generator):
+    """Scale 1% of each sequence's visible K rows by 8 (k_block: (B, Hkv, max_T, D))."""
+    B, Hkv = k_block.shape[:2]
+    for b in range(B):
+        n = int(L[b])
+        c = si.heavy_count(n, frac)
+        for h in range(Hkv):
+            rows = torch.randperm(n, generator=gen, device=k_block.device)[:c]
+            k_block[b, h, rows] *= 8
+
+
+class Timer:
+    """Per-launch HIP event pairs on the current stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+
+def setup_decode(kv, w, dev, seed):
+    ctx = si.decode_contexts(w)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    cache = kv.KVCache(w.layers, w.batch, w.q_heads, w.kv_heads, w.head_dim, w.max_T, dt, device=dev)
+    for layer in range(w.layers):
+        fill_normal_(cache.k_view(layer), gen)
+        fill_normal_(cache.v_view(layer), gen)
+        if w.heavy_frac > 0:
+            heavy_scale_(cache.k_view(layer), ctx, w.heavy_frac, gen)
+    qs = [torch.randn((w.batch, w.q_heads, 1, w.head_dim), generator=gen, device=dev).to(dt) for _ in range(w.layers)]
+    kn = [torch.randn((w.batch, w.kv_heads, 1, w.head_dim), generator=gen, device=dev).to(dt) for _ in range(w.layers)]
+    vn = [torch.randn((w.batch, w.kv_heads, 1, w.head_dim), generator=gen, device=dev).to(dt) for _ in range(w.layers)]
+    outs = [torch.empty_like(q) for q in qs]
+    e = 2
+    bytes_kernel = int(2 * w.kv_heads * w.head_dim * e * int(ctx.sum())   # K and V once per KV head
+                       + 2 * w.batch * w.q_heads * w.head_dim * e)         # q in, o out
+    bytes_step_layer = bytes_kernel + 2 * w.batch * w.kv_heads * w.head_dim * e  # + appended row
+    return dict(w=w, ctx=ctx, cache=cache, q=qs, kn=kn, vn=vn, o=outs,
+                bytes_kernel=bytes_kernel, bytes_step=bytes_step_layer * w.layers)
+
+
+def decode_step(d, timer=None):
+    w, c = d["w"], d["cache"]
+    c.set_lengths([int(L) - 1 for L in d["ctx"]])
+    for layer in range(w.layers):
+        c.append(layer, d["kn"][layer], d["vn"][layer])
+        ev = timer.start() if timer else None
+        c.decode(layer, d["q"][layer], out=d["o"][layer], scale=w.scale)
+        if timer:
+            timer.stop(ev)
+
+
+def setup_prefill(kv, w, dev, seed):
+    T = w.extra_prefill_T
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    dt = torch.float16
+    cache = kv.KVCache(w.layers, 1, w.q_heads, w.kv_heads, w.head_dim, T, dt, device=dev)
+    q, k, v, o = [], [], [], []
+    for layer in range(w.layers):
+        shape_q = (1, w.q_heads, T, w.head_dim)
+        shape_kv = (1, w.kv_heads, T, w.head_dim)
+        q.append(torch.randn(shape_q, generator=gen, device=dev).to(dt))
+        kk = torch.randn(shape_kv, generator=gen, device=dev).to(dt)
+        heavy_scale_(kk, [T], w.heavy_frac, gen)
+        k.append(kk)
+        v.append(torch.randn(shape_kv, generator=gen, device=dev).to(dt))
+        o.append(torch.empty(shape_q, dtype=dt, device=dev))
+    flops = 4.0 * 1 * w.q_heads * w.head_dim * T * (T + 1) / 2
+    return dict(w=w, T=T, cache=cache, q=q, k=k, v=v, o=o, flops_layer=flops)
+
+
+def prefill_step(p, timer=None):
+    w, c = p["w"], p["cache"]
+    c.set_lengths([0])
+    for layer in range(w.layers):
+        ev = timer.start() if timer else None
+        c.prefill(layer, p["q"][layer], p["k"][layer], p["v"][layer], out=p["o"][layer], scale=w.scale)
+        if timer:
+            timer.stop(ev)
+
+
+def timed(fn, steps, warmup):
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    timer = Timer()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, timer.mean_ms()
+
+
+def cpu_baseline():
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    w = si.WORKLOADS[5]
+    cores = len(os.sched_getaffinity(0))
+    threads = cores
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        if info:
+            threads = max(i.get("num_threads", 0) for i in info)
+    except Exception:
+        pass
+    ctx = si.decode_contexts(w)
+    n_seq = 8
+    log(f"cpu baseline: generating decode sample ({n_seq} sequences of layer 0)")
+    ks, vs = [], []
+    for b in range(n_seq):
+        kh, vh = si.decode_history(w, 0, b, int(ctx[b]))
+        ks.append(si.to_f64(kh, w.dtype))
+        vs.append(si.to_f64(vh, w.dtype))
+    q, kn, vn = si.decode_step_inputs(w, 0, 0, ctx)
+    Lmax = int(ctx[:n_seq].max())
+    ck = np.zeros((n_seq, w.kv_heads, Lmax, w.head_dim))
+    cv = np.zeros_like(ck)
+    for b in range(n_seq):
+        L = int(ctx[b])
+        ck[b, :, :L - 1] = ks[b]
+        cv[b, :, :L - 1] = vs[b]
+        ck[b, :, L - 1] = si.to_f64(kn[b, :, 0], w.dtype)
+        cv[b, :, L - 1] = si.to_f64(vn[b, :, 0], w.dtype)
+    qf = si.to_f64(q[:n_seq, :, 0], w.dtype)
+    reps, t_dec = 0, 0.0
+    t0 = time.perf_counter()
+    while t_dec < 5.0:
+        oracle.decode_cached(qf, ck, cv, ctx[:n_seq], w.scale)
+        reps += 1
+        t_dec = time.perf_counter() - t0
+    dec_bytes = reps * (2 * w.kv_heads * w.head_dim * 2 * int(ctx[:n_seq].sum())
+                        + 2 * n_seq * w.q_heads * w.head_dim * 2)
+    # prefill sample: whole heads of one layer at T = 8192, naive (materialises T x T)
+    T = w.extra_prefill_T
+    n_heads = 2
+    log(f"cpu baseline: naive prefill of {n_heads} heads at T={T}")
+    pq, pk, pv = si.prefill_inputs(w, 0, T, batch=1, variant=1)
+    pq = si.to_f64(pq[:, :n_heads], w.dtype)
+    pk = si.to_f64(pk[:, :n_heads], w.dtype)
+    pv = si.to_f64(pv[:, :n_heads], w.dtype)
+    t0 = time.perf_counter()
+    oracle.naive_causal(pq, pk, pv, w.scale)
+    t_pre = time.perf_counter() - t0
+    pre_flops = 4.0 * n_heads * w.head_dim * T * (T + 1) / 2
+    return {
+        "value": round(dec_bytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"decode: layer 0 of the ragged batch-32 workload, first {n_seq} sequences x 32 heads "
+                   f"(sum of contexts {int(ctx[:n_seq].sum())}), {reps} repetitions in {t_dec:.1f} s, fp64 NumPy; "
+                   f"prefill: {n_heads} of 32 heads of one layer at T={T}, naive fp64 in {t_pre:.1f} s"),
+        "prefill": {"value": round(pre_flops / t_pre / 1e12, 6), "unit": "TFLOP/s"},
+        "host_cores_affinity": cores,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import kv_cached_causal_amd as kv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    w5, w4 = si.WORKLOADS[5], si.WORKLOADS[4]
+    res = {}
+
+    dec = pre = gqa = None
+    if args.only in (None, "decode"):
+        log("setting up ragged batch-32 decode cache (64 GiB)")
+        dec = setup_decode(kv, w5, dev, 5)
+    if args.only in (None, "prefill"):
+        log("setting up T=8192 prefill inputs")
+        pre = setup_prefill(kv, w5, dev, 55)
+    torch.cuda.synchronize()
+
+    def step(timer):
+        tp, td = (timer if timer else (None, None))
+        if pre is not None:
+            prefill_step(pre, tp)
+        if dec is not None:
+            decode_step(dec, td)
+
+    # warmup
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    tp, td = Timer(), Timer()
+    # phase clocks: events at phase boundaries of every step
+    marks = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True); e0.record()
+        if pre is not None:
+            prefill_step(pre, tp)
+        e1 = torch.cuda.Event(enable_timing=True); e1.record()
+        if dec is not None:
+            decode_step(dec, td)
+        e2 = torch.cuda.Event(enable_timing=True); e2.record()
+        marks.append((e0, e1, e2))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    pre_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in marks]))
+    dec_ms = float(np.mean([b.elapsed_time(c) for _, b, c in marks]))
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f16", "data": "synthetic"}
+    dec_hash = kernel_source_hash(["decode.hip"])
+    pre_hash = kernel_source_hash(["prefill.hip"])
+    if dec is not None:
+        k_ms = td.mean_ms()
+        achieved = dec["bytes_kernel"] / (k_ms * 1e-3) / 1e9
+        out["value"] = round(dec["bytes_step"] / (dec_ms * 1e-3) / 1e9, 2)
+        out["unit"] = "GB/s"
+        out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": traffic_from_profiles("decode_ragged_b32", dec_hash),
+                           "kernel": "kvattn_decode (split-K partial + merge) per layer",
+                           "algorithmic_bytes_per_launch": dec["bytes_kernel"],
+                           "mean_launch_ms": round(k_ms, 5)}
+        out["decode"] = {"ms_per_step": round(dec_ms, 4), "us_per_layer": round(dec_ms * 1e3 / w5.layers, 2),
+                         "bytes_per_step": dec["bytes_step"], "sum_contexts": int(dec["ctx"].sum())}
+    if pre is not None:
+        k_ms = tp.mean_ms()
+        tf = pre["flops_layer"] / (k_ms * 1e-3) / 1e12
+        out["prefill"] = {"value": round(pre["flops_layer"] * w5.layers / (pre_ms * 1e-3) / 1e12, 2),
+                          "unit": "TFLOP/s", "ms_per_step": round(pre_ms, 4),
+                          "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                       "traffic": traffic_from_profiles("prefill_t8192", pre_hash),
+                                       "kernel": "prefill_mfma_kernel<f16, D=128>",
+                                       "algorithmic_flops_per_launch": pre["flops_layer"],
+                                       "mean_launch_ms": round(k_ms, 5)}}
+        if "value" not in out:
+            out["value"], out["unit"] = out["prefill"]["value"], "TFLOP/s"
+    out["config"] = {"workload": w5.name, "layers": w5.layers, "q_heads": w5.q_heads, "kv_heads": w5.kv_heads,
+                     "head_dim": w5.head_dim, "decode_batch": w5.batch,
+                     "decode_contexts": f"U[{w5.ctx_lo},{w5.ctx_hi}]", "heavy_k_rows": w5.heavy_frac,
+                     "prefill_batch": 1, "prefill_T": w5.extra_prefill_T, "dtype": "f16"}
+    out["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                     "cus": props.multi_processor_count}
+    # free the big caches before the GQA workload
+    if dec is not None:
+        dec["cache"].close()
+    if pre is not None:
+        pre["cache"].close()
+    dec = pre = None
+    torch.cuda.empty_cache()
+
+    if not args.skip_gqa and args.only in (None, "gqa"):
+        log("GQA bf16 decode workload (8 GiB cache)")
+        g = setup_decode(kv, w4, dev, 4)
+        wall, k_ms = timed(lambda t: decode_step(g, t), args.steps, args.warmup)
+        step_ms = wall / args.steps * 1e3
+        achieved = g["bytes_kernel"] / (k_ms * 1e-3) / 1e9
+        out["decode_gqa"] = {"workload": w4.name, "value": round(g["bytes_step"] / (step_ms * 1e-3) / 1e9, 2),
+                             "unit": "GB/s", "ms_per_step": round(step_ms, 4),
+                             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                                          "traffic": traffic_from_profiles("decode_gqa_b16", dec_hash),
+                                          "mean_launch_ms": round(k_ms, 5)}}
+        g["cache"].close()
+        if args.only == "gqa":
+            out["value"], out["unit"] = out["decode_gqa"]["value"], "GB/s"
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
