@@ -57,8 +57,17 @@ hipError_t launch_set_lengths(int32_t *dst, int layers, int batch, const int32_t
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 
-// decode split size in keys: a function of the head dim only, never of the batch
-inline int decode_chunk(int head_dim) { return head_dim <= 32 ? 512 : 256; }
+// decode splits per (sequence, KV head) are capped so the merge keeps its
+// split weights in LDS
+constexpr int kMaxSplits = 64;
+
+// decode split size in keys: a function of the head dim and the capacity,
+// never of the batch (so each sequence's result is independent of the others)
+inline int decode_chunk(int head_dim, int max_T) {
+  int c = head_dim <= 32 ? 512 : 256;
+  while ((max_T + c - 1) / c > kMaxSplits) c *= 2;
+  return c;
+}
 
 // ---------------------------------------------------------------- device side
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {

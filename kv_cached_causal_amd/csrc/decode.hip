@@ -7,9 +7,12 @@
 // with 16-byte loads, the G query heads that share a KV head (roadmap page,
 // project 12, MQA/GQA) are served by the same workgroup, and long contexts
 // are split across workgroups.  Each split keeps the online-softmax state
-// (m, l, u) -- the chunked-attention recurrence of the README -- and a second
-// kernel merges the splits by log-sum-exp.  Scores carry log2(e) inside the
-// scale so that every exponential is a single exp2.
+// (m, l, u) -- the chunked-attention recurrence of the README -- and a small
+// second kernel merges the splits of each (sequence, KV head) by log-sum-exp.
+// (Merging in the last-arriving workgroup would need a device-scope fence per
+// workgroup, which on this multi-XCD part writes back and invalidates the
+// whole L2 each time: measured ten times slower.)  Scores carry log2(e) inside the scale so that every
+// exponential is a single exp2.
 #include "common.hpp"
 
 namespace kvattn {
@@ -64,36 +67,63 @@ __device__ __forceinline__ float elem(TagBF16, const uint4 &x, int e) {
   return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
+// DPP lane permutations inside a row of 16 lanes
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <- lane 7-i within 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <- lane 15-i within 16
+
+// sum over the LPR consecutive lanes that share one key row; every one of
+// those lanes ends with the full sum
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  if constexpr (LPR >= 2) x += dpp<DPP_XOR1>(x);
+  if constexpr (LPR >= 4) x += dpp<DPP_XOR2>(x);
+  if constexpr (LPR >= 8) x += dpp<DPP_HALF_MIRROR>(x);
+  if constexpr (LPR >= 16) x += dpp<DPP_MIRROR>(x);
+  if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
   return x;
 }
 
-// grid (n_splits, Hkv * G/GT, B), 256 threads.  Workgroup = one split of
+__device__ __forceinline__ void store_out(void *o, size_t idx, float x, kvattn_dtype dt) {
+  if (dt == KVATTN_F32)
+    ((float *)o)[idx] = x;
+  else if (dt == KVATTN_F16)
+    ((half_t *)o)[idx] = (half_t)x;
+  else
+    ((bf16_t *)o)[idx] = (bf16_t)x;
+}
+
+// grid (n_splits, Hkv * G/GT, B), 256 threads.  A workgroup owns one split of
 // `chunk` keys of one KV head, for GT query heads of its group.
-template <class Tag, int D, int GT>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
+template <class Tag, int D, int GT, int U>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int EPL = Tag::EPL;
   constexpr int LPR = D / EPL;   // lanes that share one key row
-  constexpr int RPW = 64 / LPR;  // key rows per wave per load
-  constexpr int U = 8;           // loads in flight per lane and tensor
+  constexpr int RPW = 64 / LPR;  // key rows per wave per 16-byte load
   constexpr int ESZ = Tag::bytes;
+  constexpr int ROWS_PER_STEP = 4 * RPW;  // key rows covered by one load across the 4 waves
 
   const int b = blockIdx.z;
   const int split = blockIdx.x;
   const int G = a.q_heads / a.kv_heads;
   const int subs = G / GT;
-  const int kvh = blockIdx.y / subs;
-  const int h0 = kvh * G + (blockIdx.y - kvh * subs) * GT;
+  const int unit = blockIdx.y;  // (kv head, sub-group of GT query heads)
+  const int kvh = unit / subs;
+  const int h0 = kvh * G + (unit - kvh * subs) * GT;
   const int L = a.len[b];
   const int kb = split * a.chunk;
-  if (kb >= L) return;  // empty split: the merge only reads splits below L
+  if (kb >= L) return;  // empty split
   const int rows = min(a.chunk, L - kb);
+  const int n_valid = (L + a.chunk - 1) / a.chunk;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int rg = lane / LPR;
   const int cl = (lane % LPR) * EPL;
 
@@ -115,15 +145,15 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
   }
 
-  const int steps = (rows + 4 * RPW - 1) / (4 * RPW);
-  for (int s0 = 0; s0 < steps; s0 += U) {
-    uint4 kr[U], vr[U];
-    bool ok[U];
+  const int steps = (rows + ROWS_PER_STEP - 1) / ROWS_PER_STEP;
+  const int nb = (steps + U - 1) / U;
+
+  uint4 k0[U], v0[U], k1[U], v1[U];
+  auto load = [&](int ib, uint4 (&kr)[U], uint4 (&vr)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = ((s0 + u) * 4 + wave) * RPW + rg;
-      ok[u] = r < rows;
-      if (ok[u]) {
+      const int r = ((ib * U + u) * 4 + wave) * RPW + rg;
+      if (r < rows) {
         kr[u] = *(const uint4 *)(Kb + (size_t)r * D * ESZ);
         vr[u] = *(const uint4 *)(Vb + (size_t)r * D * ESZ);
       } else {
@@ -131,14 +161,18 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
         vr[u] = make_uint4(0, 0, 0, 0);
       }
     }
+  };
+  auto compute = [&](int ib, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
     float sc[U][GT];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      const bool ok = ((ib * U + u) * 4 + wave) * RPW + rg < rows;
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
         const float d = row_sum<LPR>(dot16(Tag{}, qv[g], kr[u]));
-        sc[u][g] = ok[u] ? d * a.scale_log2 : -INFINITY;
+        sc[u][g] = ok ? d * a.scale_log2 : -INFINITY;
       }
+    }
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       float mx = sc[0][g];
@@ -158,6 +192,17 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
         for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p, elem(Tag{}, vr[u], e), acc[g][e]);
       }
       m[g] = mn;
+    }
+  };
+
+  // two register buffers: the loads of batch i+1 are in flight while batch i computes
+  load(0, k0, v0);
+  for (int ib = 0; ib < nb; ib += 2) {
+    if (ib + 1 < nb) load(ib + 1, k1, v1);
+    compute(ib, k0, v0);
+    if (ib + 1 < nb) {
+      if (ib + 2 < nb) load(ib + 2, k0, v0);
+      compute(ib + 1, k1, v1);
     }
   }
 
@@ -182,7 +227,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
     }
   }
 
-  // merge the four waves through LDS and write this split's (m, l, u)
+  // merge the four waves through LDS
   __shared__ float s_m[4][GT], s_l[4][GT];
   __shared__ float s_acc[4][GT][D];
   if (lane < LPR) {
@@ -197,7 +242,27 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < GT * D; t += 256) {
+
+  if (n_valid == 1) {
+    // the whole context fits one split: normalise and store directly
+    for (int t = tid; t < GT * D; t += 256) {
+      const int g = t / D;
+      const int d = t - g * D;
+      const float M = fmaxf(fmaxf(s_m[0][g], s_m[1][g]), fmaxf(s_m[2][g], s_m[3][g]));
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float al = fast_exp2(s_m[w][g] - M);
+        num = fmaf(al, s_acc[w][g][d], num);
+        den = fmaf(al, s_l[w][g], den);
+      }
+      store_out(a.o, (size_t)(b * a.q_heads + h0 + g) * D + d, num / den, a.o_dt);
+    }
+    return;
+  }
+
+  // write this split's (m, l, u) for the GT heads; decode_merge combines them
+  for (int t = tid; t < GT * D; t += 256) {
     const int g = t / D;
     const int d = t - g * D;
     const float M = fmaxf(fmaxf(s_m[0][g], s_m[1][g]), fmaxf(s_m[2][g], s_m[3][g]));
@@ -217,53 +282,75 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   }
 }
 
-__device__ __forceinline__ void store_out(void *o, size_t idx, float x, kvattn_dtype dt) {
-  if (dt == KVATTN_F32)
-    ((float *)o)[idx] = x;
-  else if (dt == KVATTN_F16)
-    ((half_t *)o)[idx] = (half_t)x;
-  else
-    ((bf16_t *)o)[idx] = (bf16_t)x;
-}
-
-// grid (H, B), D threads: log-sum-exp merge of the non-empty splits.
-template <int D>
-__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
-  const int h = blockIdx.x;
+// grid (Hkv * G/GT, B), 256 threads: log-sum-exp merge of the non-empty splits
+// of one (sequence, KV head, GT query heads) unit.  Units whose context fits
+// one split were finished by decode_kernel.
+template <int D, int GT>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int MAXS = kMaxSplits;
   const int b = blockIdx.y;
+  const int G = a.q_heads / a.kv_heads;
+  const int subs = G / GT;
+  const int unit = blockIdx.x;
+  const int kvh = unit / subs;
+  const int h0 = kvh * G + (unit - kvh * subs) * GT;
   const int L = a.len[b];
   const int ns = (L + a.chunk - 1) / a.chunk;
-  const float *w = a.ws + (size_t)(b * a.q_heads + h) * a.n_splits * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, w[(size_t)s * (D + 2)]);
-  const int d = threadIdx.x;
-  if (d >= D) return;
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float *ws = w + (size_t)s * (D + 2);
-    const float al = fast_exp2(ws[0] - M);
-    den = fmaf(al, ws[1], den);
-    num = fmaf(al, ws[2 + d], num);
+  if (ns <= 1) return;
+  __shared__ float s_w[GT][MAXS];
+  __shared__ float s_den[GT];
+  const int tid = threadIdx.x;
+  // split weights relative to the per-head maximum
+  for (int t = tid; t < GT * ns; t += 256) {
+    const int g = t / ns;
+    const int s = t - g * ns;
+    s_w[g][s] = a.ws[((size_t)(b * a.q_heads + h0 + g) * a.n_splits + s) * (D + 2)];
   }
-  store_out(a.o, (size_t)(b * a.q_heads + h) * D + d, num / den, a.o_dt);
+  __syncthreads();
+  if (tid < GT) {
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, s_w[tid][s]);
+    float den = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float w = fast_exp2(s_w[tid][s] - M);
+      s_w[tid][s] = w;
+      den = fmaf(w, a.ws[((size_t)(b * a.q_heads + h0 + tid) * a.n_splits + s) * (D + 2) + 1], den);
+    }
+    s_den[tid] = den;
+  }
+  __syncthreads();
+  for (int t = tid; t < GT * D; t += 256) {
+    const int g = t / D;
+    const int d = t - g * D;
+    const float *u = a.ws + (size_t)(b * a.q_heads + h0 + g) * a.n_splits * (D + 2) + 2 + d;
+    float num = 0.f;
+    for (int s = 0; s < ns; ++s) num = fmaf(s_w[g][s], u[(size_t)s * (D + 2)], num);
+    store_out(a.o, (size_t)(b * a.q_heads + h0 + g) * D + d, num / s_den[g], a.o_dt);
+  }
+}
+
+template <class Tag, int D, int GT>
+static hipError_t launch_gt(const DecodeArgs &a, hipStream_t s) {
+  constexpr int U = 4;
+  const int units = a.q_heads / GT;  // = Hkv * (G / GT)
+  decode_kernel<Tag, D, GT, U><<<dim3(a.n_splits, units, a.batch), 256, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_splits == 1) return e;
+  decode_merge_kernel<D, GT><<<dim3(units, a.batch), 256, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <class Tag, int D>
 static hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
   const int G = a.q_heads / a.kv_heads;
   const int GT = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 3 == 0) ? 3 : (G % 2 == 0) ? 2 : 1;
-  const dim3 grid(a.n_splits, a.kv_heads * (G / GT), a.batch);
   switch (GT) {
-    case 8: decode_partial_kernel<Tag, D, 8><<<grid, 256, 0, s>>>(a); break;
-    case 4: decode_partial_kernel<Tag, D, 4><<<grid, 256, 0, s>>>(a); break;
-    case 3: decode_partial_kernel<Tag, D, 3><<<grid, 256, 0, s>>>(a); break;
-    case 2: decode_partial_kernel<Tag, D, 2><<<grid, 256, 0, s>>>(a); break;
-    default: decode_partial_kernel<Tag, D, 1><<<grid, 256, 0, s>>>(a); break;
+    case 8: return launch_gt<Tag, D, 8>(a, s);
+    case 4: return launch_gt<Tag, D, 4>(a, s);
+    case 3: return launch_gt<Tag, D, 3>(a, s);
+    case 2: return launch_gt<Tag, D, 2>(a, s);
+    default: return launch_gt<Tag, D, 1>(a, s);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  decode_merge_kernel<D><<<dim3(a.q_heads, a.batch), dim3(D < 64 ? 64 : D), 0, s>>>(a);
-  return hipGetLastError();
 }
 
 template <class Tag>

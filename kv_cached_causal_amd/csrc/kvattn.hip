@@ -116,7 +116,7 @@ int kvattn_cache_alloc(kvattn_cache **out, int layers, int batch, int q_heads, i
   c->elem = elem_bytes(dt);
   c->payload_bytes = bytes;
   c->layer_bytes = bytes / layers;
-  c->chunk = decode_chunk(head_dim);
+  c->chunk = decode_chunk(head_dim, max_T);
   c->n_splits = (max_T + c->chunk - 1) / c->chunk;
   c->h_len.assign((size_t)layers * batch, 0);
 
