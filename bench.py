@@ -134,11 +134,13 @@ def setup_decode(kv, w, dev, seed):
     kn = [torch.randn((w.batch, w.kv_heads, 1, w.head_dim), generator=gen, device=dev).to(dt) for _ in range(w.layers)]
     vn = [torch.randn((w.batch, w.kv_heads, 1, w.head_dim), generator=gen, device=dev).to(dt) for _ in range(w.layers)]
     outs = [torch.empty_like(q) for q in qs]
+    appends = [cache.bind_append(l, kn[l], vn[l]) for l in range(w.layers)]
+    decodes = [cache.bind_decode(l, qs[l], outs[l], scale=w.scale) for l in range(w.layers)]
     e = 2
     bytes_kernel = int(2 * w.kv_heads * w.head_dim * e * int(ctx.sum())   # K and V once per KV head
                        + 2 * w.batch * w.q_heads * w.head_dim * e)         # q in, o out
     bytes_step_layer = bytes_kernel + 2 * w.batch * w.kv_heads * w.head_dim * e  # + appended row
-    return dict(w=w, ctx=ctx, cache=cache, q=qs, kn=kn, vn=vn, o=outs,
+    return dict(w=w, ctx=ctx, cache=cache, q=qs, kn=kn, vn=vn, o=outs, appends=appends, decodes=decodes,
                 bytes_kernel=bytes_kernel, bytes_step=bytes_step_layer * w.layers)
 
 
@@ -146,9 +148,9 @@ def decode_step(d, timer=None):
     w, c = d["w"], d["cache"]
     c.set_lengths([int(L) - 1 for L in d["ctx"]])
     for layer in range(w.layers):
-        c.append(layer, d["kn"][layer], d["vn"][layer])
+        d["appends"][layer]()
         ev = timer.start() if timer else None
-        c.decode(layer, d["q"][layer], out=d["o"][layer], scale=w.scale)
+        d["decodes"][layer]()
         if timer:
             timer.stop(ev)
 
@@ -170,7 +172,8 @@ def setup_prefill(kv, w, dev, seed):
         v.append(torch.randn(shape_kv, generator=gen, device=dev).to(dt))
         o.append(torch.empty(shape_q, dtype=dt, device=dev))
     flops = 4.0 * 1 * w.q_heads * w.head_dim * T * (T + 1) / 2
-    return dict(w=w, T=T, cache=cache, q=q, k=k, v=v, o=o, flops_layer=flops)
+    calls = [cache.bind_prefill(l, q[l], k[l], v[l], o[l], scale=w.scale) for l in range(w.layers)]
+    return dict(w=w, T=T, cache=cache, q=q, k=k, v=v, o=o, calls=calls, flops_layer=flops)
 
 
 def prefill_step(p, timer=None):
@@ -178,7 +181,7 @@ def prefill_step(p, timer=None):
     c.set_lengths([0])
     for layer in range(w.layers):
         ev = timer.start() if timer else None
-        c.prefill(layer, p["q"][layer], p["k"][layer], p["v"][layer], out=p["o"][layer], scale=w.scale)
+        p["calls"][layer]()
         if timer:
             timer.stop(ev)
 
@@ -340,7 +343,7 @@ def main():
                           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                                        "traffic": traffic_from_profiles("prefill_t8192", pre_hash),
-                                       "kernel": "prefill_mfma_kernel<f16, D=128>",
+                                       "kernel": "prefill_pipe_kernel<f16, D=128> (8 waves x 32 query rows, 64-key tiles)",
                                        "algorithmic_flops_per_launch": pre["flops_layer"],
                                        "mean_launch_ms": round(k_ms, 5)}}
         if "value" not in out:

@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of prefill, append and decode runs in
 the HIP kernels of ``libkvattn.so`` (built in-tree by
-``kv_cached_causal_amd.build``).  PyTorch supplies device memory and the
+``kv_cached_causal_amd/build.py``).  PyTorch supplies device memory and the
 stream.  If the library is missing this module raises at import time: there
 is no CPU fallback.
 
@@ -20,7 +20,8 @@ import torch
 __all__ = ["KVCache", "KVAttnError", "cache_bytes", "lib", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvattn.so")
+# KVATTN_LIB names another build of the library (for example a tuning variant)
+LIB_PATH = os.environ.get("KVATTN_LIB") or os.path.join(_HERE, "libkvattn.so")
 
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _ELEM = {torch.float32: 4, torch.float16: 2, torch.bfloat16: 2}
@@ -58,7 +59,7 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is not built: run `python -m kv_cached_causal_amd.build`")
+            raise ImportError(f"{LIB_PATH} is not built: run `python kv_cached_causal_amd/build.py`")
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             fn = getattr(handle, name)
@@ -222,6 +223,43 @@ class KVCache:
                                        _stream_ptr(self.device)),
                    "kvattn_decode")
         return out
+
+    # ------------------------------------------------------------------ pre-bound calls
+    # For launch-bound loops (many short kernels): the arguments are checked
+    # and marshalled once, on the stream current at bind time, and the returned
+    # callable only enqueues the C call.  The tensors must stay alive.
+    def bind_prefill(self, layer: int, q, k, v, out, scale: float | None = None):
+        B, H, Hkv, D = self.batch, self.q_heads, self.kv_heads, self.head_dim
+        T = q.shape[2] if q.dim() == 4 else -1
+        self._tensor(q, (B, H, T, D), "q")
+        self._tensor(k, (B, Hkv, T, D), "k")
+        self._tensor(v, (B, Hkv, T, D), "v")
+        self._tensor(out, (B, H, T, D), "out", out.dtype)
+        if out.dtype not in (self.dtype, torch.float32):
+            raise TypeError(f"out has dtype {out.dtype}")
+        fn = lib().kvattn_prefill
+        args = (self._handle, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(out), T, ctypes.c_float(self._scale(scale)),
+                _DT[out.dtype], _stream_ptr(self.device))
+        return lambda: _check(fn(*args), "kvattn_prefill")
+
+    def bind_append(self, layer: int, k_new, v_new):
+        shape = (self.batch, self.kv_heads, 1, self.head_dim)
+        self._tensor(k_new, shape, "k_new")
+        self._tensor(v_new, shape, "v_new")
+        fn = lib().kvattn_append
+        args = (self._handle, layer, _ptr(k_new), _ptr(v_new), _stream_ptr(self.device))
+        return lambda: _check(fn(*args), "kvattn_append")
+
+    def bind_decode(self, layer: int, q, out, scale: float | None = None):
+        shape = (self.batch, self.q_heads, 1, self.head_dim)
+        self._tensor(q, shape, "q")
+        self._tensor(out, shape, "out", out.dtype)
+        if out.dtype not in (self.dtype, torch.float32):
+            raise TypeError(f"out has dtype {out.dtype}")
+        fn = lib().kvattn_decode
+        args = (self._handle, layer, _ptr(q), _ptr(out), ctypes.c_float(self._scale(scale)), _DT[out.dtype],
+                _stream_ptr(self.device))
+        return lambda: _check(fn(*args), "kvattn_decode")
 
     # ------------------------------------------------------------------ lifetime
     def close(self) -> None:

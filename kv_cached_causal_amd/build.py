@@ -1,6 +1,6 @@
 """Build libkvattn.so in-tree with hipcc for gfx950.
 
-``python -m kv_cached_causal_amd.build`` (or ``__graft_entry__.build()``)
+``python kv_cached_causal_amd/build.py`` (or ``__graft_entry__.build()``)
 compiles every ``csrc/*.hip`` file to an object and links the shared library
 next to this file.  It always recompiles.
 """

@@ -15,6 +15,10 @@ typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+// 16 raw bytes as a native vector: plain loads/stores that stay in registers
+// (HIP's uint4 struct is copied with memcpy, which can force it into scratch)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- launch args
 struct AppendArgs {

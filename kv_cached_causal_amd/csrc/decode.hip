@@ -15,6 +15,11 @@
 // exponential is a single exp2.
 #include "common.hpp"
 
+// 16-byte K and V loads per lane per batch (two batches are in flight)
+#ifndef KVATTN_DECODE_U
+#define KVATTN_DECODE_U 4
+#endif
+
 namespace kvattn {
 
 struct TagF32 {
@@ -149,17 +154,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int nb = (steps + U - 1) / U;
 
   uint4 k0[U], v0[U], k1[U], v1[U];
+  // Rows past the split's end are clamped to its last row (always valid: the
+  // split is non-empty) and their scores masked to -inf.  Keeping the loads
+  // free of branches lets the compiler wait for one batch while the next is
+  // still in flight.
   auto load = [&](int ib, uint4 (&kr)[U], uint4 (&vr)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = ((ib * U + u) * 4 + wave) * RPW + rg;
-      if (r < rows) {
-        kr[u] = *(const uint4 *)(Kb + (size_t)r * D * ESZ);
-        vr[u] = *(const uint4 *)(Vb + (size_t)r * D * ESZ);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-      }
+      const int r = min(((ib * U + u) * 4 + wave) * RPW + rg, rows - 1);
+      kr[u] = *(const uint4 *)(Kb + (size_t)r * D * ESZ);
+      vr[u] = *(const uint4 *)(Vb + (size_t)r * D * ESZ);
     }
   };
   auto compute = [&](int ib, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
@@ -195,15 +199,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
   };
 
-  // two register buffers: the loads of batch i+1 are in flight while batch i computes
+  // two register buffers: the loads of batch i+1 are in flight while batch i
+  // computes.  The loads are issued unconditionally (a batch past the end
+  // re-reads the clamped last row) so that only the compute is branched over.
+  // The scheduling barriers keep the compiler from sinking the loads below
+  // the compute (which it does to shorten register live ranges).
   load(0, k0, v0);
   for (int ib = 0; ib < nb; ib += 2) {
-    if (ib + 1 < nb) load(ib + 1, k1, v1);
+    load(ib + 1, k1, v1);
+    __builtin_amdgcn_sched_barrier(0);
     compute(ib, k0, v0);
-    if (ib + 1 < nb) {
-      if (ib + 2 < nb) load(ib + 2, k0, v0);
-      compute(ib + 1, k1, v1);
-    }
+    load(ib + 2, k0, v0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ib + 1 < nb) compute(ib + 1, k1, v1);
   }
 
   // merge the row groups of this wave (lanes that hold the same columns)
@@ -284,10 +292,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
 // grid (Hkv * G/GT, B), 256 threads: log-sum-exp merge of the non-empty splits
 // of one (sequence, KV head, GT query heads) unit.  Units whose context fits
-// one split were finished by decode_kernel.
+// one split were finished by decode_kernel.  All global reads are issued in
+// parallel (the split statistics by one lane per split, the partial sums
+// eight splits at a time), since the kernel is bound by load latency.
 template <int D, int GT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   constexpr int MAXS = kMaxSplits;
+  static_assert(MAXS <= 64, "one lane per split");
+  constexpr int PARTS = (GT * D >= 256) ? 1 : 256 / (GT * D);  // threads per output
   const int b = blockIdx.y;
   const int G = a.q_heads / a.kv_heads;
   const int subs = G / GT;
@@ -299,39 +311,63 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   if (ns <= 1) return;
   __shared__ float s_w[GT][MAXS];
   __shared__ float s_den[GT];
+  __shared__ float s_part[PARTS > 1 ? 256 : 1];
   const int tid = threadIdx.x;
-  // split weights relative to the per-head maximum
-  for (int t = tid; t < GT * ns; t += 256) {
-    const int g = t / ns;
-    const int s = t - g * ns;
-    s_w[g][s] = a.ws[((size_t)(b * a.q_heads + h0 + g) * a.n_splits + s) * (D + 2)];
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const float *ws_unit = a.ws + (size_t)(b * a.q_heads + h0) * a.n_splits * (D + 2);
+  // split weights relative to the per-head maximum: one wave per head, one lane per split
+  for (int g = wave; g < GT; g += 4) {
+    const float *st = ws_unit + ((size_t)g * a.n_splits + min(lane, ns - 1)) * (D + 2);
+    const float ms = lane < ns ? st[0] : -INFINITY;
+    const float ls = lane < ns ? st[1] : 0.f;
+    float M = ms;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float w = lane < ns ? fast_exp2(ms - M) : 0.f;
+    float den = w * ls;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+    s_w[g][lane] = w;
+    if (lane == 0) s_den[g] = den;
   }
   __syncthreads();
-  if (tid < GT) {
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, s_w[tid][s]);
-    float den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float w = fast_exp2(s_w[tid][s] - M);
-      s_w[tid][s] = w;
-      den = fmaf(w, a.ws[((size_t)(b * a.q_heads + h0 + tid) * a.n_splits + s) * (D + 2) + 1], den);
-    }
-    s_den[tid] = den;
-  }
-  __syncthreads();
-  for (int t = tid; t < GT * D; t += 256) {
-    const int g = t / D;
-    const int d = t - g * D;
-    const float *u = a.ws + (size_t)(b * a.q_heads + h0 + g) * a.n_splits * (D + 2) + 2 + d;
+  for (int t = tid; t < GT * D * PARTS; t += 256) {
+    const int part = t / (GT * D);
+    const int gd = t - part * GT * D;
+    const int g = gd / D;
+    const int d = gd - g * D;
+    const float *u = ws_unit + (size_t)g * a.n_splits * (D + 2) + 2 + d;
     float num = 0.f;
-    for (int s = 0; s < ns; ++s) num = fmaf(s_w[g][s], u[(size_t)s * (D + 2)], num);
-    store_out(a.o, (size_t)(b * a.q_heads + h0 + g) * D + d, num / s_den[g], a.o_dt);
+    for (int s0 = part * 8; s0 < ns; s0 += 8 * PARTS) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = u[(size_t)min(s0 + i, ns - 1) * (D + 2)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) num = fmaf(s0 + i < ns ? s_w[g][min(s0 + i, MAXS - 1)] : 0.f, x[i], num);
+    }
+    if constexpr (PARTS > 1) {
+      s_part[t] = num;
+    } else {
+      store_out(a.o, (size_t)(b * a.q_heads + h0 + g) * D + d, num / s_den[g], a.o_dt);
+    }
+  }
+  if constexpr (PARTS > 1) {
+    __syncthreads();
+    for (int t = tid; t < GT * D; t += 256) {
+      float num = 0.f;
+#pragma unroll
+      for (int p = 0; p < PARTS; ++p) num += s_part[p * GT * D + t];
+      const int g = t / D;
+      const int d = t - g * D;
+      store_out(a.o, (size_t)(b * a.q_heads + h0 + g) * D + d, num / s_den[g], a.o_dt);
+    }
   }
 }
 
 template <class Tag, int D, int GT>
 static hipError_t launch_gt(const DecodeArgs &a, hipStream_t s) {
-  constexpr int U = 4;
+  constexpr int U = KVATTN_DECODE_U;
   const int units = a.q_heads / GT;  // = Hkv * (G / GT)
   decode_kernel<Tag, D, GT, U><<<dim3(a.n_splits, units, a.batch), 256, 0, s>>>(a);
   hipError_t e = hipGetLastError();

@@ -21,6 +21,8 @@
 // store that K/V tile into the cache from the registers it was loaded into.
 //
 // F32 takes a plain vector-ALU kernel (one lane per query row).
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace kvattn {
@@ -81,28 +83,40 @@ __device__ __forceinline__ void store4(void *o, size_t idx, const float4_t &x, f
 template <int D, int BN>
 struct PrefillLds {
   static constexpr int KSTR = D + 8;   // K row stride (elements): conflict-free 16-B reads
-  static constexpr int VSTR = BN + 8;  // V^T row stride (elements)
+  // V^T row stride (elements): 34 dwords for BN = 64, so the 16 lanes of a
+  // quarter-wave reading 8 bytes each from consecutive rows hit distinct bank pairs
+  static constexpr int VSTR = BN + 4;
   static constexpr int K_ELEMS = BN * KSTR;
   static constexpr int V_ELEMS = D * VSTR;
   static constexpr int BUF = K_ELEMS + V_ELEMS;
   static constexpr size_t BYTES = 2 * BUF * 2;  // two buffers of 2-byte elements
 };
 
-// 1-D grid over (q-tile, b, h), heaviest (last) query tiles first.
-template <typename T, int D, int QW, int BN>
-__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
+// The running maximum of a row is only raised when a tile's maximum exceeds
+// it by more than 2^kLazyMax (in exp2 units), so most tiles skip the rescale
+// of O; P then stays below 2^kLazyMax, well inside fp16/bf16 range, and the
+// result is the same attention (softmax is invariant to the reference point).
+constexpr float kLazyMax = 8.0f;
+
+// 1-D grid over (q-tile, b, h), heaviest (last) query tiles first.  With NW = 4
+// every thread stages both K and V; with NW = 8 waves 0-3 stage K and waves 4-7
+// stage V.
+template <typename T, int D, int QW, int BN, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(PrefillArgs a) {
   typedef typename Mfma<T>::vec vec8;
   typedef PrefillLds<D, BN> LDS;
-  constexpr int BM = 4 * QW;
+  constexpr int BM = NW * QW;
   constexpr int NT = QW / 16;  // query sub-tiles per wave
   constexpr int KT = BN / 16;  // key sub-tiles per tile
   constexpr int KS = D / 32;   // MFMA k-steps over D
   constexpr int DT = D / 16;   // output sub-tiles over D
   constexpr int PS = BN / 32;  // MFMA k-steps over keys
-  constexpr int KCH = BN * D / 8 / 256;  // 16-B K chunks per thread
+  constexpr int KCH = BN * D / 8 / 256;       // 16-B K chunks per staging thread
   constexpr int VPAIRS = (BN / 4) * (D / 8);  // (4-key group, 8-column slice) pairs
-  static_assert(KCH >= 1 && BN * D / 8 == KCH * 256, "K tile must split evenly");
-  static_assert(VPAIRS <= 256, "V tile too large");
+  constexpr bool SPLIT_STAGE = NW == 8;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(KCH >= 1 && BN * D / 8 == KCH * 256, "K tile must split evenly over 256 threads");
+  static_assert(VPAIRS <= 256 && VPAIRS % 64 == 0, "V tile must cover whole waves");
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T *smem = reinterpret_cast<T *>(smem_raw);
@@ -126,6 +140,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int lg = lane >> 4;
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * QW;
+  // staging roles
+  const int stid = SPLIT_STAGE ? (tid & 255) : tid;
+  const bool stage_k = SPLIT_STAGE ? (tid < 256) : true;
+  const bool stage_v = (SPLIT_STAGE ? (tid >= 256) : true) && stid < VPAIRS;
 
   const T *qb = (const T *)a.q + (size_t)bh * Tn * D;
   const T *kb = (const T *)a.k + (size_t)(b * a.kv_heads + g) * Tn * D;
@@ -139,14 +157,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   vec8 qf[NT][KS];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int row = qw0 + nt * 16 + l16;
+    const int row = min(qw0 + nt * 16 + l16, Tn - 1);  // rows past T are never stored
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (row < Tn)
-        qf[nt][ks] = *(const vec8 *)(qb + (size_t)row * D + ks * 32 + lg * 8);
-      else
-        qf[nt][ks] = vec8{};
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[nt][ks] = *(const vec8 *)(qb + (size_t)row * D + ks * 32 + lg * 8);
   }
 
   float4_t oacc[DT][NT];
@@ -162,77 +175,92 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int kv_end = min(q0 + BM, Tn);
   const int n_tiles = (kv_end + BN - 1) / BN;
 
-  uint4 kreg[KCH];
-  uint4 vreg[4];
-  const int v_kg = tid % (BN / 4);
-  const int v_ds = tid / (BN / 4);
+  u32x4 kreg[KCH];
+  u32x4 vreg[4];
+  const int v_kg = stid % (BN / 4);
+  const int v_ds = stid / (BN / 4);
 
+  // Global loads of one K/V tile into registers.  Keys past T are clamped to
+  // the last key (always in bounds) and masked in the scores, so the loads
+  // carry no per-lane branches.
   auto load_tile = [&](int j) {
     const int k0 = j * BN;
+    if (stage_k) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = c * 256 + tid;
-      const int row = idx / (D / 8);
-      const int col = (idx % (D / 8)) * 8;
-      const int key = k0 + row;
-      if (key < Tn) {
-        kreg[c] = *(const uint4 *)(kb + (size_t)key * D + col);
-        if (writer && key >= q0) *(uint4 *)(ckb + (size_t)key * D + col) = kreg[c];
-      } else {
-        kreg[c] = make_uint4(0, 0, 0, 0);
+      for (int c = 0; c < KCH; ++c) {
+        const int idx = c * 256 + stid;
+        const int key = min(k0 + idx / (D / 8), Tn - 1);
+        kreg[c] = *(const u32x4 *)(kb + (size_t)key * D + (idx % (D / 8)) * 8);
       }
     }
-    if (tid < VPAIRS) {
+    if (stage_v) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 4 * v_kg + r;
-        if (key < Tn) {
-          vreg[r] = *(const uint4 *)(vb + (size_t)key * D + v_ds * 8);
-          if (writer && key >= q0) *(uint4 *)(cvb + (size_t)key * D + v_ds * 8) = vreg[r];
-        } else {
-          vreg[r] = make_uint4(0, 0, 0, 0);
-        }
+        const int key = min(k0 + 4 * v_kg + r, Tn - 1);
+        vreg[r] = *(const u32x4 *)(vb + (size_t)key * D + v_ds * 8);
       }
     }
   };
 
-  auto store_tile = [&](int buf) {
+  // Registers -> LDS (V transposed); the rows of this workgroup's own query
+  // range also go to the cache (bit copies), by the first query head of
+  // each KV group.
+  auto store_tile = [&](int j, int buf) {
+    const int k0 = j * BN;
     T *Ks = smem + buf * LDS::BUF;
     T *Vt = Ks + LDS::K_ELEMS;
+    const bool to_cache = writer && k0 + BN > q0;  // workgroup-uniform
+    if (stage_k) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = c * 256 + tid;
-      const int row = idx / (D / 8);
-      const int col = (idx % (D / 8)) * 8;
-      *(uint4 *)(Ks + row * LDS::KSTR + col) = kreg[c];
+      for (int c = 0; c < KCH; ++c) {
+        const int idx = c * 256 + stid;
+        *(u32x4 *)(Ks + (idx / (D / 8)) * LDS::KSTR + (idx % (D / 8)) * 8) = kreg[c];
+      }
+      if (to_cache) {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+          const int idx = c * 256 + stid;
+          const int key = k0 + idx / (D / 8);
+          if (key >= q0 && key < Tn) *(u32x4 *)(ckb + (size_t)key * D + (idx % (D / 8)) * 8) = kreg[c];
+        }
+      }
     }
-    if (tid < VPAIRS) {
+    if (stage_v) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1;
-        const uint32_t r0 = word4(vreg[0], w), r1 = word4(vreg[1], w);
-        const uint32_t r2 = word4(vreg[2], w), r3 = word4(vreg[3], w);
-        uint2 out;
+        const uint32_t r0 = vreg[0][w], r1 = vreg[1][w];
+        const uint32_t r2 = vreg[2][w], r3 = vreg[3][w];
+        u32x2 out;
         if (e & 1) {
-          out.x = (r0 >> 16) | (r1 & 0xffff0000u);
-          out.y = (r2 >> 16) | (r3 & 0xffff0000u);
+          out[0] = (r0 >> 16) | (r1 & 0xffff0000u);
+          out[1] = (r2 >> 16) | (r3 & 0xffff0000u);
         } else {
-          out.x = (r0 & 0xffffu) | (r1 << 16);
-          out.y = (r2 & 0xffffu) | (r3 << 16);
+          out[0] = (r0 & 0xffffu) | (r1 << 16);
+          out[1] = (r2 & 0xffffu) | (r3 << 16);
         }
-        *(uint2 *)(Vt + (v_ds * 8 + e) * LDS::VSTR + 4 * v_kg) = out;
+        *(u32x2 *)(Vt + (v_ds * 8 + e) * LDS::VSTR + 4 * v_kg) = out;
+      }
+      if (to_cache) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + 4 * v_kg + r;
+          if (key >= q0 && key < Tn) *(u32x4 *)(cvb + (size_t)key * D + v_ds * 8) = vreg[r];
+        }
       }
     }
   };
 
   load_tile(0);
-  store_tile(0);
+  store_tile(0, 0);
   __syncthreads();
 
   const float c = a.scale_log2;
   for (int j = 0; j < n_tiles; ++j) {
     const int buf = j & 1;
     if (j + 1 < n_tiles) load_tile(j + 1);
+    // keep the next tile's loads ahead of this tile's math
+    __builtin_amdgcn_sched_barrier(0);
 
     const int k0 = j * BN;
     if (k0 <= qw0 + QW - 1) {  // wave-uniform: this tile has keys some row of the wave sees
@@ -252,8 +280,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
           for (int nt = 0; nt < NT; ++nt) s[kt][nt] = Mfma<T>::mma(ka, qf[nt][ks], s[kt][nt]);
         }
       }
-      // causal mask: lane holds S^T[key = k0 + 16kt + 4lg + i][query = qw0 + 16nt + l16]
+      // causal mask (diagonal tiles only): lane holds
+      // S^T[key = k0 + 16kt + 4lg + i][query = qw0 + 16nt + l16]
       if (k0 + BN - 1 > qw0) {
+        asm volatile("" ::);  // diagonal tiles only: keep it a real branch
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -277,10 +307,18 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][nt][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // tile 0 holds key 0, visible to every row, so m is finite from then on
-        const float mn = fmaxf(mrow[nt], mx * c);
-        const float al = fast_exp2(mrow[nt] - mn);
-        mrow[nt] = mn;
+        const float mx2 = mx * c;
+        // tile 0 holds key 0, visible to every row, so m is finite after it
+        if (__any(mx2 > mrow[nt] + kLazyMax)) {
+          asm volatile("" ::);  // rare: keep it a real branch
+          const float mn = fmaxf(mrow[nt], mx2);
+          const float al = fast_exp2(mrow[nt] - mn);
+          mrow[nt] = mn;
+          lrow[nt] *= al;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] *= al;
+        }
+        const float mn = mrow[nt];
         float ls = 0.f;
         if constexpr (Mfma<T>::kSplitP) {
 #pragma unroll
@@ -305,9 +343,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
           for (int ps = 0; ps < PS; ++ps) ls = Mfma<T>::sum8(pb[ps][nt], ls);
         }
-        lrow[nt] = fmaf(lrow[nt], al, ls);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] *= al;
+        lrow[nt] += ls;
       }
       // O^T += V^T P^T ; A operand: V^T[d][keys of this lane's k-slots]
 #pragma unroll
@@ -315,9 +351,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const T *vrow = Vt + (dt * 16 + l16) * LDS::VSTR + ps * 32 + lg * 4;
-          const uint2 lo = *(const uint2 *)vrow;
-          const uint2 hi = *(const uint2 *)(vrow + 16);
-          const uint4 raw = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          const u32x2 lo = *(const u32x2 *)vrow;
+          const u32x2 hi = *(const u32x2 *)(vrow + 16);
+          const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
           const vec8 va = __builtin_bit_cast(vec8, raw);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
@@ -328,7 +364,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       }
     }
 
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+    if (j + 1 < n_tiles) store_tile(j + 1, buf ^ 1);
     __syncthreads();
   }
 
@@ -338,6 +374,365 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     float lt = lrow[nt] + __shfl_xor(lrow[nt], 16);
     lt += __shfl_xor(lt, 32);
     const float inv = 1.0f / lt;
+    const int qr = qw0 + nt * 16 + l16;
+    if (qr < Tn) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        store4(a.o, ((size_t)bh * Tn + qr) * D + dt * 16 + lg * 4, oacc[dt][nt], inv, a.o_dt);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pipelined kernel
+// Software-pipelined variant: while the vector ALUs turn the scores of tile j
+// into P (max, exp2, rounding, row sums), the matrix cores already compute the
+// scores of tile j+1; then P_j V_j runs.  K and V live in separate two-deep
+// LDS rings: iteration j reads K_{j+1} and V_j and stages K_{j+2} and V_{j+1},
+// so a single barrier per tile suffices.  Cross-lane row maxima use the
+// permlane swaps (no LDS traffic).  The rare branches (lazy rescale of O, the
+// causal mask of a wave's diagonal tile) sit between the overlapped blocks.
+template <int D, int BN>
+struct PipeLds {
+  static constexpr int KSTR = D + 8;   // K row stride (elements)
+  static constexpr int VSTR = BN + 4;  // V^T row stride (elements)
+  static constexpr int K_ELEMS = BN * KSTR;
+  static constexpr int V_ELEMS = D * VSTR;
+  static constexpr size_t BYTES = (size_t)(2 * K_ELEMS + 2 * V_ELEMS) * 2;
+};
+
+// x combined over the four lanes l, l^16, l^32, l^48 (the lanes holding one query column)
+template <bool MAX>
+__device__ __forceinline__ float across_lg(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = MAX ? fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])) : __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return MAX ? fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])) : __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <typename T, int D, int QW, int BN, int NW>
+__global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefill_pipe_kernel(PrefillArgs a) {
+  typedef typename Mfma<T>::vec vec8;
+  typedef PipeLds<D, BN> LDS;
+  constexpr int BM = NW * QW;
+  constexpr int NT = QW / 16;
+  constexpr int KT = BN / 16;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int PS = BN / 32;
+  constexpr int KCH = BN * D / 8 / 256;
+  constexpr int VPAIRS = (BN / 4) * (D / 8);
+  constexpr bool SPLIT_STAGE = NW == 8;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(QW <= BN && BN % QW == 0, "a wave's rows fall in one key tile");
+  static_assert(KCH >= 1 && BN * D / 8 == KCH * 256, "K tile must split evenly over 256 threads");
+  static_assert(VPAIRS <= 256 && VPAIRS % 64 == 0, "V tile must cover whole waves");
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T *const Kbuf = reinterpret_cast<T *>(smem_raw);  // [2][BN][KSTR]
+  T *const Vbuf = Kbuf + 2 * LDS::K_ELEMS;         // [2][D][VSTR]
+
+  const int Tn = a.T;
+  const int H = a.q_heads;
+  const int G = H / a.kv_heads;
+  const int n_qt = (Tn + BM - 1) / BM;
+  const int BH = a.batch * H;
+  const int qt = n_qt - 1 - (int)(blockIdx.x / BH);
+  const int bh = blockIdx.x % BH;
+  const int b = bh / H;
+  const int h = bh - b * H;
+  const int g = h / G;
+  const bool writer = (h - g * G) == 0;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+  const int q0 = qt * BM;
+  const int qw0 = q0 + wave * QW;
+  const int dw = qw0 / BN;  // this wave's diagonal tile; tiles after it are never needed
+  const int stid = SPLIT_STAGE ? (tid & 255) : tid;
+  const bool stage_k = SPLIT_STAGE ? (tid < 256) : true;
+  const bool stage_v = (SPLIT_STAGE ? (tid >= 256) : true) && stid < VPAIRS;
+
+  const T *qb = (const T *)a.q + (size_t)bh * Tn * D;
+  const T *kb = (const T *)a.k + (size_t)(b * a.kv_heads + g) * Tn * D;
+  const T *vb = (const T *)a.v + (size_t)(b * a.kv_heads + g) * Tn * D;
+  T *ckb = (T *)a.cache_k + (size_t)(b * a.kv_heads + g) * a.max_T * D;
+  T *cvb = (T *)a.cache_v + (size_t)(b * a.kv_heads + g) * a.max_T * D;
+
+  if (qt == 0 && h == 0 && tid == 0) a.len[b] = Tn;
+
+  vec8 qf[NT][KS];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = min(qw0 + nt * 16 + l16, Tn - 1);  // rows past T are never stored
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[nt][ks] = *(const vec8 *)(qb + (size_t)row * D + ks * 32 + lg * 8);
+  }
+
+  float4_t oacc[DT][NT];
+  float mrow[NT], lrow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    mrow[nt] = -INFINITY;
+    lrow[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int kv_end = min(q0 + BM, Tn);
+  const int n_tiles = (kv_end + BN - 1) / BN;
+
+  // staging registers: with split staging a thread holds either K or V chunks
+  constexpr int SR = KCH > 4 ? KCH : 4;
+  u32x4 sreg_a[SPLIT_STAGE ? SR : KCH];
+  u32x4 sreg_b[SPLIT_STAGE ? 1 : 4];
+  u32x4 *const kreg = sreg_a;
+  u32x4 *const vreg = SPLIT_STAGE ? sreg_a : sreg_b;
+  const int v_kg = stid % (BN / 4);
+  const int v_ds = stid / (BN / 4);
+
+  // ---- staging: global -> registers (keys past T clamped, masked later) -> LDS (+ cache rows)
+  auto load_k = [&](int t) {
+    if (stage_k) {
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) {
+        const int idx = c * 256 + stid;
+        const int key = min(t * BN + idx / (D / 8), Tn - 1);
+        kreg[c] = *(const u32x4 *)(kb + (size_t)key * D + (idx % (D / 8)) * 8);
+      }
+    }
+  };
+  auto load_v = [&](int t) {
+    if (stage_v) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = min(t * BN + 4 * v_kg + r, Tn - 1);
+        vreg[r] = *(const u32x4 *)(vb + (size_t)key * D + v_ds * 8);
+      }
+    }
+  };
+  auto store_k = [&](int t, int slot) {
+    if (stage_k) {
+      T *Ks = Kbuf + slot * LDS::K_ELEMS;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) {
+        const int idx = c * 256 + stid;
+        *(u32x4 *)(Ks + (idx / (D / 8)) * LDS::KSTR + (idx % (D / 8)) * 8) = kreg[c];
+      }
+      if (writer && t * BN + BN > q0) {  // workgroup-uniform
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+          const int idx = c * 256 + stid;
+          const int key = t * BN + idx / (D / 8);
+          if (key >= q0 && key < Tn) *(u32x4 *)(ckb + (size_t)key * D + (idx % (D / 8)) * 8) = kreg[c];
+        }
+      }
+    }
+  };
+  auto store_v = [&](int t, int slot) {
+    if (stage_v) {
+      T *Vt = Vbuf + slot * LDS::V_ELEMS;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        const uint32_t r0 = vreg[0][w], r1 = vreg[1][w];
+        const uint32_t r2 = vreg[2][w], r3 = vreg[3][w];
+        u32x2 out;
+        if (e & 1) {
+          out[0] = (r0 >> 16) | (r1 & 0xffff0000u);
+          out[1] = (r2 >> 16) | (r3 & 0xffff0000u);
+        } else {
+          out[0] = (r0 & 0xffffu) | (r1 << 16);
+          out[1] = (r2 & 0xffffu) | (r3 << 16);
+        }
+        *(u32x2 *)(Vt + (v_ds * 8 + e) * LDS::VSTR + 4 * v_kg) = out;
+      }
+      if (writer && t * BN + BN > q0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = t * BN + 4 * v_kg + r;
+          if (key >= q0 && key < Tn) *(u32x4 *)(cvb + (size_t)key * D + v_ds * 8) = vreg[r];
+        }
+      }
+    }
+  };
+
+  // ---- math pieces
+  // S^T (keys x queries) = K_t Q^T from K slot `slot`
+  auto scores = [&](int slot, float4_t (&s)[KT][NT]) {
+    const T *Ks = Kbuf + slot * LDS::K_ELEMS;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) s[kt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const vec8 ka = *(const vec8 *)(Ks + (kt * 16 + l16) * LDS::KSTR + ks * 32 + lg * 8);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) s[kt][nt] = Mfma<T>::mma(ka, qf[nt][ks], s[kt][nt]);
+      }
+    }
+  };
+  // causal mask of the diagonal tile t: lane holds S^T[key = tBN + 16kt + 4lg + i][query = qw0 + 16nt + l16]
+  auto mask = [&](int t, float4_t (&s)[KT][NT]) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t * BN + kt * 16 + lg * 4 + i > qw0 + nt * 16 + l16) s[kt][nt][i] = -INFINITY;
+  };
+  const float c = a.scale_log2;
+  // Row statistics of a score tile: the new running max (raised lazily) and
+  // the rescale factor of O per sub-tile.  Holds every cross-lane operation.
+  auto stats = [&](float4_t (&s)[KT][NT], float (&al)[NT]) -> bool {
+    bool any_resc = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float mx = s[0][nt][0];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][nt][i]);
+      const float mx2 = across_lg<true>(mx) * c;
+      const bool resc = __any(mx2 > mrow[nt] + kLazyMax);  // wave-uniform
+      const float mn = resc ? fmaxf(mrow[nt], mx2) : mrow[nt];
+      al[nt] = fast_exp2(mrow[nt] - mn);
+      mrow[nt] = mn;
+      any_resc |= resc;
+    }
+    return any_resc;
+  };
+  // scores -> P (rounded to T; bf16 as hi + lo) and the row sums over the same P
+  auto expo = [&](float4_t (&s)[KT][NT], vec8 (&pb)[PS][NT], vec8 (&pl)[Mfma<T>::kSplitP ? PS : 1][NT],
+                  const float (&al)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mn = mrow[nt];
+      float ls = 0.f;
+      if constexpr (Mfma<T>::kSplitP) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = fast_exp2(fmaf(s[kt][nt][i], c, -mn));
+            const T hi = (T)p;
+            ls += p;
+            pb[kt >> 1][nt][(kt & 1) * 4 + i] = hi;
+            pl[kt >> 1][nt][(kt & 1) * 4 + i] = (T)(p - (float)hi);
+          }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pb[kt >> 1][nt][(kt & 1) * 4 + i] = (T)fast_exp2(fmaf(s[kt][nt][i], c, -mn));
+#pragma unroll
+        for (int ps = 0; ps < PS; ++ps) ls = Mfma<T>::sum8(pb[ps][nt], ls);
+      }
+      lrow[nt] = fmaf(lrow[nt], al[nt], ls);
+    }
+  };
+  // O^T += V_t^T P^T from V slot `slot`
+  auto pv = [&](int slot, const vec8 (&pb)[PS][NT], const vec8 (&pl)[Mfma<T>::kSplitP ? PS : 1][NT]) {
+    const T *Vt = Vbuf + slot * LDS::V_ELEMS;
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const T *vrow = Vt + (dt * 16 + l16) * LDS::VSTR + ps * 32 + lg * 4;
+        const u32x2 lo = *(const u32x2 *)vrow;
+        const u32x2 hi = *(const u32x2 *)(vrow + 16);
+        const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
+        const vec8 va = __builtin_bit_cast(vec8, raw);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          oacc[dt][nt] = Mfma<T>::mma(va, pb[ps][nt], oacc[dt][nt]);
+          if constexpr (Mfma<T>::kSplitP) oacc[dt][nt] = Mfma<T>::mma(va, pl[ps][nt], oacc[dt][nt]);
+        }
+      }
+    }
+  };
+
+  // ---- prologue: K_0, V_0, K_1 in LDS; S_0
+  load_k(0);
+  load_v(0);
+  store_k(0, 0);
+  store_v(0, 0);
+  if (n_tiles > 1) {
+    load_k(1);
+    store_k(1, 1);
+  }
+  __syncthreads();
+
+  float4_t sa[KT][NT], sb[KT][NT];
+  scores(0, sa);
+  if (dw == 0) mask(0, sa);
+
+  // one tile: softmax(cur) overlapped with nxt = K_{j+1} Q^T, then P V_j
+  auto step = [&](int j, float4_t (&cur)[KT][NT], float4_t (&nxt)[KT][NT]) {
+    if (j + 2 < n_tiles) load_k(j + 2);
+    if (j + 1 < n_tiles) load_v(j + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j <= dw) {  // wave-uniform
+      vec8 pb[PS][NT];
+      vec8 pl[Mfma<T>::kSplitP ? PS : 1][NT];
+      float al[NT];
+      const bool any_resc = stats(cur, al);
+      // The next tile's scores are computed unconditionally (on the wave's
+      // diagonal tile they go unused: the slot then holds finite stale data
+      // or is never read back), which keeps this block free of branches.
+      scores((j + 1) & 1, nxt);
+      expo(cur, pb, pl, al);
+      {
+        // Interleave: K-fragment reads run a few ahead; each score MFMA is
+        // followed by a share of the exponentials' vector instructions.
+        constexpr int NMF = KT * NT * KS;  // score MFMAs
+        constexpr int NRD = KT * KS;       // K-fragment reads
+        constexpr int VPM = (QW * BN / 64 * (Mfma<T>::kSplitP ? 5 : 3)) / NMF + 1;
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+          if (i % NT == NT - 1 && i / NT + 4 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+      if (any_resc) {
+        // rare: keep it a real branch (the compiler would otherwise run the
+        // multiplies on every tile, since al is 1 when nothing moved)
+        asm volatile("" ::);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] *= al[nt];
+      }
+      pv(j & 1, pb, pl);
+      if (j + 1 == dw) {
+        // once per wave; the opaque tile index keeps the compares from being
+        // hoisted out of the loop as invariants
+        int t = j + 1;
+        asm volatile("" : "+v"(t));
+        mask(t, nxt);
+      }
+    }
+    if (j + 2 < n_tiles) store_k(j + 2, j & 1);
+    if (j + 1 < n_tiles) store_v(j + 1, (j + 1) & 1);
+    __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, sa, sb);
+    if (j + 1 < n_tiles) step(j + 1, sb, sa);
+  }
+
+  // normalise and store: lane holds O^T[d = 16dt + 4lg + i][query = qw0 + 16nt + l16]
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float inv = 1.0f / across_lg<false>(lrow[nt]);
     const int qr = qw0 + nt * 16 + l16;
     if (qr < Tn) {
 #pragma unroll
@@ -436,20 +831,44 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   }
 }
 
+// Tile configurations, chosen by measurement on MI355X: the pipelined kernel
+// (8 waves of 32 query rows, 64-key tiles) wins for f16 at D = 128; bf16 there
+// (which carries P as two parts and would spill) and the smaller head dims are
+// faster with the plain kernel (4 waves of 32 rows; 128-key tiles at D = 32).
+template <typename T, int D>
+struct PrefillConfig {
+  static constexpr bool kPipe = std::is_same<T, half_t>::value && D == 128;
+  static constexpr int NW = kPipe ? 8 : 4;
+  static constexpr int QW = 32;
+  static constexpr int BN = (!kPipe && D == 32) ? 128 : 64;
+};
+
 template <typename T, int D>
 static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
-  constexpr int QW = 32, BN = 64, BM = 4 * QW;
-  const size_t lds = PrefillLds<D, BN>::BYTES;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void *)prefill_mfma_kernel<T, D, QW, BN>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  typedef PrefillConfig<T, D> C;
+  constexpr int BM = C::NW * C::QW;
   const int n_qt = (a.T + BM - 1) / BM;
   const dim3 grid((unsigned)n_qt * a.batch * a.q_heads);
-  prefill_mfma_kernel<T, D, QW, BN><<<grid, 256, lds, s>>>(a);
+  static bool attr_done = false;
+  if constexpr (C::kPipe) {
+    auto kern = prefill_pipe_kernel<T, D, C::QW, C::BN, C::NW>;
+    const size_t lds = PipeLds<D, C::BN>::BYTES;
+    if (!attr_done) {
+      hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr_done = true;
+    }
+    kern<<<grid, C::NW * 64, lds, s>>>(a);
+  } else {
+    auto kern = prefill_mfma_kernel<T, D, C::QW, C::BN, C::NW>;
+    const size_t lds = PrefillLds<D, C::BN>::BYTES;
+    if (!attr_done) {
+      hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr_done = true;
+    }
+    kern<<<grid, C::NW * 64, lds, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -204,3 +204,34 @@ def test_config1_end_to_end():
         check_output(od[:, :, 0], fullh[:, :, T + s], dt, f"step {s} vs GPU prefill row")
     c.close()
     c2.close()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_bound_calls_match_regular_calls(dtype):
+    """The pre-bound prefill/append/decode callables enqueue the same C calls: bit-identical outputs."""
+    kv = _kv()
+    B, H, Hkv, D, T = 2, 4, 2, 64, 77
+    say(f"bound calls dtype={dtype}")
+    q = to_dev(_rand((B, H, T + 1, D), dtype, 1), dtype)
+    k = to_dev(_rand((B, Hkv, T + 1, D), dtype, 2), dtype)
+    v = to_dev(_rand((B, Hkv, T + 1, D), dtype, 3), dtype)
+    outs = []
+    for bound in (False, True):
+        c = kv.KVCache(1, B, H, Hkv, D, T + 1, TORCH_DT[dtype])
+        qp, kp, vp = q[:, :, :T].contiguous(), k[:, :, :T].contiguous(), v[:, :, :T].contiguous()
+        qd, kd, vd = q[:, :, T:].contiguous(), k[:, :, T:].contiguous(), v[:, :, T:].contiguous()
+        op = torch.empty_like(qp)
+        od = torch.empty_like(qd)
+        if bound:
+            c.bind_prefill(0, qp, kp, vp, op)()
+            c.bind_append(0, kd, vd)()
+            c.bind_decode(0, qd, od)()
+        else:
+            c.prefill(0, qp, kp, vp, out=op)
+            c.append(0, kd, vd)
+            c.decode(0, qd, out=od)
+        torch.cuda.synchronize()
+        outs.append((host_bits(op), host_bits(od), host_bits(c._buf)))
+        c.close()
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
