@@ -66,9 +66,13 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 constexpr int kMaxSplits = 64;
 
 // decode split size in keys: a function of the head dim and the capacity,
-// never of the batch (so each sequence's result is independent of the others)
+// never of the batch (so each sequence's result is independent of the others).
+// 384 keys (96 KB of K and of V at D = 128) rather than a power of two: with
+// 256- or 512-key splits the concurrently streaming workgroups sit at aligned
+// offsets and the ragged batch-32 decode ran at 4.9 TB/s instead of 6.3 TB/s
+// on MI355X (measured over split sizes 256..576).
 inline int decode_chunk(int head_dim, int max_T) {
-  int c = head_dim <= 32 ? 512 : 256;
+  int c = head_dim <= 32 ? 512 : 384;
   while ((max_T + c - 1) / c > kMaxSplits) c *= 2;
   return c;
 }

@@ -15,11 +15,6 @@
 // exponential is a single exp2.
 #include "common.hpp"
 
-// 16-byte K and V loads per lane per batch (two batches are in flight)
-#ifndef KVATTN_DECODE_U
-#define KVATTN_DECODE_U 4
-#endif
-
 namespace kvattn {
 
 struct TagF32 {
@@ -162,8 +157,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = min(((ib * U + u) * 4 + wave) * RPW + rg, rows - 1);
-      kr[u] = *(const uint4 *)(Kb + (size_t)r * D * ESZ);
-      vr[u] = *(const uint4 *)(Vb + (size_t)r * D * ESZ);
+      // streamed once: nontemporal loads (measured 5% faster than cached ones)
+      const u32x4 tk = __builtin_nontemporal_load((const u32x4 *)(Kb + (size_t)r * D * ESZ));
+      const u32x4 tv = __builtin_nontemporal_load((const u32x4 *)(Vb + (size_t)r * D * ESZ));
+      kr[u] = make_uint4(tk[0], tk[1], tk[2], tk[3]);
+      vr[u] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
     }
   };
   auto compute = [&](int ib, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
@@ -367,7 +365,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
 template <class Tag, int D, int GT>
 static hipError_t launch_gt(const DecodeArgs &a, hipStream_t s) {
-  constexpr int U = KVATTN_DECODE_U;
+  // 16-byte K and V loads per lane per batch (two batches are in flight);
+  // fewer for groups of 8 query heads to stay within 256 registers
+  constexpr int U = GT >= 8 ? 4 : 6;
   const int units = a.q_heads / GT;  // = Hkv * (G / GT)
   decode_kernel<Tag, D, GT, U><<<dim3(a.n_splits, units, a.batch), 256, 0, s>>>(a);
   hipError_t e = hipGetLastError();

@@ -843,6 +843,18 @@ struct PrefillConfig {
   static constexpr int BN = (!kPipe && D == 32) ? 128 : 64;
 };
 
+template <typename KernelT>
+static hipError_t launch_with_lds(KernelT kern, dim3 grid, int threads, size_t lds, hipStream_t s, bool &attr_done,
+                                  const PrefillArgs &a) {
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  kern<<<grid, threads, lds, s>>>(a);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
   typedef PrefillConfig<T, D> C;
@@ -851,25 +863,12 @@ static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)n_qt * a.batch * a.q_heads);
   static bool attr_done = false;
   if constexpr (C::kPipe) {
-    auto kern = prefill_pipe_kernel<T, D, C::QW, C::BN, C::NW>;
-    const size_t lds = PipeLds<D, C::BN>::BYTES;
-    if (!attr_done) {
-      hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      attr_done = true;
-    }
-    kern<<<grid, C::NW * 64, lds, s>>>(a);
+    return launch_with_lds(prefill_pipe_kernel<T, D, C::QW, C::BN, C::NW>, grid, C::NW * 64,
+                           PipeLds<D, C::BN>::BYTES, s, attr_done, a);
   } else {
-    auto kern = prefill_mfma_kernel<T, D, C::QW, C::BN, C::NW>;
-    const size_t lds = PrefillLds<D, C::BN>::BYTES;
-    if (!attr_done) {
-      hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      attr_done = true;
-    }
-    kern<<<grid, C::NW * 64, lds, s>>>(a);
+    return launch_with_lds(prefill_mfma_kernel<T, D, C::QW, C::BN, C::NW>, grid, C::NW * 64,
+                           PrefillLds<D, C::BN>::BYTES, s, attr_done, a);
   }
-  return hipGetLastError();
 }
 
 template <int D>
