@@ -56,6 +56,12 @@ def parse():
     p.add_argument("--skip-gqa", action="store_true")
     p.add_argument("--only", choices=["prefill", "decode", "gqa"], default=None,
                    help="time one phase only (for profiling runs)")
+    p.add_argument("--calibrate", action="store_true",
+                   help="also run a plain 4 GiB read and a 4 GiB fill, whose FETCH_SIZE / WRITE_SIZE counter "
+                        "readings calibrate the counters (for the --pmc runs that produce profiles/traffic.json)")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="read the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE rocprofv3 run of "
+                        "`bench.py --calibrate`, write profiles/traffic.json and exit (no GPU needed)")
     return p.parse_args()
 
 
@@ -65,6 +71,100 @@ def kernel_source_hash(names):
         with open(os.path.join(ROOT, "kv_cached_causal_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+# sources each measured kernel depends on (a traffic figure is dropped once any changes)
+DECODE_SOURCES = ["decode.hip", "common.hpp", "kvattn.hip"]
+PREFILL_SOURCES = ["prefill.hip", "common.hpp"]
+CALIB_BYTES = 4 << 30
+# kernels of each measured launch, by a substring of the demangled or mangled name
+TRAFFIC_KERNELS = {
+    "decode_ragged_b32": (DECODE_SOURCES, ["decode_kernel<kvattn::TagF16, 128, 1,", "decode_merge_kernel<128, 1>"]),
+    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4,", "decode_merge_kernel<128, 4>"]),
+    "prefill_t8192": (PREFILL_SOURCES, ["prefill_pipe_kernelIDF16_Li128"]),
+}
+
+
+def _counter_medians(directory, counter):
+    """Median counter value per kernel name over the dispatches of a rocprofv3 --pmc run."""
+    import csv
+    import glob
+    vals = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: float(np.median(v)) for k, v in vals.items()}
+
+
+def write_traffic(fetch_dir, write_dir):
+    """profiles/traffic.json: HBM bytes per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by the reading for a plain read (write) of CALIB_BYTES bytes in the same run."""
+    fetch = _counter_medians(fetch_dir, "FETCH_SIZE")
+    write = _counter_medians(write_dir, "WRITE_SIZE")
+
+    def pick(table, key):
+        hits = [v for k, v in table.items() if key in k]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {key!r}, found {len(hits)}")
+        return hits[0]
+
+    f_scale = CALIB_BYTES / 1024.0 / pick(fetch, "stream_read_kernel")
+    w_scale = CALIB_BYTES / 1024.0 / pick(write, "FillFunctor<c10::Half>")
+    out = {"calibration": {"bytes": CALIB_BYTES, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                           "note": "FETCH_SIZE scaled by a plain streaming read, WRITE_SIZE by a fill, same run"}}
+    for key, (sources, kernels) in TRAFFIC_KERNELS.items():
+        fb = sum(pick(fetch, k) for k in kernels) * 1024.0 * f_scale
+        wb = sum(pick(write, k) for k in kernels) * 1024.0 * w_scale
+        out[key] = {"source_hash": kernel_source_hash(sources), "kernels": kernels,
+                    "fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
+                    "bytes_per_launch": int(fb + wb)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def measure_read_ceiling(kv, dev, nbytes=CALIB_BYTES, reps=10):
+    """Streaming-read rate of this device (plain read kernel of the library), GB/s."""
+    import ctypes
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(8192, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    fn = kv.lib().kvattn_measure_stream_read
+
+    def run():
+        if fn(ctypes.c_void_p(buf.data_ptr()), nbytes, 8192, ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+            raise RuntimeError("kvattn_measure_stream_read failed")
+    for _ in range(3):
+        run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    rate = nbytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    return rate
+
+
+def calibration_kernels(kv, dev):
+    """A plain read and a fill of CALIB_BYTES each (run under --pmc to calibrate the HBM counters)."""
+    import ctypes
+    buf = torch.empty(CALIB_BYTES // 2, dtype=torch.float16, device=dev)
+    sink = torch.zeros(8192, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    for _ in range(3):
+        if kv.lib().kvattn_measure_stream_read(ctypes.c_void_p(buf.data_ptr()), CALIB_BYTES, 8192,
+                                               ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+            raise RuntimeError("kvattn_measure_stream_read failed")
+        buf.fill_(1.5)
+    torch.cuda.synchronize()
+    del buf, sink
+    torch.cuda.empty_cache()
 
 
 def traffic_from_profiles(kernel_key, src_hash):
@@ -263,6 +363,9 @@ def cpu_baseline():
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
@@ -320,8 +423,8 @@ def main():
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f16", "data": "synthetic"}
-    dec_hash = kernel_source_hash(["decode.hip"])
-    pre_hash = kernel_source_hash(["prefill.hip"])
+    dec_hash = kernel_source_hash(DECODE_SOURCES)
+    pre_hash = kernel_source_hash(PREFILL_SOURCES)
     if dec is not None:
         k_ms = td.mean_ms()
         achieved = dec["bytes_kernel"] / (k_ms * 1e-3) / 1e9
@@ -378,6 +481,13 @@ def main():
         if args.only == "gqa":
             out["value"], out["unit"] = out["decode_gqa"]["value"], "GB/s"
 
+    if args.only is None:
+        ceil = measure_read_ceiling(kv, dev)
+        out["hbm_read_ceiling"] = {"value": round(ceil, 1), "unit": "GB/s", "kernel": "kvattn_measure_stream_read",
+                                   "bytes": CALIB_BYTES,
+                                   "decode_frac_of_ceiling": round(out["roofline"]["achieved"] / ceil, 4)}
+    if args.calibrate:
+        calibration_kernels(kv, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

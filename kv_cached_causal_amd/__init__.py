@@ -48,6 +48,8 @@ _SIGS = {
     "kvattn_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kvattn_measure_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                                  ctypes.c_void_p]),
     "kvattn_last_error": (ctypes.c_char_p, []),
 }
 

@@ -9,13 +9,16 @@ import pytest
 import kv_cached_causal_amd as kv
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kvattn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvattn_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(kvattn_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
@@ -93,3 +96,14 @@ def test_status_strings():
     for s in range(-6, 1):
         assert lib.kvattn_status_string(s)
     assert lib.kvattn_status_string(-99) == b"unknown status"
+
+
+def test_measure_stream_read_validates_on_host():
+    lib = kv.lib()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation first
+    assert lib.kvattn_measure_stream_read(None, 1 << 20, 64, fake, None) == -1
+    assert lib.kvattn_measure_stream_read(fake, 0, 64, fake, None) == -1
+    assert lib.kvattn_measure_stream_read(fake, 100, 64, fake, None) == -1      # not a multiple of 16
+    assert lib.kvattn_measure_stream_read(ctypes.c_void_p((1 << 20) + 4), 1 << 20, 64, fake, None) == -1
+    assert lib.kvattn_measure_stream_read(fake, 1 << 20, 0, fake, None) == -1
+    assert lib.kvattn_measure_stream_read(fake, 1 << 20, 64, None, None) == -1
