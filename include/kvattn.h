@@ -120,6 +120,21 @@ int kvattn_prefill(kvattn_cache *c, int layer, const void *q, const void *k, con
  * max_T. */
 int kvattn_append(kvattn_cache *c, int layer, const void *k_new, const void *v_new, void *stream);
 
+/* Extend one layer by T positions per sequence after its cached prefix: the
+ * chunked prefill of a long prompt (the README's chunked attention equals the
+ * one-shot form for any chunk size) and the multi-token verification step of
+ * its speculative decoding loop (draft tokens checked in one pass; rejected
+ * ones are rolled back with kvattn_cache_set_lengths).  k/v (B,Hkv,T,D) are
+ * copied bit-exactly to cache rows [len[b], len[b] + T); query t of sequence b
+ * (q (B,H,T,D)) sits at position len[b] + t and attends cache rows
+ * 0 .. len[b] + t (the causal mask aligned to the bottom right); o (B,H,T,D)
+ * in o_dtype (cache dtype or F32); then len[b] += T.  Lengths may differ
+ * between sequences and may be 0 (then this is a prefill).  CAPACITY if any
+ * len[b] + T > max_T; T >= 1.  Three kernels are enqueued on `stream` (copy,
+ * attention, length update). */
+int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, const void *v, void *o,
+                  int T, float scale, kvattn_dtype o_dtype, void *stream);
+
 /* Decode of one layer: query q[b,h] (B,H,1,D) sits at position len[b]-1 and
  * attends all len[b] cached keys of its KV head (the causal mask aligned to
  * the bottom right); o (B,H,1,D) in o_dtype (cache dtype or F32).  Lengths are

@@ -45,6 +45,8 @@ _SIGS = {
                        + [ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_append": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p]),
+    "kvattn_extend": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 4
+                      + [ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -200,6 +202,24 @@ class KVCache:
             _check(lib().kvattn_prefill(self._handle, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(out), T,
                                         self._scale(scale), _DT[od], _stream_ptr(self.device)),
                    "kvattn_prefill")
+        return out
+
+    def extend(self, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+               out: torch.Tensor | None = None, scale: float | None = None, out_dtype=None) -> torch.Tensor:
+        """T new positions per sequence after its cached prefix (chunked prefill / multi-token verify)."""
+        B, H, Hkv, D = self.batch, self.q_heads, self.kv_heads, self.head_dim
+        T = q.shape[2] if q.dim() == 4 else -1
+        self._tensor(q, (B, H, T, D), "q")
+        self._tensor(k, (B, Hkv, T, D), "k")
+        self._tensor(v, (B, Hkv, T, D), "v")
+        od = out_dtype or self.dtype
+        if out is None:
+            out = torch.empty((B, H, T, D), dtype=od, device=self.device)
+        self._tensor(out, (B, H, T, D), "out", od)
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_extend(self._handle, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(out), T,
+                                       self._scale(scale), _DT[od], _stream_ptr(self.device)),
+                   "kvattn_extend")
         return out
 
     def append(self, layer: int, k_new: torch.Tensor, v_new: torch.Tensor) -> None:

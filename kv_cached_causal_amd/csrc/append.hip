@@ -35,6 +35,41 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Extend: T rows per (sequence, KV head) copied to cache rows [len[b], len[b] + T)
+// (bit copies); grid (row chunks, Hkv, B).  The lengths are only read here and
+// advanced by add_lengths_kernel once the attention over them has run.
+__global__ __launch_bounds__(256) void extend_copy_kernel(ExtendCopyArgs a) {
+  const int b = blockIdx.z;
+  const int h = blockIdx.y;
+  const int vec_per_row = a.row_bytes >> 4;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= a.T * vec_per_row) return;
+  const int t = idx / vec_per_row;
+  const int w = idx - t * vec_per_row;
+  const int pos = a.len[b] + t;
+  const size_t src = ((size_t)(b * a.kv_heads + h) * a.T + t) * a.row_bytes + (size_t)w * 16;
+  const size_t dst = ((size_t)(b * a.kv_heads + h) * a.max_T + pos) * a.row_bytes + (size_t)w * 16;
+  *reinterpret_cast<uint4 *>(a.k_layer + dst) = *reinterpret_cast<const uint4 *>(a.k_new + src);
+  *reinterpret_cast<uint4 *>(a.v_layer + dst) = *reinterpret_cast<const uint4 *>(a.v_new + src);
+}
+
+hipError_t launch_extend_copy(const ExtendCopyArgs &a, hipStream_t s) {
+  const int vec_per_row = a.row_bytes >> 4;
+  const unsigned chunks = (unsigned)(((size_t)a.T * vec_per_row + 255) / 256);
+  extend_copy_kernel<<<dim3(chunks, a.kv_heads, a.batch), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+__global__ void add_lengths_kernel(int32_t *len, int batch, int T) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) len[b] += T;
+}
+
+hipError_t launch_add_lengths(int32_t *len, int batch, int T, hipStream_t s) {
+  add_lengths_kernel<<<dim3((batch + 255) / 256), dim3(256), 0, s>>>(len, batch, T);
+  return hipGetLastError();
+}
+
 // Lengths travel by value in the kernel arguments, so the caller's host array
 // need not outlive the call and no host-to-device copy is enqueued.
 constexpr int kLenChunk = 256;

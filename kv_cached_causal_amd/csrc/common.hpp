@@ -43,16 +43,28 @@ struct DecodeArgs {
 };
 
 struct PrefillArgs {
-  const void *q;        // (B, H, T, D)
-  const void *k;        // (B, Hkv, T, D)
+  const void *q;        // (B, H, T, D): the T query positions of each sequence
+  const void *k;        // (B, Hkv, kv_rows, D): keys 0 .. off_b + T - 1 of sequence b
   const void *v;
   void *o;              // (B, H, T, D) in o_dtype
   void *cache_k;        // layer's K block (B, Hkv, max_T, D)
   void *cache_v;
   int32_t *len;         // layer's lengths [B]
+  const int32_t *offsets;  // [B] absolute position of query 0 (device), or null for 0
   int batch, q_heads, kv_heads, head_dim, T, max_T;
+  int kv_rows;          // rows per (sequence, KV head) in k/v: T for a prompt, max_T for the cache
+  int write_cache;      // prefill: copy k/v rows [0, T) to the cache and set len = T
   float scale_log2;
   kvattn_dtype dt, o_dt;
+};
+
+struct ExtendCopyArgs {
+  char *k_layer;        // layer's K block (B, Hkv, max_T, D)
+  char *v_layer;
+  const char *k_new;    // (B, Hkv, T, D)
+  const char *v_new;
+  const int32_t *len;   // layer's lengths [B] (not modified)
+  int batch, kv_heads, max_T, row_bytes, T;
 };
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
@@ -60,19 +72,25 @@ hipError_t launch_set_lengths(int32_t *dst, int layers, int batch, const int32_t
                               hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_extend_attention(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_extend_copy(const ExtendCopyArgs &a, hipStream_t s);
+hipError_t launch_add_lengths(int32_t *len, int batch, int T, hipStream_t s);
 
 // decode splits per (sequence, KV head) are capped so the merge keeps its
 // split weights in LDS
 constexpr int kMaxSplits = 64;
 
-// decode split size in keys: a function of the head dim and the capacity,
-// never of the batch (so each sequence's result is independent of the others).
-// 384 keys (96 KB of K and of V at D = 128) rather than a power of two: with
-// 256- or 512-key splits the concurrently streaming workgroups sit at aligned
-// offsets and the ragged batch-32 decode ran at 4.9 TB/s instead of 6.3 TB/s
-// on MI355X (measured over split sizes 256..576).
-inline int decode_chunk(int head_dim, int max_T) {
-  int c = head_dim <= 32 ? 512 : 384;
+// decode split size in keys: a function of the head dim, the query-group size
+// and the capacity, never of the batch (so each sequence's result is
+// independent of the others).  384 keys (96 KB of K and of V at D = 128)
+// rather than a power of two: with 256- or 512-key splits the concurrently
+// streaming workgroups sit at aligned offsets and the ragged batch-32 decode
+// ran at 4.9 TB/s instead of 6.3 TB/s on MI355X (measured over split sizes
+// 256..576).  Groups of >= 4 query heads per KV head do four times the
+// arithmetic per byte and run best with 768-key splits (GQA 32/8: 58.5 ->
+// 54.9 us per layer).
+inline int decode_chunk(int head_dim, int group, int max_T) {
+  int c = head_dim <= 32 ? 512 : (group >= 4 ? 768 : 384);
   while ((max_T + c - 1) / c > kMaxSplits) c *= 2;
   return c;
 }

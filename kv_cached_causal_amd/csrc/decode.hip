@@ -365,9 +365,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
 template <class Tag, int D, int GT>
 static hipError_t launch_gt(const DecodeArgs &a, hipStream_t s) {
-  // 16-byte K and V loads per lane per batch (two batches are in flight);
-  // fewer for groups of 8 query heads to stay within 256 registers
-  constexpr int U = GT >= 8 ? 4 : 6;
+  // 16-byte K and V loads per lane per batch (two batches are in flight):
+  // six for one or two query heads per workgroup, four for larger groups
+  // (measured; and groups of 8 would not fit 256 registers with six)
+  constexpr int U = GT >= 4 ? 4 : 6;
   const int units = a.q_heads / GT;  // = Hkv * (G / GT)
   decode_kernel<Tag, D, GT, U><<<dim3(a.n_splits, units, a.batch), 256, 0, s>>>(a);
   hipError_t e = hipGetLastError();

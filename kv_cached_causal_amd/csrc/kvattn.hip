@@ -116,7 +116,7 @@ int kvattn_cache_alloc(kvattn_cache **out, int layers, int batch, int q_heads, i
   c->elem = elem_bytes(dt);
   c->payload_bytes = bytes;
   c->layer_bytes = bytes / layers;
-  c->chunk = decode_chunk(head_dim, max_T);
+  c->chunk = decode_chunk(head_dim, q_heads / kv_heads, max_T);
   c->n_splits = (max_T + c->chunk - 1) / c->chunk;
   c->h_len.assign((size_t)layers * batch, 0);
 
@@ -228,18 +228,82 @@ int kvattn_prefill(kvattn_cache *c, int layer, const void *q, const void *k, con
   a.cache_k = layer_k(c, layer);
   a.cache_v = layer_v(c, layer);
   a.len = c->d_len + (size_t)layer * c->batch;
+  a.offsets = nullptr;
   a.batch = c->batch;
   a.q_heads = c->q_heads;
   a.kv_heads = c->kv_heads;
   a.head_dim = c->head_dim;
   a.T = T;
   a.max_T = c->max_T;
+  a.kv_rows = T;
+  a.write_cache = 1;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dt = c->dt;
   a.o_dt = o_dtype;
   hipError_t e = launch_prefill(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   for (int b = 0; b < c->batch; ++b) c->h_len[(size_t)layer * c->batch + b] = T;
+  return KVATTN_OK;
+}
+
+int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, const void *v, void *o,
+                  int T, float scale, kvattn_dtype o_dtype, void *stream) {
+  int rc = check_layer(c, layer);
+  if (rc) return rc;
+  if (!q || !k || !v || !o) return KVATTN_ERR_INVALID_ARG;
+  if (T <= 0 || !(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
+  if (!valid_out_dtype(c, o_dtype)) return KVATTN_ERR_UNSUPPORTED;
+  int32_t *hl = &c->h_len[(size_t)layer * c->batch];
+  for (int b = 0; b < c->batch; ++b)
+    if (hl[b] > c->max_T - T) return KVATTN_ERR_CAPACITY;
+  rc = check_device(c);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t *len = c->d_len + (size_t)layer * c->batch;
+
+  // 1. the new K/V rows go to cache rows [len[b], len[b] + T)
+  ExtendCopyArgs cp;
+  cp.k_layer = layer_k(c, layer);
+  cp.v_layer = layer_v(c, layer);
+  cp.k_new = (const char *)k;
+  cp.v_new = (const char *)v;
+  cp.len = len;
+  cp.batch = c->batch;
+  cp.kv_heads = c->kv_heads;
+  cp.max_T = c->max_T;
+  cp.row_bytes = c->head_dim * c->elem;
+  cp.T = T;
+  hipError_t e = launch_extend_copy(cp, st);
+  if (e != hipSuccess) return hip_fail(e, "extend copy launch");
+
+  // 2. attention of the T new queries over cache rows [0, len[b] + T)
+  PrefillArgs a;
+  a.q = q;
+  a.k = layer_k(c, layer);
+  a.v = layer_v(c, layer);
+  a.o = o;
+  a.cache_k = layer_k(c, layer);
+  a.cache_v = layer_v(c, layer);
+  a.len = len;
+  a.offsets = len;
+  a.batch = c->batch;
+  a.q_heads = c->q_heads;
+  a.kv_heads = c->kv_heads;
+  a.head_dim = c->head_dim;
+  a.T = T;
+  a.max_T = c->max_T;
+  a.kv_rows = c->max_T;
+  a.write_cache = 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dt = c->dt;
+  a.o_dt = o_dtype;
+  e = launch_extend_attention(a, st);
+  if (e != hipSuccess) return hip_fail(e, "extend attention launch");
+
+  // 3. commit: len[b] += T
+  e = launch_add_lengths(len, c->batch, T, st);
+  if (e != hipSuccess) return hip_fail(e, "extend length update launch");
+  for (int b = 0; b < c->batch; ++b) hl[b] += T;
   return KVATTN_OK;
 }
 

@@ -146,12 +146,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
   const bool stage_v = (SPLIT_STAGE ? (tid >= 256) : true) && stid < VPAIRS;
 
   const T *qb = (const T *)a.q + (size_t)bh * Tn * D;
-  const T *kb = (const T *)a.k + (size_t)(b * a.kv_heads + g) * Tn * D;
-  const T *vb = (const T *)a.v + (size_t)(b * a.kv_heads + g) * Tn * D;
+  // query row i sits at absolute position off + i and sees keys 0 .. off + i
+  const int off = a.offsets ? a.offsets[b] : 0;
+  const int last_key = off + Tn - 1;
+  const T *kb = (const T *)a.k + (size_t)(b * a.kv_heads + g) * a.kv_rows * D;
+  const T *vb = (const T *)a.v + (size_t)(b * a.kv_heads + g) * a.kv_rows * D;
   T *ckb = (T *)a.cache_k + (size_t)(b * a.kv_heads + g) * a.max_T * D;
   T *cvb = (T *)a.cache_v + (size_t)(b * a.kv_heads + g) * a.max_T * D;
 
-  if (qt == 0 && h == 0 && tid == 0) a.len[b] = Tn;
+  if (a.write_cache && qt == 0 && h == 0 && tid == 0) a.len[b] = Tn;
 
   // query fragments (B operand of S^T = K Q^T): lane holds 8 columns of one row
   vec8 qf[NT][KS];
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
     for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int kv_end = min(q0 + BM, Tn);
+  const int kv_end = off + min(q0 + BM, Tn);
   const int n_tiles = (kv_end + BN - 1) / BN;
 
   u32x4 kreg[KCH];
@@ -189,14 +192,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
         const int idx = c * 256 + stid;
-        const int key = min(k0 + idx / (D / 8), Tn - 1);
+        const int key = min(k0 + idx / (D / 8), last_key);
         kreg[c] = *(const u32x4 *)(kb + (size_t)key * D + (idx % (D / 8)) * 8);
       }
     }
     if (stage_v) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = min(k0 + 4 * v_kg + r, Tn - 1);
+        const int key = min(k0 + 4 * v_kg + r, last_key);
         vreg[r] = *(const u32x4 *)(vb + (size_t)key * D + v_ds * 8);
       }
     }
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
     const int k0 = j * BN;
     T *Ks = smem + buf * LDS::BUF;
     T *Vt = Ks + LDS::K_ELEMS;
-    const bool to_cache = writer && k0 + BN > q0;  // workgroup-uniform
+    const bool to_cache = a.write_cache && writer && k0 + BN > q0;  // workgroup-uniform
     if (stage_k) {
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     const int k0 = j * BN;
-    if (k0 <= qw0 + QW - 1) {  // wave-uniform: this tile has keys some row of the wave sees
+    if (k0 <= off + qw0 + QW - 1) {  // wave-uniform: this tile has keys some row of the wave sees
       const T *Ks = smem + buf * LDS::BUF;
       const T *Vt = Ks + LDS::K_ELEMS;
       float4_t s[KT][NT];
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
       }
       // causal mask (diagonal tiles only): lane holds
       // S^T[key = k0 + 16kt + 4lg + i][query = qw0 + 16nt + l16]
-      if (k0 + BN - 1 > qw0) {
+      if (k0 + BN - 1 > off + qw0) {
         asm volatile("" ::);  // diagonal tiles only: keep it a real branch
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int key = k0 + kt * 16 + lg * 4 + i;
-              const int qr = qw0 + nt * 16 + l16;
+              const int qr = off + qw0 + nt * 16 + l16;
               if (key > qr) s[kt][nt][i] = -INFINITY;
             }
       }
@@ -765,11 +768,12 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   const int row = q0 + threadIdx.x;
 
   const float *qb = (const float *)a.q + (size_t)bh * Tn * D;
-  const float *kb = (const float *)a.k + (size_t)(b * a.kv_heads + g) * Tn * D;
-  const float *vb = (const float *)a.v + (size_t)(b * a.kv_heads + g) * Tn * D;
+  const int off = a.offsets ? a.offsets[b] : 0;  // absolute position of query row 0
+  const float *kb = (const float *)a.k + (size_t)(b * a.kv_heads + g) * a.kv_rows * D;
+  const float *vb = (const float *)a.v + (size_t)(b * a.kv_heads + g) * a.kv_rows * D;
   float *ckb = (float *)a.cache_k + (size_t)(b * a.kv_heads + g) * a.max_T * D;
   float *cvb = (float *)a.cache_v + (size_t)(b * a.kv_heads + g) * a.max_T * D;
-  if (qt == 0 && h == 0 && threadIdx.x == 0) a.len[b] = Tn;
+  if (a.write_cache && qt == 0 && h == 0 && threadIdx.x == 0) a.len[b] = Tn;
 
   float qr[D], o[D];
 #pragma unroll
@@ -779,17 +783,17 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   }
   float m = -INFINITY, l = 0.f;
   const float c = a.scale_log2;
-  const int kv_end = min(q0 + BMF, Tn);
+  const int kv_end = off + min(q0 + BMF, Tn);
   for (int k0 = 0; k0 < kv_end; k0 += BNF) {
     __syncthreads();
     for (int i = threadIdx.x; i < BNF * D; i += 64) {
       const int r = i / D, d = i - r * D;
       const int key = k0 + r;
       float kx = 0.f, vx = 0.f;
-      if (key < Tn) {
+      if (key < off + Tn) {
         kx = kb[(size_t)key * D + d];
         vx = vb[(size_t)key * D + d];
-        if (writer && key >= q0) {
+        if (a.write_cache && writer && key >= q0) {
           // bit copy: reinterpret, never round
           ((uint32_t *)ckb)[(size_t)key * D + d] = __float_as_uint(kx);
           ((uint32_t *)cvb)[(size_t)key * D + d] = __float_as_uint(vx);
@@ -806,7 +810,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
       float acc = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) acc = fmaf(qr[d], Ks[j][d], acc);
-      s[j] = (k0 + j <= row) ? acc * c : -INFINITY;
+      s[j] = (k0 + j <= off + row) ? acc * c : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }
     const float mn = fmaxf(m, mx);
@@ -876,6 +880,40 @@ static hipError_t launch_f32(const PrefillArgs &a, hipStream_t s) {
   const int n_qt = (a.T + 63) / 64;
   prefill_f32_kernel<D><<<dim3((unsigned)n_qt * a.batch * a.q_heads), 64, 0, s>>>(a);
   return hipGetLastError();
+}
+
+// Extend (queries after a cached prefix, K/V read from the cache): the plain
+// kernel for every 16-bit type and head dim, the vector kernel for fp32.
+template <typename T, int D>
+static hipError_t launch_extend_mfma(const PrefillArgs &a, hipStream_t s) {
+  constexpr int NW = 4, QW = 32, BN = D == 32 ? 128 : 64, BM = NW * QW;
+  const int n_qt = (a.T + BM - 1) / BM;
+  static bool attr_done = false;
+  return launch_with_lds(prefill_mfma_kernel<T, D, QW, BN, NW>, dim3((unsigned)n_qt * a.batch * a.q_heads),
+                         NW * 64, PrefillLds<D, BN>::BYTES, s, attr_done, a);
+}
+
+hipError_t launch_extend_attention(const PrefillArgs &a, hipStream_t s) {
+  if (a.dt == KVATTN_F32) {
+    switch (a.head_dim) {
+      case 32: return launch_f32<32>(a, s);
+      case 64: return launch_f32<64>(a, s);
+      case 128: return launch_f32<128>(a, s);
+    }
+  } else if (a.dt == KVATTN_F16) {
+    switch (a.head_dim) {
+      case 32: return launch_extend_mfma<half_t, 32>(a, s);
+      case 64: return launch_extend_mfma<half_t, 64>(a, s);
+      case 128: return launch_extend_mfma<half_t, 128>(a, s);
+    }
+  } else if (a.dt == KVATTN_BF16) {
+    switch (a.head_dim) {
+      case 32: return launch_extend_mfma<bf16_t, 32>(a, s);
+      case 64: return launch_extend_mfma<bf16_t, 64>(a, s);
+      case 128: return launch_extend_mfma<bf16_t, 128>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {

@@ -6,6 +6,7 @@ from .attention import (  # noqa: F401
     chunked,
     decode_cached,
     decode_recompute,
+    extend,
     kv_bytes,
     kv_head_of,
     naive_causal,

@@ -204,6 +204,37 @@ def decode_recompute(q_hist: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# extend: T new positions after a cached prefix (chunked prefill, multi-token
+# verification of the README's speculative loop; chapter 9.3's cache)
+# --------------------------------------------------------------------------
+def extend(q_new: np.ndarray, cache_k: np.ndarray, cache_v: np.ndarray, offsets,
+           scale: float) -> np.ndarray:
+    """Attention of T new queries appended after a cached prefix.
+
+    q_new (B, H, T, D); cache_k/v (B, Hkv, >= off_b + T, D) already hold the
+    prefix in rows [0, off_b) and the T new keys/values in rows [off_b,
+    off_b + T).  New query t of sequence b sits at absolute position off_b + t
+    and sees keys 0 .. off_b + t (the causal mask aligned to the bottom right).
+    Every row goes through ``attend_row``, the routine of the decode paths.
+    """
+    q_new = np.asarray(q_new, dtype=np.float64)
+    B, H, T, D = q_new.shape
+    Hkv = cache_k.shape[1]
+    out = np.empty((B, H, T, cache_v.shape[-1]), dtype=np.float64)
+    for b in range(B):
+        off = int(offsets[b])
+        if off < 0 or off + T > cache_k.shape[2]:
+            raise ValueError("new positions must fit the cache")
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            for t in range(T):
+                n = off + t + 1
+                out[b, h, t] = attend_row(q_new[b, h, t], np.asarray(cache_k[b, g, :n], np.float64),
+                                          np.asarray(cache_v[b, g, :n], np.float64), scale)
+    return out
+
+
+# --------------------------------------------------------------------------
 # textbook brute force (pure Python loops)
 # --------------------------------------------------------------------------
 def brute(q, k, v, scale: float) -> list:
@@ -243,8 +274,8 @@ class CacheModel:
     Storage arrays keep the raw storage dtype (bf16 as uint16 bits), laid out
     [layer][B][Hkv][max_T][D] for K and for V, plus lengths[layer][B].
     prefill writes rows [0, T) and sets the length to T; append writes one row
-    at the current length and increments it; set_lengths truncates or rolls
-    back.  Rows at or past a sequence's length are never read.
+    at the current length and increments it; extend writes T rows there and
+    advances it by T; set_lengths truncates or rolls back.  Rows at or past a sequence's length are never read.
     """
 
     def __init__(self, layers, batch, kv_heads, head_dim, max_T, storage_dtype):
@@ -272,6 +303,17 @@ class CacheModel:
             self.k[layer, b, :, pos] = k_new[b, :, 0]
             self.v[layer, b, :, pos] = v_new[b, :, 0]
         self.lengths[layer] += 1
+
+    def extend(self, layer, k_new, v_new):
+        """Write T rows per sequence at its current length, then advance it by T."""
+        T = k_new.shape[2]
+        if (self.lengths[layer] + T > self.max_T).any():
+            raise RuntimeError("cache full")
+        for b in range(self.k.shape[1]):
+            pos = self.lengths[layer, b]
+            self.k[layer, b, :, pos:pos + T] = k_new[b]
+            self.v[layer, b, :, pos:pos + T] = v_new[b]
+        self.lengths[layer] += T
 
     def set_lengths(self, layer, lengths):
         lengths = np.asarray(lengths, dtype=np.int64)

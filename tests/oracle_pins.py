@@ -242,9 +242,51 @@ def check_cached_equals_recompute(decode_cached=oracle.decode_cached,
             assert np.array_equal(got, ref), f"cached != recompute at step {s}, B={B}"
 
 
+def check_extend_matches_prefill_rows(extend=oracle.extend, naive=oracle.naive_causal):
+    """New positions after ragged cached prefixes equal the matching rows of one
+    causal prefill over the whole sequence (matrix form, written independently)."""
+    B, H, Hkv, S, D, T = 3, 4, 2, 23, 6, 5
+    q = _rand((B, H, S, D), 141)
+    k = _rand((B, Hkv, S, D), 142)
+    v = _rand((B, Hkv, S, D), 143)
+    full = naive(q, k, v, 0.4)
+    offsets = [0, 9, S - T]
+    q_new = np.stack([q[b, :, o:o + T] for b, o in enumerate(offsets)])
+    got = extend(q_new, k, v, offsets, 0.4)
+    for b, o in enumerate(offsets):
+        np.testing.assert_allclose(got[b], full[b, :, o:o + T], rtol=1e-12, atol=1e-13)
+
+
+def check_chunked_prefill_by_extend(extend=oracle.extend, naive=oracle.naive_causal):
+    """A prompt fed in chunks of any sizes (the README's chunked form) equals one prefill."""
+    B, H, Hkv, S, D = 2, 2, 1, 19, 5
+    q = _rand((B, H, S, D), 151)
+    k = _rand((B, Hkv, S, D), 152)
+    v = _rand((B, Hkv, S, D), 153)
+    full = naive(q, k, v, 0.5)
+    for sizes in ([S], [1] * S, [5, 1, 7, 6], [18, 1]):
+        outs, off = [], 0
+        for n in sizes:
+            outs.append(extend(q[:, :, off:off + n], k, v, [off] * B, 0.5))
+            off += n
+        np.testing.assert_allclose(np.concatenate(outs, axis=2), full, rtol=1e-12, atol=1e-13)
+
+
+def check_extend_brute(extend=oracle.extend):
+    """Brute force (pure Python, fsum) on the whole sequence, rows after a prefix."""
+    B, H, Hkv, S, D, T = 1, 2, 1, 7, 3, 3
+    q = _rand((B, H, S, D), 161)
+    k = _rand((B, Hkv, S, D), 162)
+    v = _rand((B, Hkv, S, D), 163)
+    ref = np.array(oracle.brute(_to_lists(q), _to_lists(k), _to_lists(v), 0.7))
+    got = extend(q[:, :, S - T:], k, v, [S - T], 0.7)
+    np.testing.assert_allclose(got, ref[:, :, S - T:], rtol=1e-12, atol=1e-13)
+
+
 ALL_CHECKS = [
     check_kv_bytes, check_brute, check_row0_is_v0, check_zero_query_prefix_mean,
     check_two_key_logistic, check_rows_sum_to_one, check_large_scores, check_causality,
     check_gqa_equals_repeated_mha, check_torch_sdpa, check_chunked, check_decode_single_key,
     check_decode_permutation, check_decode_matches_prefill_rows, check_cached_equals_recompute,
+    check_extend_matches_prefill_rows, check_chunked_prefill_by_extend, check_extend_brute,
 ]

@@ -107,3 +107,8 @@ def test_measure_stream_read_validates_on_host():
     assert lib.kvattn_measure_stream_read(ctypes.c_void_p((1 << 20) + 4), 1 << 20, 64, fake, None) == -1
     assert lib.kvattn_measure_stream_read(fake, 1 << 20, 0, fake, None) == -1
     assert lib.kvattn_measure_stream_read(fake, 1 << 20, 64, None, None) == -1
+
+
+def test_extend_rejects_null_cache_without_a_device():
+    lib = kv.lib()
+    assert lib.kvattn_extend(None, 0, None, None, None, None, 4, 0.1, 1, None) == -1

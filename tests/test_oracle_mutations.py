@@ -115,6 +115,11 @@ def _run_all(overrides):
         "check_cached_equals_recompute": lambda: pins.check_cached_equals_recompute(
             overrides.get("decode_cached", oracle.decode_cached), oracle.decode_recompute,
             overrides.get("CacheModel", oracle.CacheModel)),
+        "check_extend_matches_prefill_rows": lambda: pins.check_extend_matches_prefill_rows(
+            overrides.get("extend", oracle.extend), oracle.naive_causal),
+        "check_chunked_prefill_by_extend": lambda: pins.check_chunked_prefill_by_extend(
+            overrides.get("extend", oracle.extend), oracle.naive_causal),
+        "check_extend_brute": lambda: pins.check_extend_brute(overrides.get("extend", oracle.extend)),
     }
     with np.errstate(all="ignore"):
         for name, fn in calls.items():
@@ -138,6 +143,22 @@ def _decode_cached_with(attend_row):
     return f
 
 
+def _extend_visible(count):
+    """An extend whose new query t sees count(off, t, T) keys instead of off + t + 1."""
+    def f(q_new, ck, cv, offsets, scale):
+        B, H, T, D = q_new.shape
+        Hkv = ck.shape[1]
+        out = np.empty((B, H, T, cv.shape[-1]))
+        for b in range(B):
+            for h in range(H):
+                g = h // (H // Hkv)
+                for t in range(T):
+                    n = max(1, count(int(offsets[b]), t, T))
+                    out[b, h, t] = oracle.attend_row(q_new[b, h, t], ck[b, g, :n], cv[b, g, :n], scale)
+        return out
+    return f
+
+
 MUTANTS = {f"naive_{n}": {"naive": fn} for n, fn in NAIVE_MUTANTS.items()}
 MUTANTS.update({
     "kv_bytes_without_factor_2": {"kv_bytes": lambda L, Hk, D, T, e, B: L * Hk * D * T * e * B},
@@ -147,6 +168,9 @@ MUTANTS.update({
     "decode_unnormalised": {"attend_row": _attend_row_no_normalise,
                             "decode_cached": _decode_cached_with(_attend_row_no_normalise)},
     "cache_append_off_by_one": {"CacheModel": _CacheModelOffByOne},
+    "extend_ignores_offset": {"extend": _extend_visible(lambda off, t, T: t + 1)},
+    "extend_misses_own_key": {"extend": _extend_visible(lambda off, t, T: off + t)},
+    "extend_sees_whole_block": {"extend": _extend_visible(lambda off, t, T: off + T)},
 })
 
 
