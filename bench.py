@@ -286,6 +286,71 @@ def prefill_step(p, timer=None):
             timer.stop(ev)
 
 
+def extend_measurements(kv, w, dec, pre, reps=3):
+    """The extend path on the same workload: (a) the T=8192 prompt of 4 layers fed as four
+    2048-token chunks (algorithmic flops as for one prefill), (b) a 4-token verification step
+    on the ragged batch-32 decode cache (K/V of every sequence read once per query head, plus
+    the 4 new rows), then rolled back."""
+    out = {}
+    T, layers, chunk = pre["T"], 4, 2048
+    c = kv.KVCache(layers, 1, w.q_heads, w.kv_heads, w.head_dim, T, torch.float16, device=pre["q"][0].device)
+    calls = []
+    for l in range(layers):
+        for off in range(0, T, chunk):
+            sl = slice(off, off + chunk)
+            q, k, v = (pre[n][l][:, :, sl].contiguous() for n in ("q", "k", "v"))
+            calls.append((l, q, k, v, torch.empty_like(q)))
+
+    def run_chunked():
+        c.set_lengths([0])
+        for l, q, k, v, o in calls:
+            c.extend(l, q, k, v, out=o, scale=w.scale)
+    run_chunked()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run_chunked()
+    b.record()
+    torch.cuda.synchronize()
+    ms_layer = a.elapsed_time(b) / reps / layers
+    out["chunked_prefill"] = {"workload": f"T={T} in {T // chunk} chunks of {chunk}, H={w.q_heads}, D={w.head_dim}",
+                              "us_per_layer": round(ms_layer * 1e3, 1),
+                              "value": round(pre["flops_layer"] / (ms_layer * 1e-3) / 1e12, 1), "unit": "TFLOP/s"}
+    c.close()
+    del calls
+    # verification of 4 draft positions per sequence on the decode cache, then rollback
+    g = 4
+    dc = dec["cache"]
+    ctx = dec["ctx"]
+    dev = dec["q"][0].device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(44)
+    qv = torch.randn((w.batch, w.q_heads, g, w.head_dim), generator=gen, device=dev).to(torch.float16)
+    kvn = torch.randn((w.batch, w.kv_heads, g, w.head_dim), generator=gen, device=dev).to(torch.float16)
+    ov = torch.empty_like(qv)
+    base = [int(L) - g for L in ctx]
+
+    def run_verify():
+        dc.set_lengths(base)
+        for l in range(layers):
+            dc.extend(l, qv, kvn, kvn, out=ov, scale=w.scale)
+    run_verify()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        run_verify()
+    b.record()
+    torch.cuda.synchronize()
+    ms_layer = a.elapsed_time(b) / reps / layers
+    e = 2
+    nbytes = 2 * w.kv_heads * w.head_dim * e * int(ctx.sum()) + 2 * w.batch * w.q_heads * g * w.head_dim * e
+    out["verify_4_tokens"] = {"workload": f"batch {w.batch}, contexts U[{w.ctx_lo},{w.ctx_hi}] (4 new each)",
+                              "us_per_layer": round(ms_layer * 1e3, 1),
+                              "value": round(nbytes / (ms_layer * 1e-3) / 1e9, 1), "unit": "GB/s"}
+    return out
+
+
 def timed(fn, steps, warmup):
     for _ in range(warmup):
         fn(None)
@@ -457,6 +522,9 @@ def main():
                      "prefill_batch": 1, "prefill_T": w5.extra_prefill_T, "dtype": "f16"}
     out["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                      "cus": props.multi_processor_count}
+    if dec is not None and pre is not None:
+        log("extend: chunked prefill and 4-token verification")
+        out["extend"] = extend_measurements(kv, w5, dec, pre)
     # free the big caches before the GQA workload
     if dec is not None:
         dec["cache"].close()
