@@ -104,6 +104,20 @@ int kvattn_cache_set_lengths(kvattn_cache *c, int layer, const int32_t *host_len
  * mirror is updated at enqueue time, so it already includes enqueued work. */
 int kvattn_cache_get_lengths(const kvattn_cache *c, int layer, int32_t *host_lens);
 
+/* Sliding-window and attention-sink masks of one layer (layer >= 0) or of
+ * every layer (-1), the long-context variants of the roadmap page (project 13:
+ * attend only a recent window; keep the first few positions).  With window W
+ * > 0 and sink S >= 0, the query at position i sees key j iff j <= i and
+ * (i - j < W or j < S); window 0 (the default) is the plain causal mask and
+ * resets the sink to 0.  Later prefill, extend and decode calls on the layer
+ * use the mask; decode then reads only the min(len, S) sink rows and the last
+ * W rows of each sequence.  INVALID_ARG for a negative W or S or a bad layer.
+ * Host-only: enqueues nothing. */
+int kvattn_cache_set_window(kvattn_cache *c, int layer, int window, int sink);
+
+/* The window and sink set for one layer (0, 0 when none). */
+int kvattn_cache_get_window(const kvattn_cache *c, int layer, int *window, int *sink);
+
 /* Prefill of one layer (inference chapter 9.1/9.3): causal attention of the T
  * prompt queries over the T prompt keys, o = attn(q, k, v), and a bit-exact
  * copy of k, v into cache rows [0, T); the layer's lengths become T.

@@ -41,6 +41,9 @@ _SIGS = {
     "kvattn_cache_set_lengths": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
                                                 ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]),
     "kvattn_cache_get_lengths": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int32)]),
+    "kvattn_cache_set_window": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "kvattn_cache_get_window": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                               ctypes.POINTER(ctypes.c_int)]),
     "kvattn_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 4
                        + [ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_append": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -168,6 +171,18 @@ class KVCache:
         arr = (ctypes.c_int32 * self.batch)()
         _check(lib().kvattn_cache_get_lengths(self._handle, layer, arr), "kvattn_cache_get_lengths")
         return list(arr)
+
+    # ------------------------------------------------------------------ masks
+    def set_window(self, window: int, sink: int = 0, layer: int = -1) -> None:
+        """Sliding window W (0: none) and sink S of one layer, or of all (-1)."""
+        _check(lib().kvattn_cache_set_window(self._handle, layer, int(window), int(sink)),
+               "kvattn_cache_set_window")
+
+    def window(self, layer: int) -> tuple:
+        w, s = ctypes.c_int(), ctypes.c_int()
+        _check(lib().kvattn_cache_get_window(self._handle, layer, ctypes.byref(w), ctypes.byref(s)),
+               "kvattn_cache_get_window")
+        return w.value, s.value
 
     # ------------------------------------------------------------------ checks
     def _tensor(self, t: torch.Tensor, shape, name: str, dtype=None) -> None:

@@ -38,9 +38,24 @@ struct DecodeArgs {
   float *ws;            // (B, H, n_splits, D + 2) fp32: m (log2 domain), l, u[D]
   const int32_t *len;   // layer's lengths [B]
   int batch, q_heads, kv_heads, head_dim, max_T, chunk, n_splits;
+  int window, sink;     // sliding window (0: none) and attention-sink positions
   float scale_log2;     // scale * log2(e)
   kvattn_dtype dt, o_dt;
 };
+
+// The keys a decode query at position L - 1 sees, as one run of visible
+// indices 0 .. count - 1: the first `sink` positions, then the last `window`
+// ones (all L positions without a window).  Visible index i is cache row
+// i + (i >= first ? gap : 0).
+struct VisibleKeys {
+  int count, first, gap;
+};
+__host__ __device__ inline VisibleKeys visible_keys(int L, int window, int sink) {
+  if (window <= 0 || window + sink >= L) return VisibleKeys{L, L, 0};
+  const int s = sink < L ? sink : L;
+  const int lo = (L - window) > s ? (L - window) : s;
+  return VisibleKeys{s + (L - lo), s, lo - s};
+}
 
 struct PrefillArgs {
   const void *q;        // (B, H, T, D): the T query positions of each sequence
@@ -54,6 +69,7 @@ struct PrefillArgs {
   int batch, q_heads, kv_heads, head_dim, T, max_T;
   int kv_rows;          // rows per (sequence, KV head) in k/v: T for a prompt, max_T for the cache
   int write_cache;      // prefill: copy k/v rows [0, T) to the cache and set len = T
+  int window, sink;     // sliding window (0: none) and attention-sink positions
   float scale_log2;
   kvattn_dtype dt, o_dt;
 };

@@ -115,11 +115,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int unit = blockIdx.y;  // (kv head, sub-group of GT query heads)
   const int kvh = unit / subs;
   const int h0 = kvh * G + (unit - kvh * subs) * GT;
-  const int L = a.len[b];
-  const int kb = split * a.chunk;
-  if (kb >= L) return;  // empty split
-  const int rows = min(a.chunk, L - kb);
-  const int n_valid = (L + a.chunk - 1) / a.chunk;
+  // splits run over the visible keys (all L, or the sink and window ones)
+  const VisibleKeys vk = visible_keys(a.len[b], a.window, a.sink);
+  const int kb = split * a.chunk;  // first visible index of this split
+  if (kb >= vk.count) return;  // empty split
+  const int rows = min(a.chunk, vk.count - kb);
+  const int n_valid = (vk.count + a.chunk - 1) / a.chunk;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -130,6 +131,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const size_t head_off = (size_t)(b * a.kv_heads + kvh) * a.max_T * D;
   const char *Kb = (const char *)a.k_layer + (head_off + (size_t)kb * D + cl) * ESZ;
   const char *Vb = (const char *)a.v_layer + (head_off + (size_t)kb * D + cl) * ESZ;
+  // rows of this split at or past `jump` lie after the gap between sink and window
+  const int jump = vk.first - kb;
+  const int gap = vk.gap;
 
   uint4 qv[GT];
 #pragma unroll
@@ -156,7 +160,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   auto load = [&](int ib, uint4 (&kr)[U], uint4 (&vr)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = min(((ib * U + u) * 4 + wave) * RPW + rg, rows - 1);
+      int r = min(((ib * U + u) * 4 + wave) * RPW + rg, rows - 1);
+      r += r >= jump ? gap : 0;
       // streamed once: nontemporal loads (measured 5% faster than cached ones)
       const u32x4 tk = __builtin_nontemporal_load((const u32x4 *)(Kb + (size_t)r * D * ESZ));
       const u32x4 tv = __builtin_nontemporal_load((const u32x4 *)(Vb + (size_t)r * D * ESZ));
@@ -304,8 +309,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int unit = blockIdx.x;
   const int kvh = unit / subs;
   const int h0 = kvh * G + (unit - kvh * subs) * GT;
-  const int L = a.len[b];
-  const int ns = (L + a.chunk - 1) / a.chunk;
+  const int ns = (visible_keys(a.len[b], a.window, a.sink).count + a.chunk - 1) / a.chunk;
   if (ns <= 1) return;
   __shared__ float s_w[GT][MAXS];
   __shared__ float s_den[GT];

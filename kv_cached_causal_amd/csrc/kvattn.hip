@@ -28,6 +28,7 @@ struct kvattn_cache {
   bool owns_base;
   int32_t *d_len;         // [layers][batch] (device)
   std::vector<int32_t> h_len;  // host mirror
+  std::vector<int> window, sink;  // per layer: sliding window (0: none), sink positions
   float *d_ws;            // decode split-K workspace (device)
   int chunk, n_splits;
   int device;
@@ -119,6 +120,8 @@ int kvattn_cache_alloc(kvattn_cache **out, int layers, int batch, int q_heads, i
   c->chunk = decode_chunk(head_dim, q_heads / kv_heads, max_T);
   c->n_splits = (max_T + c->chunk - 1) / c->chunk;
   c->h_len.assign((size_t)layers * batch, 0);
+  c->window.assign(layers, 0);
+  c->sink.assign(layers, 0);
 
   hipError_t e = hipGetDevice(&c->device);
   if (e != hipSuccess) {
@@ -198,6 +201,28 @@ int kvattn_cache_set_lengths(kvattn_cache *c, int layer, const int32_t *host_len
   return KVATTN_OK;
 }
 
+int kvattn_cache_set_window(kvattn_cache *c, int layer, int window, int sink) {
+  if (!c) return KVATTN_ERR_INVALID_ARG;
+  if (layer != -1 && (layer < 0 || layer >= c->layers)) return KVATTN_ERR_INVALID_ARG;
+  if (window < 0 || sink < 0) return KVATTN_ERR_INVALID_ARG;
+  const int first = layer < 0 ? 0 : layer;
+  const int count = layer < 0 ? c->layers : 1;
+  for (int l = first; l < first + count; ++l) {
+    c->window[l] = window;
+    c->sink[l] = window > 0 ? sink : 0;
+  }
+  return KVATTN_OK;
+}
+
+int kvattn_cache_get_window(const kvattn_cache *c, int layer, int *window, int *sink) {
+  int rc = check_layer(c, layer);
+  if (rc) return rc;
+  if (!window || !sink) return KVATTN_ERR_INVALID_ARG;
+  *window = c->window[layer];
+  *sink = c->sink[layer];
+  return KVATTN_OK;
+}
+
 int kvattn_cache_get_lengths(const kvattn_cache *c, int layer, int32_t *host_lens) {
   int rc = check_layer(c, layer);
   if (rc) return rc;
@@ -237,6 +262,8 @@ int kvattn_prefill(kvattn_cache *c, int layer, const void *q, const void *k, con
   a.max_T = c->max_T;
   a.kv_rows = T;
   a.write_cache = 1;
+  a.window = c->window[layer];
+  a.sink = c->sink[layer];
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dt = c->dt;
   a.o_dt = o_dtype;
@@ -294,6 +321,8 @@ int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, cons
   a.max_T = c->max_T;
   a.kv_rows = c->max_T;
   a.write_cache = 0;
+  a.window = c->window[layer];
+  a.sink = c->sink[layer];
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dt = c->dt;
   a.o_dt = o_dtype;
@@ -358,6 +387,8 @@ int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scal
   a.max_T = c->max_T;
   a.chunk = c->chunk;
   a.n_splits = c->n_splits;
+  a.window = c->window[layer];
+  a.sink = c->sink[layer];
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dt = c->dt;
   a.o_dt = o_dtype;

@@ -177,6 +177,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
 
   const int kv_end = off + min(q0 + BM, Tn);
   const int n_tiles = (kv_end + BN - 1) / BN;
+  // With a sliding window W the workgroup visits the tiles holding the S sink
+  // keys, then the tiles from the one holding its first row's oldest visible
+  // key; the tiles in between are never read.  Without a window: all tiles.
+  const int W = a.window, S = a.sink;
+  int sink_tiles = 0, win_tile0 = 0;
+  if (W > 0) {
+    sink_tiles = min((S + BN - 1) / BN, n_tiles);
+    win_tile0 = max(sink_tiles, max(0, off + q0 - W + 1) / BN);
+  }
+  const int n_iter = sink_tiles + (n_tiles - win_tile0);
+  auto tile_of = [&](int it) { return it < sink_tiles ? it : it - sink_tiles + win_tile0; };
 
   u32x4 kreg[KCH];
   u32x4 vreg[4];
@@ -254,19 +265,22 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
     }
   };
 
-  load_tile(0);
-  store_tile(0, 0);
+  load_tile(tile_of(0));
+  store_tile(tile_of(0), 0);
   __syncthreads();
 
   const float c = a.scale_log2;
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
+  for (int it = 0; it < n_iter; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < n_iter) load_tile(tile_of(it + 1));
     // keep the next tile's loads ahead of this tile's math
     __builtin_amdgcn_sched_barrier(0);
 
-    const int k0 = j * BN;
-    if (k0 <= off + qw0 + QW - 1) {  // wave-uniform: this tile has keys some row of the wave sees
+    const int k0 = tile_of(it) * BN;
+    // wave-uniform: skip a tile no row of the wave sees (past the diagonal, or
+    // wholly older than every row's window and not a sink tile)
+    const bool seen = k0 <= off + qw0 + QW - 1 && !(W > 0 && k0 >= S && k0 + BN - 1 <= off + qw0 - W);
+    if (seen) {
       const T *Ks = smem + buf * LDS::BUF;
       const T *Vt = Ks + LDS::K_ELEMS;
       float4_t s[KT][NT];
@@ -283,10 +297,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
           for (int nt = 0; nt < NT; ++nt) s[kt][nt] = Mfma<T>::mma(ka, qf[nt][ks], s[kt][nt]);
         }
       }
-      // causal mask (diagonal tiles only): lane holds
-      // S^T[key = k0 + 16kt + 4lg + i][query = qw0 + 16nt + l16]
-      if (k0 + BN - 1 > off + qw0) {
-        asm volatile("" ::);  // diagonal tiles only: keep it a real branch
+      // mask (diagonal tiles, and tiles at the lower edge of a window): lane
+      // holds S^T[key = k0 + 16kt + 4lg + i][query = qw0 + 16nt + l16]
+      const bool diag = k0 + BN - 1 > off + qw0;
+      const bool edge = W > 0 && k0 + BN > S && k0 <= off + qw0 + QW - 1 - W;
+      if (diag || edge) {
+        asm volatile("" ::);  // rare tiles only: keep it a real branch
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -295,7 +311,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
             for (int i = 0; i < 4; ++i) {
               const int key = k0 + kt * 16 + lg * 4 + i;
               const int qr = off + qw0 + nt * 16 + l16;
-              if (key > qr) s[kt][nt][i] = -INFINITY;
+              if (key > qr || (W > 0 && key <= qr - W && key >= S)) s[kt][nt][i] = -INFINITY;
             }
       }
       // online softmax per query column
@@ -311,17 +327,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mx2 = mx * c;
-        // tile 0 holds key 0, visible to every row, so m is finite after it
+        // m stays -inf while a row has seen no visible key (possible under a
+        // window); the -inf guards keep such rows at p = 0 instead of NaN
         if (__any(mx2 > mrow[nt] + kLazyMax)) {
           asm volatile("" ::);  // rare: keep it a real branch
           const float mn = fmaxf(mrow[nt], mx2);
-          const float al = fast_exp2(mrow[nt] - mn);
+          const float al = fast_exp2(mrow[nt] - (mn == -INFINITY ? 0.f : mn));
           mrow[nt] = mn;
           lrow[nt] *= al;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] *= al;
         }
-        const float mn = mrow[nt];
+        const float mn = mrow[nt] == -INFINITY ? 0.f : mrow[nt];
         float ls = 0.f;
         if constexpr (Mfma<T>::kSplitP) {
 #pragma unroll
@@ -367,7 +384,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
       }
     }
 
-    if (j + 1 < n_tiles) store_tile(j + 1, buf ^ 1);
+    if (it + 1 < n_iter) store_tile(tile_of(it + 1), buf ^ 1);
     __syncthreads();
   }
 
@@ -784,7 +801,10 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   float m = -INFINITY, l = 0.f;
   const float c = a.scale_log2;
   const int kv_end = off + min(q0 + BMF, Tn);
+  const int W = a.window, S = a.sink;
   for (int k0 = 0; k0 < kv_end; k0 += BNF) {
+    // workgroup-uniform: a tile older than every row's window and past the sink is never read
+    if (W > 0 && k0 >= S && k0 + BNF - 1 <= off + q0 - W) continue;
     __syncthreads();
     for (int i = threadIdx.x; i < BNF * D; i += 64) {
       const int r = i / D, d = i - r * D;
@@ -810,17 +830,20 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
       float acc = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) acc = fmaf(qr[d], Ks[j][d], acc);
-      s[j] = (k0 + j <= off + row) ? acc * c : -INFINITY;
+      const int key = k0 + j, pos = off + row;
+      const bool vis = key <= pos && (W == 0 || pos - key < W || key < S);
+      s[j] = vis ? acc * c : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }
     const float mn = fmaxf(m, mx);
-    const float al = fast_exp2(m - mn);
+    const float ms = mn == -INFINITY ? 0.f : mn;  // no visible key yet (window): p = 0, not NaN
+    const float al = fast_exp2(m - ms);
     l *= al;
 #pragma unroll
     for (int d = 0; d < D; ++d) o[d] *= al;
 #pragma unroll
     for (int j = 0; j < BNF; ++j) {
-      const float p = fast_exp2(s[j] - mn);
+      const float p = fast_exp2(s[j] - ms);
       l += p;
 #pragma unroll
       for (int d = 0; d < D; ++d) o[d] = fmaf(p, Vs[j][d], o[d]);
@@ -860,6 +883,9 @@ static hipError_t launch_with_lds(KernelT kern, dim3 grid, int threads, size_t l
 }
 
 template <typename T, int D>
+static hipError_t launch_extend_mfma(const PrefillArgs &a, hipStream_t s);
+
+template <typename T, int D>
 static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
   typedef PrefillConfig<T, D> C;
   constexpr int BM = C::NW * C::QW;
@@ -867,6 +893,7 @@ static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)n_qt * a.batch * a.q_heads);
   static bool attr_done = false;
   if constexpr (C::kPipe) {
+    if (a.window > 0) return launch_extend_mfma<T, D>(a, s);  // the plain kernel takes the window mask
     return launch_with_lds(prefill_pipe_kernel<T, D, C::QW, C::BN, C::NW>, grid, C::NW * 64,
                            PipeLds<D, C::BN>::BYTES, s, attr_done, a);
   } else {

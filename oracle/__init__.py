@@ -10,4 +10,7 @@ from .attention import (  # noqa: F401
     kv_bytes,
     kv_head_of,
     naive_causal,
+    naive_windowed,
+    visible,
+    visible_keys,
 )

@@ -92,6 +92,47 @@ def naive_causal(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 
 # --------------------------------------------------------------------------
+# sliding window and attention sink (roadmap page, project 13 long context)
+# --------------------------------------------------------------------------
+def visible(i: int, j: int, window: int = 0, sink: int = 0) -> bool:
+    """Key j is visible to the query at position i: causal (j <= i) and, with a
+    window W > 0, within the last W positions (i - j < W) or among the first
+    `sink` positions (j < sink).  W = 0 means no window."""
+    return j <= i and (window <= 0 or i - j < window or j < sink)
+
+
+def naive_windowed(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                   window: int, sink: int) -> np.ndarray:
+    """Causal attention restricted to a sliding window plus attention-sink keys,
+    with the full T x T score matrix materialised per head (matrix form)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, T, D = q.shape
+    Hkv = k.shape[1]
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    hidden = j > i
+    if window > 0:
+        hidden |= (i - j >= window) & (j >= sink)
+    out = np.empty((B, H, T, v.shape[-1]), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            s = (q[b, h] @ k[b, g].T) * scale
+            s[hidden] = -np.inf
+            s = s - s.max(axis=1, keepdims=True)
+            e = np.exp(s)
+            out[b, h] = (e / e.sum(axis=1, keepdims=True)) @ v[b, g]
+    return out
+
+
+def visible_keys(pos: int, window: int, sink: int) -> np.ndarray:
+    """Indices of the keys the query at position `pos` sees, in increasing order."""
+    return np.array([j for j in range(pos + 1) if visible(pos, j, window, sink)], dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
 # the tiled form (README: chunked == naive; chapter 9.7: flash-style tiling)
 # --------------------------------------------------------------------------
 def chunked(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
@@ -157,11 +198,12 @@ def attend_row(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) ->
 
 
 def decode_cached(q: np.ndarray, cache_k: np.ndarray, cache_v: np.ndarray,
-                  lengths, scale: float) -> np.ndarray:
+                  lengths, scale: float, window: int = 0, sink: int = 0) -> np.ndarray:
     """Decode step from a cache: q (B, H, D); cache_k/v (B, Hkv, >=L, D); lengths (B,).
 
     Sequence b's query sits at position L_b - 1 and sees the L_b cached keys,
-    including the one appended this step (bottom-right aligned causal mask).
+    including the one appended this step (bottom-right aligned causal mask);
+    with a window, only the keys ``visible`` to it.
     """
     q = np.asarray(q, dtype=np.float64)
     B, H, D = q.shape
@@ -171,10 +213,11 @@ def decode_cached(q: np.ndarray, cache_k: np.ndarray, cache_v: np.ndarray,
         L = int(lengths[b])
         if L < 1:
             raise ValueError("decode needs at least one cached key")
+        keys = visible_keys(L - 1, window, sink) if window > 0 else slice(0, L)
         for h in range(H):
             g = kv_head_of(h, H, Hkv)
-            out[b, h] = attend_row(q[b, h], np.asarray(cache_k[b, g, :L], np.float64),
-                                   np.asarray(cache_v[b, g, :L], np.float64), scale)
+            out[b, h] = attend_row(q[b, h], np.asarray(cache_k[b, g, keys], np.float64),
+                                   np.asarray(cache_v[b, g, keys], np.float64), scale)
     return out
 
 
@@ -208,7 +251,7 @@ def decode_recompute(q_hist: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarray,
 # verification of the README's speculative loop; chapter 9.3's cache)
 # --------------------------------------------------------------------------
 def extend(q_new: np.ndarray, cache_k: np.ndarray, cache_v: np.ndarray, offsets,
-           scale: float) -> np.ndarray:
+           scale: float, window: int = 0, sink: int = 0) -> np.ndarray:
     """Attention of T new queries appended after a cached prefix.
 
     q_new (B, H, T, D); cache_k/v (B, Hkv, >= off_b + T, D) already hold the
@@ -228,9 +271,9 @@ def extend(q_new: np.ndarray, cache_k: np.ndarray, cache_v: np.ndarray, offsets,
         for h in range(H):
             g = kv_head_of(h, H, Hkv)
             for t in range(T):
-                n = off + t + 1
-                out[b, h, t] = attend_row(q_new[b, h, t], np.asarray(cache_k[b, g, :n], np.float64),
-                                          np.asarray(cache_v[b, g, :n], np.float64), scale)
+                keys = visible_keys(off + t, window, sink) if window > 0 else slice(0, off + t + 1)
+                out[b, h, t] = attend_row(q_new[b, h, t], np.asarray(cache_k[b, g, keys], np.float64),
+                                          np.asarray(cache_v[b, g, keys], np.float64), scale)
     return out
 
 

@@ -283,10 +283,89 @@ def check_extend_brute(extend=oracle.extend):
     np.testing.assert_allclose(got, ref[:, :, S - T:], rtol=1e-12, atol=1e-13)
 
 
+def check_window_special_cases(naive_windowed=oracle.naive_windowed, naive=oracle.naive_causal):
+    """Sliding window + sink reduce to plain causal attention when nothing is cut
+    (W = 0, W >= T, sink >= T), to v_i when a query sees only itself (W = 1, no
+    sink), and to the two-key logistic mix of v_0 and v_i when W = 1, sink = 1."""
+    B, H, Hkv, T, D = 2, 2, 1, 11, 4
+    q = _rand((B, H, T, D), 171)
+    k = _rand((B, Hkv, T, D), 172)
+    v = _rand((B, Hkv, T, D), 173)
+    full = naive(q, k, v, 0.6)
+    for W, S in ((0, 0), (T, 0), (T + 5, 2), (3, T)):
+        np.testing.assert_allclose(naive_windowed(q, k, v, 0.6, W, S), full, rtol=1e-12, atol=1e-13)
+    own = naive_windowed(q, k, v, 0.6, 1, 0)
+    np.testing.assert_array_equal(own, np.repeat(v, H // Hkv, axis=1))
+    two = naive_windowed(q, k, v, 0.6, 1, 1)
+    for i in range(1, T):
+        s0 = 0.6 * np.einsum("bhd,bd->bh", q[:, :, i], k[:, 0, 0])
+        si = 0.6 * np.einsum("bhd,bd->bh", q[:, :, i], k[:, 0, i])
+        p0 = 1.0 / (1.0 + np.exp(si - s0))
+        expect = p0[..., None] * v[:, 0, 0][:, None] + (1 - p0)[..., None] * v[:, 0, i][:, None]
+        np.testing.assert_allclose(two[:, :, i], expect, rtol=1e-12, atol=1e-13)
+
+
+def check_window_brute(naive_windowed=oracle.naive_windowed):
+    """Row-by-row pure-Python loops (math.fsum) with the window/sink rule spelled out."""
+    B, H, Hkv, T, D = 1, 2, 2, 9, 3
+    q = _rand((B, H, T, D), 181)
+    k = _rand((B, Hkv, T, D), 182)
+    v = _rand((B, Hkv, T, D), 183)
+    for W, S in ((2, 0), (3, 1), (4, 2)):
+        got = naive_windowed(q, k, v, 0.8, W, S)
+        for h in range(H):
+            for i in range(T):
+                keys = [j for j in range(T) if j <= i and (i - j < W or j < S)]
+                sc = [0.8 * math.fsum(float(q[0, h, i, d]) * float(k[0, h, j, d]) for d in range(D)) for j in keys]
+                top = max(sc)
+                w = [math.exp(x - top) for x in sc]
+                z = math.fsum(w)
+                ref = [math.fsum(w[n] * float(v[0, h, j, d]) for n, j in enumerate(keys)) / z for d in range(D)]
+                np.testing.assert_allclose(got[0, h, i], ref, rtol=1e-12, atol=1e-13)
+
+
+def check_window_decode_and_extend_rows(decode_cached=oracle.decode_cached, extend=oracle.extend,
+                                        naive_windowed=oracle.naive_windowed):
+    """Decode at each position and extend after ragged prefixes give the rows of one windowed prefill."""
+    B, H, Hkv, T, D = 2, 4, 2, 21, 5
+    q = _rand((B, H, T, D), 191)
+    k = _rand((B, Hkv, T, D), 192)
+    v = _rand((B, Hkv, T, D), 193)
+    for W, S in ((4, 0), (5, 3), (1, 1)):
+        full = naive_windowed(q, k, v, 0.45, W, S)
+        for p in (0, 3, 12, T - 1):
+            got = decode_cached(q[:, :, p], k, v, np.full(B, p + 1), 0.45, W, S)
+            np.testing.assert_allclose(got, full[:, :, p], rtol=1e-12, atol=1e-13)
+        offsets = [2, 13]
+        n = 6
+        q_new = np.stack([q[b, :, o:o + n] for b, o in enumerate(offsets)])
+        got = extend(q_new, k, v, offsets, 0.45, W, S)
+        for b, o in enumerate(offsets):
+            np.testing.assert_allclose(got[b], full[b, :, o:o + n], rtol=1e-12, atol=1e-13)
+
+
+def check_window_ignores_hidden_keys(naive_windowed=oracle.naive_windowed):
+    """Changing keys/values a query cannot see leaves its row bit-identical."""
+    B, H, Hkv, T, D = 1, 2, 1, 16, 4
+    q = _rand((B, H, T, D), 201)
+    k = _rand((B, Hkv, T, D), 202)
+    v = _rand((B, Hkv, T, D), 203)
+    W, S, i = 4, 2, 12
+    base = naive_windowed(q, k, v, 0.5, W, S)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, S:i - W + 1] *= -3.0
+    v2[:, :, S:i - W + 1] += 7.0
+    k2[:, :, i + 1:] = 0.0
+    got = naive_windowed(q, k2, v2, 0.5, W, S)
+    assert np.array_equal(got[:, :, i], base[:, :, i])
+
+
 ALL_CHECKS = [
     check_kv_bytes, check_brute, check_row0_is_v0, check_zero_query_prefix_mean,
     check_two_key_logistic, check_rows_sum_to_one, check_large_scores, check_causality,
     check_gqa_equals_repeated_mha, check_torch_sdpa, check_chunked, check_decode_single_key,
     check_decode_permutation, check_decode_matches_prefill_rows, check_cached_equals_recompute,
     check_extend_matches_prefill_rows, check_chunked_prefill_by_extend, check_extend_brute,
+    check_window_special_cases, check_window_brute, check_window_decode_and_extend_rows,
+    check_window_ignores_hidden_keys,
 ]

@@ -112,3 +112,11 @@ def test_measure_stream_read_validates_on_host():
 def test_extend_rejects_null_cache_without_a_device():
     lib = kv.lib()
     assert lib.kvattn_extend(None, 0, None, None, None, None, 4, 0.1, 1, None) == -1
+
+
+def test_window_calls_reject_null_cache_without_a_device():
+    lib = kv.lib()
+    assert lib.kvattn_cache_set_window(None, 0, 16, 4) == -1
+    assert lib.kvattn_cache_set_window(None, -1, 0, 0) == -1
+    w, s = ctypes.c_int(), ctypes.c_int()
+    assert lib.kvattn_cache_get_window(None, 0, ctypes.byref(w), ctypes.byref(s)) == -1

@@ -120,6 +120,14 @@ def _run_all(overrides):
         "check_chunked_prefill_by_extend": lambda: pins.check_chunked_prefill_by_extend(
             overrides.get("extend", oracle.extend), oracle.naive_causal),
         "check_extend_brute": lambda: pins.check_extend_brute(overrides.get("extend", oracle.extend)),
+        "check_window_special_cases": lambda: pins.check_window_special_cases(
+            overrides.get("naive_windowed", oracle.naive_windowed), oracle.naive_causal),
+        "check_window_brute": lambda: pins.check_window_brute(overrides.get("naive_windowed", oracle.naive_windowed)),
+        "check_window_decode_and_extend_rows": lambda: pins.check_window_decode_and_extend_rows(
+            overrides.get("decode_cached", oracle.decode_cached), overrides.get("extend", oracle.extend),
+            overrides.get("naive_windowed", oracle.naive_windowed)),
+        "check_window_ignores_hidden_keys": lambda: pins.check_window_ignores_hidden_keys(
+            overrides.get("naive_windowed", oracle.naive_windowed)),
     }
     with np.errstate(all="ignore"):
         for name, fn in calls.items():
@@ -159,6 +167,25 @@ def _extend_visible(count):
     return f
 
 
+def _windowed_variant(rule):
+    """naive_windowed with another visibility rule(i, j, W, S)."""
+    def f(q, k, v, scale, W, S):
+        B, H, T, D = q.shape
+        Hkv = k.shape[1]
+        out = np.empty((B, H, T, v.shape[-1]))
+        hidden = np.array([[not rule(i, j, W, S) for j in range(T)] for i in range(T)])
+        for b in range(B):
+            for h in range(H):
+                g = h // (H // Hkv)
+                s = (q[b, h] @ k[b, g].T) * scale
+                s[hidden] = -np.inf
+                s = s - s.max(axis=1, keepdims=True)
+                e = np.exp(s)
+                out[b, h] = (e / e.sum(axis=1, keepdims=True)) @ v[b, g]
+        return out
+    return f
+
+
 MUTANTS = {f"naive_{n}": {"naive": fn} for n, fn in NAIVE_MUTANTS.items()}
 MUTANTS.update({
     "kv_bytes_without_factor_2": {"kv_bytes": lambda L, Hk, D, T, e, B: L * Hk * D * T * e * B},
@@ -171,6 +198,14 @@ MUTANTS.update({
     "extend_ignores_offset": {"extend": _extend_visible(lambda off, t, T: t + 1)},
     "extend_misses_own_key": {"extend": _extend_visible(lambda off, t, T: off + t)},
     "extend_sees_whole_block": {"extend": _extend_visible(lambda off, t, T: off + T)},
+    "window_one_too_wide": {"naive_windowed": _windowed_variant(
+        lambda i, j, W, S: j <= i and (W <= 0 or i - j <= W or j < S))},
+    "window_sink_ignored": {"naive_windowed": _windowed_variant(
+        lambda i, j, W, S: j <= i and (W <= 0 or i - j < W))},
+    "window_sink_one_too_many": {"naive_windowed": _windowed_variant(
+        lambda i, j, W, S: j <= i and (W <= 0 or i - j < W or j <= S))},
+    "window_not_causal": {"naive_windowed": _windowed_variant(
+        lambda i, j, W, S: W <= 0 and j <= i or W > 0 and (abs(i - j) < W or j < S))},
 })
 
 
