@@ -351,6 +351,36 @@ def extend_measurements(kv, w, dec, pre, reps=3):
     return out
 
 
+def window_measurements(kv, w, dec, full_us, window=1024, sink=4, reps=5):
+    """Decode of the ragged batch-32 cache under a sliding window of `window` keys plus
+    `sink` sink positions: only the visible rows are read (min(L, window + sink) per
+    sequence), so the time per layer falls with the visible share of the contexts."""
+    c, ctx = dec["cache"], dec["ctx"]
+    vis = int(sum(min(int(L), window + sink) for L in ctx))
+    c.set_lengths([int(L) for L in ctx])
+    c.set_window(window, sink)
+
+    def run():
+        for d in dec["decodes"]:
+            d()
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    c.set_window(0, 0)
+    us = a.elapsed_time(b) * 1e3 / reps / w.layers
+    e = 2
+    nbytes = 2 * w.kv_heads * w.head_dim * e * vis + 2 * w.batch * w.q_heads * w.head_dim * e
+    return {"workload": f"batch {w.batch}, contexts U[{w.ctx_lo},{w.ctx_hi}], window {window} + sink {sink}",
+            "us_per_layer": round(us, 1), "visible_fraction": round(vis / int(ctx.sum()), 4),
+            "value": round(nbytes / (us * 1e-6) / 1e9, 1), "unit": "GB/s",
+            "speedup_vs_full_context": round(full_us / us, 2)}
+
+
 def timed(fn, steps, warmup):
     for _ in range(warmup):
         fn(None)
@@ -522,6 +552,9 @@ def main():
                      "prefill_batch": 1, "prefill_T": w5.extra_prefill_T, "dtype": "f16"}
     out["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                      "cus": props.multi_processor_count}
+    if dec is not None:
+        log("decode under a sliding window")
+        out["decode_window"] = window_measurements(kv, w5, dec, out["roofline"]["mean_launch_ms"] * 1e3)
     if dec is not None and pre is not None:
         log("extend: chunked prefill and 4-token verification")
         out["extend"] = extend_measurements(kv, w5, dec, pre)
