@@ -102,11 +102,12 @@ constexpr int kMaxSplits = 64;
 // rather than a power of two: with 256- or 512-key splits the concurrently
 // streaming workgroups sit at aligned offsets and the ragged batch-32 decode
 // ran at 4.9 TB/s instead of 6.3 TB/s on MI355X (measured over split sizes
-// 256..576).  Groups of >= 4 query heads per KV head do four times the
-// arithmetic per byte and run best with 768-key splits (GQA 32/8: 58.5 ->
-// 54.9 us per layer).
+// 256..576).  Groups of >= 4 query heads per KV head run best with 1024-key
+// splits: fewer, longer streams (GQA 32/8, batch 16 at 4096 keys: 512
+// workgroups, 54.7 -> 52.4 us per layer against 768-key splits; 256 to 1366
+// keys measured).
 inline int decode_chunk(int head_dim, int group, int max_T) {
-  int c = head_dim <= 32 ? 512 : (group >= 4 ? 768 : 384);
+  int c = head_dim <= 32 ? 512 : (group >= 4 ? 1024 : 384);
   while ((max_T + c - 1) / c > kMaxSplits) c *= 2;
   return c;
 }

@@ -99,14 +99,18 @@ __device__ __forceinline__ void store_out(void *o, size_t idx, float x, kvattn_d
 }
 
 // grid (n_splits, Hkv * G/GT, B), 256 threads.  A workgroup owns one split of
-// `chunk` keys of one KV head, for GT query heads of its group.
-template <class Tag, int D, int GT, int U>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+// `chunk` keys of one KV head, for GT query heads of its group.  LPR lanes
+// share one key row, each holding NV 16-byte slices of it (columns cl + v *
+// LPR * EPL), so one load instruction reads RPW whole rows.
+template <class Tag, int D, int GT, int U, int NV, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   constexpr int EPL = Tag::EPL;
-  constexpr int LPR = D / EPL;   // lanes that share one key row
-  constexpr int RPW = 64 / LPR;  // key rows per wave per 16-byte load
+  constexpr int LPR = D / (EPL * NV);  // lanes that share one key row
+  constexpr int RPW = 64 / LPR;        // key rows per wave per load instruction
+  constexpr int VSTRIDE = LPR * EPL;   // columns between a lane's slices
   constexpr int ESZ = Tag::bytes;
-  constexpr int ROWS_PER_STEP = 4 * RPW;  // key rows covered by one load across the 4 waves
+  constexpr int ROWS_PER_STEP = NW * RPW;  // key rows covered by one load across the NW waves
+  static_assert(LPR >= 1 && LPR <= 32 && LPR * EPL * NV == D, "row split");
 
   const int b = blockIdx.z;
   const int split = blockIdx.x;
@@ -135,70 +139,101 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int jump = vk.first - kb;
   const int gap = vk.gap;
 
-  uint4 qv[GT];
+  uint4 qv[GT][NV];
 #pragma unroll
   for (int g = 0; g < GT; ++g)
-    qv[g] = *(const uint4 *)((const char *)a.q + ((size_t)(b * a.q_heads + h0 + g) * D + cl) * ESZ);
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      qv[g][v] = *(const uint4 *)((const char *)a.q +
+                                  ((size_t)(b * a.q_heads + h0 + g) * D + cl + v * VSTRIDE) * ESZ);
 
-  float m[GT], l[GT], acc[GT][EPL];
+  // m: the row's reference point (log2 units), raised only when a score
+  // exceeds it by more than kLazyMax, so P = exp2(s - m) <= 2^kLazyMax and the
+  // rescale of (l, acc) is rare.  -inf until the first visible key.
+  constexpr float kLazyMax = 8.f;
+  float m[GT], l[GT], acc[GT][NV * EPL];
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+    for (int e = 0; e < NV * EPL; ++e) acc[g][e] = 0.f;
   }
 
   const int steps = (rows + ROWS_PER_STEP - 1) / ROWS_PER_STEP;
   const int nb = (steps + U - 1) / U;
+  const float c = a.scale_log2;
 
-  uint4 k0[U], v0[U], k1[U], v1[U];
+  uint4 k0[U][NV], v0[U][NV], k1[U][NV], v1[U][NV];
   // Rows past the split's end are clamped to its last row (always valid: the
   // split is non-empty) and their scores masked to -inf.  Keeping the loads
   // free of branches lets the compiler wait for one batch while the next is
   // still in flight.
-  auto load = [&](int ib, uint4 (&kr)[U], uint4 (&vr)[U]) {
+  auto load = [&](int ib, uint4 (&kr)[U][NV], uint4 (&vr)[U][NV]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      int r = min(((ib * U + u) * 4 + wave) * RPW + rg, rows - 1);
+      int r = min(((ib * U + u) * NW + wave) * RPW + rg, rows - 1);
       r += r >= jump ? gap : 0;
-      // streamed once: nontemporal loads (measured 5% faster than cached ones)
-      const u32x4 tk = __builtin_nontemporal_load((const u32x4 *)(Kb + (size_t)r * D * ESZ));
-      const u32x4 tv = __builtin_nontemporal_load((const u32x4 *)(Vb + (size_t)r * D * ESZ));
-      kr[u] = make_uint4(tk[0], tk[1], tk[2], tk[3]);
-      vr[u] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        // streamed once: nontemporal loads (measured 5% faster than cached ones)
+        const size_t off = ((size_t)r * D + v * VSTRIDE) * ESZ;
+        const u32x4 tk = __builtin_nontemporal_load((const u32x4 *)(Kb + off));
+        const u32x4 tv = __builtin_nontemporal_load((const u32x4 *)(Vb + off));
+        kr[u][v] = make_uint4(tk[0], tk[1], tk[2], tk[3]);
+        vr[u][v] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
+      }
     }
   };
-  auto compute = [&](int ib, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
-    float sc[U][GT];
+  auto compute = [&](int ib, const uint4 (&kr)[U][NV], const uint4 (&vr)[U][NV]) {
+    float sc[U][GT];  // raw q.k; the scale is applied inside the exponent
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool ok = ((ib * U + u) * 4 + wave) * RPW + rg < rows;
+      const bool ok = ((ib * U + u) * NW + wave) * RPW + rg < rows;
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
-        const float d = row_sum<LPR>(dot16(Tag{}, qv[g], kr[u]));
-        sc[u][g] = ok ? d * a.scale_log2 : -INFINITY;
+        float d = dot16(Tag{}, qv[g][0], kr[u][0]);
+#pragma unroll
+        for (int v = 1; v < NV; ++v) d += dot16(Tag{}, qv[g][v], kr[u][v]);
+        d = row_sum<LPR>(d);
+        sc[u][g] = ok ? d : -INFINITY;
+      }
+    }
+    float mx[GT];
+    bool raise = false;
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      mx[g] = sc[0][g];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mx[g] = fmaxf(mx[g], sc[u][g]);
+      mx[g] *= c;
+      raise |= mx[g] > m[g] + kLazyMax;
+    }
+    if (__any(raise)) {
+      asm volatile("" ::);  // rare: keep it a real branch
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        const float mn = fmaxf(m[g], mx[g]);
+        const float al = fast_exp2(m[g] - (mn == -INFINITY ? 0.f : mn));
+        l[g] *= al;
+#pragma unroll
+        for (int e = 0; e < NV * EPL; ++e) acc[g][e] *= al;
+        m[g] = mn;
       }
     }
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-      float mx = sc[0][g];
-#pragma unroll
-      for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
-      const float mn = fmaxf(m[g], mx);
-      const float ms = (mn == -INFINITY) ? 0.f : mn;
-      const float al = fast_exp2(m[g] - ms);
-      l[g] *= al;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] *= al;
+      const float ms = m[g] == -INFINITY ? 0.f : m[g];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float p = fast_exp2(sc[u][g] - ms);
+        const float p = fast_exp2(fmaf(sc[u][g], c, -ms));
         l[g] += p;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p, elem(Tag{}, vr[u], e), acc[g][e]);
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            acc[g][v * EPL + e] = fmaf(p, elem(Tag{}, vr[u][v], e), acc[g][v * EPL + e]);
       }
-      m[g] = mn;
     }
   };
 
@@ -230,7 +265,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const float a2 = fast_exp2(mo - ms);
       l[g] = l[g] * a1 + lo * a2;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
+      for (int e = 0; e < NV * EPL; ++e) {
         const float ao = __shfl_xor(acc[g][e], off);
         acc[g][e] = acc[g][e] * a1 + ao * a2;
       }
@@ -239,13 +274,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 
   // merge the four waves through LDS
-  __shared__ float s_m[4][GT], s_l[4][GT];
-  __shared__ float s_acc[4][GT][D];
+  __shared__ float s_m[NW][GT], s_l[NW][GT];
+  __shared__ float s_acc[NW][GT][D];
   if (lane < LPR) {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][g][cl + e] = acc[g][e];
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_acc[wave][g][cl + v * VSTRIDE + e] = acc[g][v * EPL + e];
       if (lane == 0) {
         s_m[wave][g] = m[g];
         s_l[wave][g] = l[g];
@@ -256,13 +293,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   if (n_valid == 1) {
     // the whole context fits one split: normalise and store directly
-    for (int t = tid; t < GT * D; t += 256) {
+    for (int t = tid; t < GT * D; t += NW * 64) {
       const int g = t / D;
       const int d = t - g * D;
-      const float M = fmaxf(fmaxf(s_m[0][g], s_m[1][g]), fmaxf(s_m[2][g], s_m[3][g]));
+      float M = s_m[0][g];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
       float num = 0.f, den = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float al = fast_exp2(s_m[w][g] - M);
         num = fmaf(al, s_acc[w][g][d], num);
         den = fmaf(al, s_l[w][g], den);
@@ -273,13 +312,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 
   // write this split's (m, l, u) for the GT heads; decode_merge combines them
-  for (int t = tid; t < GT * D; t += 256) {
+  for (int t = tid; t < GT * D; t += NW * 64) {
     const int g = t / D;
     const int d = t - g * D;
-    const float M = fmaxf(fmaxf(s_m[0][g], s_m[1][g]), fmaxf(s_m[2][g], s_m[3][g]));
+    float M = s_m[0][g];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float al = fast_exp2(s_m[w][g] - M);
       num = fmaf(al, s_acc[w][g][d], num);
       den = fmaf(al, s_l[w][g], den);
@@ -293,16 +334,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// grid (Hkv * G/GT, B), 256 threads: log-sum-exp merge of the non-empty splits
-// of one (sequence, KV head, GT query heads) unit.  Units whose context fits
-// one split were finished by decode_kernel.  All global reads are issued in
-// parallel (the split statistics by one lane per split, the partial sums
-// eight splits at a time), since the kernel is bound by load latency.
+// threads of the merge kernel: one per output element up to 256, else a
+// block size that divides the GT * D outputs evenly
 template <int D, int GT>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int MAXS = kMaxSplits;
-  static_assert(MAXS <= 64, "one lane per split");
-  constexpr int PARTS = (GT * D >= 256) ? 1 : 256 / (GT * D);  // threads per output
+constexpr int merge_threads() {
+  return GT * D <= 256 ? GT * D : (GT * D % 256 == 0 ? 256 : 128);
+}
+
+// grid (Hkv * G/GT, B): log-sum-exp merge of the non-empty splits of one
+// (sequence, KV head, GT query heads) unit.  Units whose context fits one split
+// were finished by decode_kernel.  The kernel is bound by load latency, so
+// each thread owns whole output elements and issues the loads of eight
+// splits (their m, l and its u column) at once: one dependent round trip per
+// eight splits, no shared memory and no barrier.
+template <int D, int GT>
+__global__ __launch_bounds__((merge_threads<D, GT>())) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int THREADS = merge_threads<D, GT>();
+  constexpr int E = GT * D / THREADS;  // outputs per thread
+  static_assert(E * THREADS == GT * D, "outputs split evenly");
+  constexpr int SB = 8;                // splits per round of loads
   const int b = blockIdx.y;
   const int G = a.q_heads / a.kv_heads;
   const int subs = G / GT;
@@ -311,73 +361,75 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int h0 = kvh * G + (unit - kvh * subs) * GT;
   const int ns = (visible_keys(a.len[b], a.window, a.sink).count + a.chunk - 1) / a.chunk;
   if (ns <= 1) return;
-  __shared__ float s_w[GT][MAXS];
-  __shared__ float s_den[GT];
-  __shared__ float s_part[PARTS > 1 ? 256 : 1];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   const float *ws_unit = a.ws + (size_t)(b * a.q_heads + h0) * a.n_splits * (D + 2);
-  // split weights relative to the per-head maximum: one wave per head, one lane per split
-  for (int g = wave; g < GT; g += 4) {
-    const float *st = ws_unit + ((size_t)g * a.n_splits + min(lane, ns - 1)) * (D + 2);
-    const float ms = lane < ns ? st[0] : -INFINITY;
-    const float ls = lane < ns ? st[1] : 0.f;
-    float M = ms;
+
+  float M[E], num[E], den[E];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float w = lane < ns ? fast_exp2(ms - M) : 0.f;
-    float den = w * ls;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
-    s_w[g][lane] = w;
-    if (lane == 0) s_den[g] = den;
+  for (int e = 0; e < E; ++e) {
+    M[e] = -INFINITY;
+    num[e] = 0.f;
+    den[e] = 0.f;
   }
-  __syncthreads();
-  for (int t = tid; t < GT * D * PARTS; t += 256) {
-    const int part = t / (GT * D);
-    const int gd = t - part * GT * D;
-    const int g = gd / D;
-    const int d = gd - g * D;
-    const float *u = ws_unit + (size_t)g * a.n_splits * (D + 2) + 2 + d;
-    float num = 0.f;
-    for (int s0 = part * 8; s0 < ns; s0 += 8 * PARTS) {
-      float x[8];
+  for (int s0 = 0; s0 < ns; s0 += SB) {
+    float ms[E][SB], ls[E][SB], us[E][SB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = u[(size_t)min(s0 + i, ns - 1) * (D + 2)];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) num = fmaf(s0 + i < ns ? s_w[g][min(s0 + i, MAXS - 1)] : 0.f, x[i], num);
-    }
-    if constexpr (PARTS > 1) {
-      s_part[t] = num;
-    } else {
-      store_out(a.o, (size_t)(b * a.q_heads + h0 + g) * D + d, num / s_den[g], a.o_dt);
-    }
-  }
-  if constexpr (PARTS > 1) {
-    __syncthreads();
-    for (int t = tid; t < GT * D; t += 256) {
-      float num = 0.f;
-#pragma unroll
-      for (int p = 0; p < PARTS; ++p) num += s_part[p * GT * D + t];
+    for (int e = 0; e < E; ++e) {
+      const int t = e * THREADS + (int)threadIdx.x;
       const int g = t / D;
       const int d = t - g * D;
-      store_out(a.o, (size_t)(b * a.q_heads + h0 + g) * D + d, num / s_den[g], a.o_dt);
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        // clamped (always in bounds) and masked below
+        const float *st = ws_unit + ((size_t)g * a.n_splits + min(s0 + i, ns - 1)) * (D + 2);
+        ms[e][i] = st[0];
+        ls[e][i] = st[1];
+        us[e][i] = st[2 + d];
+      }
     }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float mx = M[e];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) mx = fmaxf(mx, s0 + i < ns ? ms[e][i] : -INFINITY);
+      // split 0 holds at least one visible key, so mx is finite from the first round on
+      const float f = fast_exp2(M[e] - mx);
+      num[e] *= f;
+      den[e] *= f;
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const float w = s0 + i < ns ? fast_exp2(ms[e][i] - mx) : 0.f;
+        num[e] = fmaf(w, us[e][i], num[e]);
+        den[e] = fmaf(w, ls[e][i], den[e]);
+      }
+      M[e] = mx;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int t = e * THREADS + (int)threadIdx.x;
+    const int g = t / D;
+    const int d = t - g * D;
+    store_out(a.o, (size_t)(b * a.q_heads + h0 + g) * D + d, num[e] / den[e], a.o_dt);
   }
 }
 
 template <class Tag, int D, int GT>
 static hipError_t launch_gt(const DecodeArgs &a, hipStream_t s) {
   // 16-byte K and V loads per lane per batch (two batches are in flight):
-  // six for one or two query heads per workgroup, four for larger groups
-  // (measured; and groups of 8 would not fit 256 registers with six)
+  // six for one to three query heads per workgroup, four for larger groups
+  // (which hold GT accumulators; eight heads would not fit 256 registers
+  // with six).  Measured on the GQA 32/8 batch-16 decode at 4096 keys:
+  // two slices per lane (NV = 2), six or eight loads, or 8-wave workgroups
+  // over 2048-key splits were no faster; none of the vector-ALU work is on
+  // the critical path there (removing the dot products and the P.V updates
+  // left the time unchanged).
+  constexpr int NV = 1, NW = 4;
   constexpr int U = GT >= 4 ? 4 : 6;
   const int units = a.q_heads / GT;  // = Hkv * (G / GT)
-  decode_kernel<Tag, D, GT, U><<<dim3(a.n_splits, units, a.batch), 256, 0, s>>>(a);
+  decode_kernel<Tag, D, GT, U, NV, NW><<<dim3(a.n_splits, units, a.batch), NW * 64, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
-  decode_merge_kernel<D, GT><<<dim3(units, a.batch), 256, 0, s>>>(a);
+  decode_merge_kernel<D, GT><<<dim3(units, a.batch), merge_threads<D, GT>(), 0, s>>>(a);
   return hipGetLastError();
 }
 
