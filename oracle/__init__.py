@@ -1,10 +1,12 @@
 """CPU fp64 oracle (test infrastructure; never imported by the product path)."""
 from .attention import (  # noqa: F401
     CacheModel,
+    PagedCacheModel,
     attend_row,
     brute,
     chunked,
     decode_cached,
+    decode_paged,
     decode_recompute,
     extend,
     kv_bytes,

@@ -22,7 +22,7 @@ Sources (the three web pages this method is described on):
   notes); the inference chapter, section 9.7: flash-style tiling is exact up to
   ordinary floating-point rounding.
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent:
 causal mask with the diagonal visible, bottom-right aligned for a decode
 query; scale = the float32 value 1/sqrt(D) passed by the caller; query head h
 uses KV head h // (H // Hkv).
@@ -363,3 +363,104 @@ class CacheModel:
         if (lengths < 0).any() or (lengths > self.max_T).any():
             raise RuntimeError("length out of range")
         self.lengths[layer] = lengths
+
+
+# --------------------------------------------------------------------------
+# paged cache model (inference chapter, section 9.6: the cache managed in
+# blocks instead of one contiguous max-length region per sequence; llm-perf-lab
+# README roadmap: vLLM-style paging with prefix sharing)
+# --------------------------------------------------------------------------
+class PagedCacheModel:
+    """Bit-level model of a block-paged cache.
+
+    A pool of ``num_blocks`` blocks per layer, K and V each laid out
+    [layer][block][Hkv][block_size][D] in the raw storage dtype.  Each of the
+    ``slots`` sequences owns a block table (a list of pool block indices, the
+    same for every layer): its logical position p lives in block
+    ``table[p // block_size]`` at row ``p % block_size``.  Two tables may name
+    the same block (prefix sharing); both then read, and may write, the same
+    rows.  Lengths are per (layer, slot); a slot holds at most
+    ``len(table) * block_size`` positions.
+    """
+
+    def __init__(self, layers, slots, num_blocks, block_size, kv_heads, head_dim, storage_dtype):
+        shape = (layers, num_blocks, kv_heads, block_size, head_dim)
+        self.k = np.zeros(shape, dtype=storage_dtype)
+        self.v = np.zeros(shape, dtype=storage_dtype)
+        self.block_size = block_size
+        self.tables = [[] for _ in range(slots)]
+        self.lengths = np.zeros((layers, slots), dtype=np.int64)
+
+    def capacity(self, slot):
+        return len(self.tables[slot]) * self.block_size
+
+    def set_blocks(self, slot, block_ids):
+        ids = [int(x) for x in block_ids]
+        if any(i < 0 or i >= self.k.shape[1] for i in ids):
+            raise RuntimeError("block index out of the pool")
+        if (self.lengths[:, slot] > len(ids) * self.block_size).any():
+            raise RuntimeError("table too short for the slot's length")
+        self.tables[slot] = ids
+
+    def where(self, slot, pos):
+        """(block, row) of logical position ``pos`` of ``slot``."""
+        return self.tables[slot][pos // self.block_size], pos % self.block_size
+
+    def _write(self, layer, slot, pos, k_row, v_row):
+        blk, row = self.where(slot, pos)
+        self.k[layer, blk, :, row] = k_row
+        self.v[layer, blk, :, row] = v_row
+
+    def prefill(self, layer, k, v):
+        T = k.shape[2]
+        if (self.lengths[layer] != 0).any():
+            raise RuntimeError("prefill needs an empty cache")
+        for s in range(len(self.tables)):
+            if T > self.capacity(s):
+                raise RuntimeError("prompt longer than the slot's blocks")
+        for s in range(len(self.tables)):
+            for t in range(T):
+                self._write(layer, s, t, k[s, :, t], v[s, :, t])
+        self.lengths[layer] = T
+
+    def append(self, layer, k_new, v_new):
+        for s in range(len(self.tables)):
+            if self.lengths[layer, s] >= self.capacity(s):
+                raise RuntimeError("slot full")
+        for s in range(len(self.tables)):
+            self._write(layer, s, int(self.lengths[layer, s]), k_new[s, :, 0], v_new[s, :, 0])
+        self.lengths[layer] += 1
+
+    def set_lengths(self, layer, lengths):
+        lengths = np.asarray(lengths, dtype=np.int64)
+        for s, L in enumerate(lengths):
+            if L < 0 or L > self.capacity(s):
+                raise RuntimeError("length out of range")
+        self.lengths[layer] = lengths
+
+    def gather(self, layer, slot):
+        """The slot's K and V rows in logical order: two (Hkv, L, D) arrays."""
+        L = int(self.lengths[layer, slot])
+        Hkv, D = self.k.shape[2], self.k.shape[4]
+        kg = np.empty((Hkv, L, D), dtype=self.k.dtype)
+        vg = np.empty((Hkv, L, D), dtype=self.v.dtype)
+        for p in range(L):
+            blk, row = self.where(slot, p)
+            kg[:, p] = self.k[layer, blk, :, row]
+            vg[:, p] = self.v[layer, blk, :, row]
+        return kg, vg
+
+
+def decode_paged(q: np.ndarray, model: PagedCacheModel, layer: int, scale: float, dtype: str,
+                 to_f64) -> np.ndarray:
+    """Decode step over a paged cache: each slot's rows gathered in logical
+    order, then the contiguous decode (``decode_cached``).  ``to_f64`` widens
+    the raw storage values (bf16 bits included) to float64."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, D = q.shape
+    out = np.empty((B, H, D), dtype=np.float64)
+    for s in range(B):
+        kg, vg = model.gather(layer, s)
+        L = kg.shape[1]
+        out[s:s + 1] = decode_cached(q[s:s + 1], to_f64(kg[None], dtype), to_f64(vg[None], dtype), [L], scale)
+    return out

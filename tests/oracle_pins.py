@@ -360,6 +360,86 @@ def check_window_ignores_hidden_keys(naive_windowed=oracle.naive_windowed):
     assert np.array_equal(got[:, :, i], base[:, :, i])
 
 
+def check_paged_addressing(PagedCacheModel=oracle.PagedCacheModel):
+    """Hand-worked placement: block size 2, table [5, 1, 3]; positions 0..5 land
+    at (block, row) = (5,0) (5,1) (1,0) (1,1) (3,0) (3,1); the 7th append is
+    refused (the slot holds 3 * 2 positions)."""
+    m = PagedCacheModel(1, 1, 6, 2, 1, 1, np.float32)
+    m.set_blocks(0, [5, 1, 3])
+    expect = [(5, 0), (5, 1), (1, 0), (1, 1), (3, 0), (3, 1)]
+    for p in range(6):
+        m.append(0, np.full((1, 1, 1, 1), 10.0 + p, np.float32), np.full((1, 1, 1, 1), -p, np.float32))
+    for p, (blk, row) in enumerate(expect):
+        assert m.k[0, blk, 0, row, 0] == 10.0 + p and m.v[0, blk, 0, row, 0] == -p
+    assert set(np.flatnonzero(m.k[0, :, 0, :, 0].any(axis=1))) == {1, 3, 5}
+    try:
+        m.append(0, np.zeros((1, 1, 1, 1), np.float32), np.zeros((1, 1, 1, 1), np.float32))
+    except RuntimeError:
+        pass
+    else:
+        raise AssertionError("append past the slot's blocks was accepted")
+
+
+def check_paged_equals_contiguous(PagedCacheModel=oracle.PagedCacheModel, decode_paged=oracle.decode_paged,
+                                  CacheModel=oracle.CacheModel, dtype="bf16"):
+    """The same prefill and appends through a paged cache with permuted block
+    tables and through the contiguous cache model: every slot gathers to the
+    contiguous rows bit for bit, and the paged decode equals the contiguous one
+    exactly, at every step."""
+    storage = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
+    B, H, Hkv, D, T, steps, bs = 3, 4, 2, 8, 5, 9, 4
+    max_T = T + steps
+    nb = -(-max_T // bs)
+    rng = np.random.default_rng(301)
+    perm = rng.permutation(B * nb + 3)  # a few pool blocks stay unused
+    tables = [list(perm[s * nb:(s + 1) * nb]) for s in range(B)]
+    paged = PagedCacheModel(2, B, B * nb + 3, bs, Hkv, D, storage)
+    for s in range(B):
+        paged.set_blocks(s, tables[s])
+    flat = CacheModel(2, B, Hkv, D, max_T, storage)
+    kh = round_to(rng.standard_normal((B, Hkv, max_T, D)), dtype)
+    vh = round_to(rng.standard_normal((B, Hkv, max_T, D)), dtype)
+    qh = round_to(rng.standard_normal((B, H, max_T, D)), dtype)
+    layer = 1
+    for c in (paged, flat):
+        c.prefill(layer, kh[:, :, :T], vh[:, :, :T])
+    for t in range(T, max_T):
+        for c in (paged, flat):
+            c.append(layer, kh[:, :, t:t + 1], vh[:, :, t:t + 1])
+        for s in range(B):
+            kg, vg = paged.gather(layer, s)
+            assert np.array_equal(kg, flat.k[layer, s, :, :t + 1]) and np.array_equal(vg, flat.v[layer, s, :, :t + 1])
+        got = decode_paged(to_f64(qh[:, :, t], dtype), paged, layer, 0.35, dtype, to_f64)
+        ref = oracle.decode_cached(to_f64(qh[:, :, t], dtype), to_f64(flat.k[layer], dtype),
+                                   to_f64(flat.v[layer], dtype), flat.lengths[layer], 0.35)
+        assert np.array_equal(got, ref), f"paged decode differs at position {t}"
+
+
+def check_paged_prefix_sharing(PagedCacheModel=oracle.PagedCacheModel, decode_paged=oracle.decode_paged):
+    """Two slots whose prompts share their first 8 positions: with the two full
+    blocks of that prefix shared between the tables, both slots decode exactly
+    as with private copies; the shared blocks hold the prefix once."""
+    dtype, B, H, Hkv, D, bs, T = "f16", 2, 2, 1, 8, 4, 10
+    rng = np.random.default_rng(311)
+    k = round_to(rng.standard_normal((B, Hkv, T + 1, D)), dtype)
+    v = round_to(rng.standard_normal((B, Hkv, T + 1, D)), dtype)
+    k[1, :, :8], v[1, :, :8] = k[0, :, :8], v[0, :, :8]
+    q = round_to(rng.standard_normal((B, H, D)), dtype)
+    shared = PagedCacheModel(1, B, 6, bs, Hkv, D, np.float16)
+    shared.set_blocks(0, [4, 0, 2])
+    shared.set_blocks(1, [4, 0, 5])
+    private = PagedCacheModel(1, B, 6, bs, Hkv, D, np.float16)
+    private.set_blocks(0, [4, 0, 2])
+    private.set_blocks(1, [1, 3, 5])
+    for c in (shared, private):
+        c.prefill(0, k[:, :, :T], v[:, :, :T])
+        c.append(0, k[:, :, T:T + 1], v[:, :, T:T + 1])
+    a = decode_paged(to_f64(q, dtype), shared, 0, 0.4, dtype, to_f64)
+    b = decode_paged(to_f64(q, dtype), private, 0, 0.4, dtype, to_f64)
+    assert np.array_equal(a, b)
+    assert not shared.k[0, [1, 3]].any(), "shared prefix was written twice"
+
+
 ALL_CHECKS = [
     check_kv_bytes, check_brute, check_row0_is_v0, check_zero_query_prefix_mean,
     check_two_key_logistic, check_rows_sum_to_one, check_large_scores, check_causality,
@@ -367,5 +447,6 @@ ALL_CHECKS = [
     check_decode_permutation, check_decode_matches_prefill_rows, check_cached_equals_recompute,
     check_extend_matches_prefill_rows, check_chunked_prefill_by_extend, check_extend_brute,
     check_window_special_cases, check_window_brute, check_window_decode_and_extend_rows,
-    check_window_ignores_hidden_keys,
+    check_window_ignores_hidden_keys, check_paged_addressing, check_paged_equals_contiguous,
+    check_paged_prefix_sharing,
 ]

@@ -132,8 +132,8 @@ def test_speculative_verify_with_rollback():
     kmix[:, :, P + 2:P + 5] = kh2[:, :, P + 2:P + 5]
     vmix[:, :, P + 2:P + 5] = vh2[:, :, P + 2:P + 5]
     ref2 = oracle.extend(f(qh2[:, :, P + 2:P + 5]), f(kmix), f(vmix), [P + 2] * B, scale)
-    check_output(o1, ref1, dtype, "verify round 1")
-    check_output(o2, ref2, dtype, "verify round 2 after rollback")
+    check_output(o1, ref1, dtype, "first verification")
+    check_output(o2, ref2, dtype, "second verification after rollback")
     assert c.lengths(0) == [P + 5] * B
     kb = host_bits(c.k_view(0))
     assert np.array_equal(kb[:, :, :P + 5], kmix[:, :, :P + 5].view(kb.dtype))

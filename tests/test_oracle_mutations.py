@@ -128,6 +128,12 @@ def _run_all(overrides):
             overrides.get("naive_windowed", oracle.naive_windowed)),
         "check_window_ignores_hidden_keys": lambda: pins.check_window_ignores_hidden_keys(
             overrides.get("naive_windowed", oracle.naive_windowed)),
+        "check_paged_addressing": lambda: pins.check_paged_addressing(
+            overrides.get("PagedCacheModel", oracle.PagedCacheModel)),
+        "check_paged_equals_contiguous": lambda: pins.check_paged_equals_contiguous(
+            overrides.get("PagedCacheModel", oracle.PagedCacheModel), oracle.decode_paged, oracle.CacheModel),
+        "check_paged_prefix_sharing": lambda: pins.check_paged_prefix_sharing(
+            overrides.get("PagedCacheModel", oracle.PagedCacheModel), oracle.decode_paged),
     }
     with np.errstate(all="ignore"):
         for name, fn in calls.items():
@@ -167,6 +173,14 @@ def _extend_visible(count):
     return f
 
 
+def _paged_variant(where):
+    """PagedCacheModel with another position -> (block, row) placement."""
+    class Variant(oracle.PagedCacheModel):
+        def where(self, slot, pos):
+            return where(self, slot, pos)
+    return Variant
+
+
 def _windowed_variant(rule):
     """naive_windowed with another visibility rule(i, j, W, S)."""
     def f(q, k, v, scale, W, S):
@@ -204,6 +218,11 @@ MUTANTS.update({
         lambda i, j, W, S: j <= i and (W <= 0 or i - j < W))},
     "window_sink_one_too_many": {"naive_windowed": _windowed_variant(
         lambda i, j, W, S: j <= i and (W <= 0 or i - j < W or j <= S))},
+    "paged_ignores_table": {"PagedCacheModel": _paged_variant(lambda m, slot, pos: (pos // m.block_size, pos % m.block_size))},
+    "paged_row_and_block_swapped": {"PagedCacheModel": _paged_variant(
+        lambda m, slot, pos: (m.tables[slot][pos % len(m.tables[slot])], (pos // len(m.tables[slot])) % m.block_size))},
+    "paged_block_off_by_one": {"PagedCacheModel": _paged_variant(
+        lambda m, slot, pos: (m.tables[slot][min((pos + 1) // m.block_size, len(m.tables[slot]) - 1)], pos % m.block_size))},
     "window_not_causal": {"naive_windowed": _windowed_variant(
         lambda i, j, W, S: W <= 0 and j <= i or W > 0 and (abs(i - j) < W or j < S))},
 })
