@@ -381,6 +381,55 @@ def window_measurements(kv, w, dec, full_us, window=1024, sink=4, reps=5):
             "speedup_vs_full_context": round(full_us / us, 2)}
 
 
+def paged_measurements(kv, w, dec, full_us, block_size=64, layers=4, reps=5):
+    """Decode of the ragged batch-32 contexts from a block-paged cache: each
+    sequence holds ceil(L / block_size) blocks drawn from one shuffled pool (no
+    capacity reserved beyond the blocks in use).  Same algorithmic bytes as the
+    contiguous decode."""
+    ctx = [int(L) for L in dec["ctx"]]
+    nblk = [-(-L // block_size) for L in ctx]
+    num_blocks = sum(nblk)
+    dev = dec["q"][0].device
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    c = kv.PagedKVCache(layers, w.batch, max(nblk), num_blocks, block_size, w.q_heads, w.kv_heads, w.head_dim,
+                        dt, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(55)
+    for layer in range(layers):
+        fill_normal_(c.k_view(layer), gen)
+        fill_normal_(c.v_view(layer), gen)
+    perm = torch.randperm(num_blocks, generator=torch.Generator().manual_seed(56)).tolist()
+    off = 0
+    for s, n in enumerate(nblk):
+        c.set_blocks(s, perm[off:off + n])
+        off += n
+    c.set_lengths(ctx)
+    outs = [torch.empty_like(dec["q"][l]) for l in range(layers)]
+    calls = [c.bind_decode(l, dec["q"][l], outs[l], scale=w.scale) for l in range(layers)]
+
+    def run():
+        for f in calls:
+            f()
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps / layers
+    out = {"workload": f"batch {w.batch}, contexts U[{w.ctx_lo},{w.ctx_hi}], {block_size}-position blocks, "
+                       f"shuffled pool",
+           "us_per_layer": round(us, 1),
+           "value": round(dec["bytes_kernel"] / (us * 1e-6) / 1e9, 1), "unit": "GB/s",
+           "vs_contiguous_time": round(us / full_us, 3),
+           "pool_bytes_per_layer": c.nbytes // layers,
+           "contiguous_bytes_per_layer": dec["cache"].nbytes // w.layers}
+    c.close()
+    return out
+
+
 def timed(fn, steps, warmup):
     for _ in range(warmup):
         fn(None)
@@ -555,6 +604,8 @@ def main():
     if dec is not None:
         log("decode under a sliding window")
         out["decode_window"] = window_measurements(kv, w5, dec, out["roofline"]["mean_launch_ms"] * 1e3)
+        log("decode from a paged cache")
+        out["decode_paged"] = paged_measurements(kv, w5, dec, out["roofline"]["mean_launch_ms"] * 1e3)
     if dec is not None and pre is not None:
         log("extend: chunked prefill and 4-token verification")
         out["extend"] = extend_measurements(kv, w5, dec, pre)

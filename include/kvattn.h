@@ -160,6 +160,72 @@ int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, cons
 int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scale,
                   kvattn_dtype o_dtype, void *stream);
 
+/* ---------------------------------------------------------------- paged cache
+ * The cache managed in fixed-size blocks instead of one max-length region per
+ * sequence (inference chapter, section 9.6, Continuous Batching and Paged KV;
+ * the llm-perf-lab README's vLLM-style paging with prefix sharing).  A pool of
+ * num_blocks blocks per layer, laid out [layer][K|V][num_blocks][Hkv]
+ * [block_size][D]; each of `slots` sequences has a block table (the same for
+ * every layer): its position p lives in block table[p / block_size], row
+ * p % block_size.  Tables may share blocks (prefix sharing); rows of a shared
+ * block must be the same for every slot that writes them.  Calls cover every
+ * slot, like the contiguous cache (slots = batch); lengths are per (layer,
+ * slot) with a host mirror; a slot holds at most n_blocks * block_size
+ * positions.  No sliding window on a paged cache. */
+typedef struct kvattn_paged kvattn_paged; /* opaque, library-owned */
+
+/* Pool bytes: 2 * layers * num_blocks * block_size * kv_heads * head_dim *
+ * bytes(dt) (the capacity formula with T = num_blocks * block_size, batch 1);
+ * 0 for a non-positive argument or an unknown dtype.  Pure host function. */
+size_t kvattn_paged_bytes(int layers, int num_blocks, int block_size, int kv_heads, int head_dim,
+                          kvattn_dtype dt);
+
+/* Create a paged cache: `slots` sequences of up to max_blocks blocks each,
+ * from a pool of num_blocks blocks of block_size positions (a power of two in
+ * [16, 4096], else UNSUPPORTED).  device_buf as for kvattn_cache_alloc.  All
+ * tables are empty and all lengths 0.  Synchronises the device once. */
+int kvattn_paged_alloc(kvattn_paged **out, int layers, int slots, int max_blocks, int num_blocks,
+                       int block_size, int q_heads, int kv_heads, int head_dim, kvattn_dtype dt,
+                       void *device_buf, size_t device_buf_bytes);
+
+/* Synchronise the device, release what the library allocated and the object. */
+int kvattn_paged_free(kvattn_paged *p);
+
+/* Device addresses of layer `layer`'s K and V pools, each (num_blocks, Hkv,
+ * block_size, D). */
+int kvattn_paged_kv_ptr(const kvattn_paged *p, int layer, void **k, void **v);
+
+/* Set the block table of one slot to host_block_ids[0..n_blocks-1] (pool
+ * indices; n_blocks <= max_blocks).  INVALID_ARG for an index outside the
+ * pool; CAPACITY if a layer's length of the slot exceeds n_blocks *
+ * block_size.  Enqueued on `stream` (the ids are copied before the call
+ * returns); later calls must be on the same stream or ordered after it. */
+int kvattn_paged_set_blocks(kvattn_paged *p, int slot, const int32_t *host_block_ids, int n_blocks,
+                            void *stream);
+
+/* Lengths of one layer (>= 0) or of every layer (-1), each within its slot's
+ * blocks (else CAPACITY): truncation and rollback, as for the contiguous cache. */
+int kvattn_paged_set_lengths(kvattn_paged *p, int layer, const int32_t *host_lens, void *stream);
+int kvattn_paged_get_lengths(const kvattn_paged *p, int layer, int32_t *host_lens);
+
+/* Prefill of one layer: causal attention of the T prompt queries of every
+ * slot (q (slots,H,T,D), k/v (slots,Hkv,T,D), o in o_dtype) as
+ * kvattn_prefill, then a bit-exact copy of k, v into each slot's blocks at
+ * positions [0, T); lengths become T.  STATE unless every length is 0;
+ * CAPACITY if T exceeds a slot's blocks. */
+int kvattn_paged_prefill(kvattn_paged *p, int layer, const void *q, const void *k, const void *v,
+                         void *o, int T, float scale, kvattn_dtype o_dtype, void *stream);
+
+/* Append one position per slot (k_new/v_new (slots,Hkv,1,D)) at its length,
+ * in the block that holds that position; len += 1.  CAPACITY if a slot's
+ * blocks are full. */
+int kvattn_paged_append(kvattn_paged *p, int layer, const void *k_new, const void *v_new, void *stream);
+
+/* Decode over the paged cache: as kvattn_decode, each slot's query attending
+ * its len positions, read through its block table. */
+int kvattn_paged_decode(kvattn_paged *p, int layer, const void *q, void *o, float scale,
+                        kvattn_dtype o_dtype, void *stream);
+
 /* Static description of a status code. */
 const char *kvattn_status_string(int status);
 

@@ -17,7 +17,7 @@ import os
 
 import torch
 
-__all__ = ["KVCache", "KVAttnError", "cache_bytes", "lib", "LIB_PATH"]
+__all__ = ["KVCache", "PagedKVCache", "KVAttnError", "cache_bytes", "paged_bytes", "lib", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # KVATTN_LIB names another build of the library (for example a tuning variant)
@@ -52,6 +52,23 @@ _SIGS = {
                       + [ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "kvattn_paged_bytes": (ctypes.c_size_t, [ctypes.c_int] * 6),
+    "kvattn_paged_alloc": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p)] + [ctypes.c_int] * 9
+                           + [ctypes.c_void_p, ctypes.c_size_t]),
+    "kvattn_paged_free": (ctypes.c_int, [ctypes.c_void_p]),
+    "kvattn_paged_kv_ptr": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p)]),
+    "kvattn_paged_set_blocks": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
+                                               ctypes.c_int, ctypes.c_void_p]),
+    "kvattn_paged_set_lengths": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
+                                                ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]),
+    "kvattn_paged_get_lengths": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int32)]),
+    "kvattn_paged_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 4
+                             + [ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "kvattn_paged_append": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p]),
+    "kvattn_paged_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvattn_measure_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                                   ctypes.c_void_p]),
@@ -302,6 +319,141 @@ class KVCache:
     def close(self) -> None:
         if self._handle and self._handle.value:
             _check(lib().kvattn_cache_free(self._handle), "kvattn_cache_free")
+            self._handle = ctypes.c_void_p()
+        self._buf = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def paged_bytes(layers: int, num_blocks: int, block_size: int, kv_heads: int, head_dim: int, dtype) -> int:
+    """Block-pool bytes of a paged cache (computed by the C library)."""
+    return int(lib().kvattn_paged_bytes(layers, num_blocks, block_size, kv_heads, head_dim, _DT[dtype]))
+
+
+class PagedKVCache:
+    """A block-paged KV cache on one GPU: a pool of ``num_blocks`` blocks of
+    ``block_size`` positions per layer and one block table per slot.
+
+    The pool is a PyTorch allocation handed to the C library, exposed per
+    layer by ``k_view``/``v_view`` as (num_blocks, Hkv, block_size, D).
+    """
+
+    def __init__(self, layers: int, slots: int, max_blocks: int, num_blocks: int, block_size: int,
+                 q_heads: int, kv_heads: int, head_dim: int, dtype=torch.float16, device=None):
+        if dtype not in _DT:
+            raise TypeError(f"unsupported dtype {dtype}")
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.layers, self.slots, self.max_blocks, self.num_blocks = layers, slots, max_blocks, num_blocks
+        self.block_size, self.q_heads, self.kv_heads, self.head_dim, self.dtype = (
+            block_size, q_heads, kv_heads, head_dim, dtype)
+        self.nbytes = paged_bytes(layers, num_blocks, block_size, kv_heads, head_dim, dtype)
+        if self.nbytes == 0:
+            raise KVAttnError(-1, "PagedKVCache")
+        self._handle = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            self._buf = torch.empty(self.nbytes, dtype=torch.uint8, device=self.device)
+            torch.cuda.synchronize(self.device)
+            _check(lib().kvattn_paged_alloc(ctypes.byref(self._handle), layers, slots, max_blocks, num_blocks,
+                                            block_size, q_heads, kv_heads, head_dim, _DT[dtype], _ptr(self._buf),
+                                            self.nbytes), "kvattn_paged_alloc")
+
+    def _view(self, layer: int, which: int) -> torch.Tensor:
+        if not 0 <= layer < self.layers:
+            raise IndexError(layer)
+        block = self.nbytes // (2 * self.layers)
+        off = (2 * layer + which) * block
+        t = self._buf[off:off + block].view(self.dtype)
+        return t.view(self.num_blocks, self.kv_heads, self.block_size, self.head_dim)
+
+    def k_view(self, layer: int) -> torch.Tensor:
+        return self._view(layer, 0)
+
+    def v_view(self, layer: int) -> torch.Tensor:
+        return self._view(layer, 1)
+
+    def set_blocks(self, slot: int, block_ids) -> None:
+        ids = [int(x) for x in block_ids]
+        arr = (ctypes.c_int32 * max(1, len(ids)))(*ids)
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_paged_set_blocks(self._handle, slot, arr, len(ids), _stream_ptr(self.device)),
+                   "kvattn_paged_set_blocks")
+
+    def set_lengths(self, lengths, layer: int = -1) -> None:
+        arr = (ctypes.c_int32 * self.slots)(*[int(x) for x in lengths])
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_paged_set_lengths(self._handle, layer, arr, _stream_ptr(self.device)),
+                   "kvattn_paged_set_lengths")
+
+    def lengths(self, layer: int) -> list:
+        arr = (ctypes.c_int32 * self.slots)()
+        _check(lib().kvattn_paged_get_lengths(self._handle, layer, arr), "kvattn_paged_get_lengths")
+        return list(arr)
+
+    def _tensor(self, t, shape, name, dtype=None):
+        KVCache._tensor(self, t, shape, name, dtype)
+
+    def _scale(self, scale):
+        return float(1.0 / math.sqrt(self.head_dim)) if scale is None else float(scale)
+
+    def prefill(self, layer: int, q, k, v, out=None, scale=None, out_dtype=None) -> torch.Tensor:
+        S, H, Hkv, D = self.slots, self.q_heads, self.kv_heads, self.head_dim
+        T = q.shape[2] if q.dim() == 4 else -1
+        self._tensor(q, (S, H, T, D), "q")
+        self._tensor(k, (S, Hkv, T, D), "k")
+        self._tensor(v, (S, Hkv, T, D), "v")
+        od = out_dtype or self.dtype
+        if out is None:
+            out = torch.empty((S, H, T, D), dtype=od, device=self.device)
+        self._tensor(out, (S, H, T, D), "out", od)
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_paged_prefill(self._handle, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(out), T,
+                                              self._scale(scale), _DT[od], _stream_ptr(self.device)),
+                   "kvattn_paged_prefill")
+        return out
+
+    def append(self, layer: int, k_new, v_new) -> None:
+        shape = (self.slots, self.kv_heads, 1, self.head_dim)
+        self._tensor(k_new, shape, "k_new")
+        self._tensor(v_new, shape, "v_new")
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_paged_append(self._handle, layer, _ptr(k_new), _ptr(v_new),
+                                             _stream_ptr(self.device)), "kvattn_paged_append")
+
+    def decode(self, layer: int, q, out=None, scale=None, out_dtype=None) -> torch.Tensor:
+        shape = (self.slots, self.q_heads, 1, self.head_dim)
+        self._tensor(q, shape, "q")
+        od = out_dtype or self.dtype
+        if out is None:
+            out = torch.empty(shape, dtype=od, device=self.device)
+        self._tensor(out, shape, "out", od)
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_paged_decode(self._handle, layer, _ptr(q), _ptr(out), self._scale(scale), _DT[od],
+                                             _stream_ptr(self.device)), "kvattn_paged_decode")
+        return out
+
+    def bind_decode(self, layer: int, q, out, scale=None):
+        """Pre-bound decode call (arguments checked and marshalled once)."""
+        shape = (self.slots, self.q_heads, 1, self.head_dim)
+        self._tensor(q, shape, "q")
+        self._tensor(out, shape, "out", out.dtype)
+        fn = lib().kvattn_paged_decode
+        args = (self._handle, layer, _ptr(q), _ptr(out), ctypes.c_float(self._scale(scale)), _DT[out.dtype],
+                _stream_ptr(self.device))
+        return lambda: _check(fn(*args), "kvattn_paged_decode")
+
+    def close(self) -> None:
+        if self._handle and self._handle.value:
+            _check(lib().kvattn_paged_free(self._handle), "kvattn_paged_free")
             self._handle = ctypes.c_void_p()
         self._buf = None
 

@@ -20,7 +20,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int h = i / vec_per_row;
     const int w = i - h * vec_per_row;
     const size_t src = ((size_t)(b * a.kv_heads + h) * a.row_bytes) + (size_t)w * 16;
-    const size_t dst = (((size_t)(b * a.kv_heads + h) * a.max_T + pos) * a.row_bytes) + (size_t)w * 16;
+    size_t row;
+    if (a.table) {  // paged: the block holding position pos of sequence b
+      const int blk = a.table[(size_t)b * a.max_blocks + (pos >> a.block_log2)];
+      row = (((size_t)blk * a.kv_heads + h) << a.block_log2) + (pos & ((1 << a.block_log2) - 1));
+    } else {
+      row = (size_t)(b * a.kv_heads + h) * a.max_T + pos;
+    }
+    const size_t dst = row * a.row_bytes + (size_t)w * 16;
     const uint4 kv = *reinterpret_cast<const uint4 *>(a.k_new + src);
     const uint4 vv = *reinterpret_cast<const uint4 *>(a.v_new + src);
     *reinterpret_cast<uint4 *>(a.k_layer + dst) = kv;
@@ -57,6 +64,32 @@ hipError_t launch_extend_copy(const ExtendCopyArgs &a, hipStream_t s) {
   const int vec_per_row = a.row_bytes >> 4;
   const unsigned chunks = (unsigned)(((size_t)a.T * vec_per_row + 255) / 256);
   extend_copy_kernel<<<dim3(chunks, a.kv_heads, a.batch), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// Paged prefill: prompt rows [0, T) of each (sequence, KV head) to their
+// blocks (bit copies); grid (row chunks, Hkv, B).  len[b] = T.
+__global__ __launch_bounds__(256) void paged_write_kernel(PagedWriteArgs a) {
+  const int b = blockIdx.z;
+  const int h = blockIdx.y;
+  if (blockIdx.x == 0 && h == 0 && threadIdx.x == 0) a.len[b] = a.T;
+  const int vec_per_row = a.row_bytes >> 4;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= a.T * vec_per_row) return;
+  const int t = idx / vec_per_row;
+  const int w = idx - t * vec_per_row;
+  const int blk = a.table[(size_t)b * a.max_blocks + (t >> a.block_log2)];
+  const size_t row = (((size_t)blk * a.kv_heads + h) << a.block_log2) + (t & ((1 << a.block_log2) - 1));
+  const size_t src = ((size_t)(b * a.kv_heads + h) * a.T + t) * a.row_bytes + (size_t)w * 16;
+  const size_t dst = row * a.row_bytes + (size_t)w * 16;
+  *reinterpret_cast<uint4 *>(a.k_pool + dst) = *reinterpret_cast<const uint4 *>(a.k_new + src);
+  *reinterpret_cast<uint4 *>(a.v_pool + dst) = *reinterpret_cast<const uint4 *>(a.v_new + src);
+}
+
+hipError_t launch_paged_write(const PagedWriteArgs &a, hipStream_t s) {
+  const int vec_per_row = a.row_bytes >> 4;
+  const unsigned chunks = (unsigned)(((size_t)a.T * vec_per_row + 255) / 256);
+  paged_write_kernel<<<dim3(chunks, a.kv_heads, a.batch), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -28,6 +28,11 @@ struct AppendArgs {
   const char *v_new;
   int32_t *len;         // layer's lengths [B]
   int batch, kv_heads, max_T, row_bytes;
+  // paged cache: k_layer/v_layer are the layer's block pools (num_blocks, Hkv,
+  // 2^block_log2, D) and row p of sequence b lives in block table[b *
+  // max_blocks + (p >> block_log2)]; null for the contiguous cache
+  const int32_t *table;
+  int block_log2, max_blocks;
 };
 
 struct DecodeArgs {
@@ -41,7 +46,14 @@ struct DecodeArgs {
   int window, sink;     // sliding window (0: none) and attention-sink positions
   float scale_log2;     // scale * log2(e)
   kvattn_dtype dt, o_dt;
+  // paged cache (as in AppendArgs); null table for the contiguous cache
+  const int32_t *table;
+  int block_log2, max_blocks;
 };
+
+// table entries a paged decode split stages in LDS: one split spans at most
+// chunk / block_size + 1 blocks
+constexpr int kPagedTab = 512;
 
 // The keys a decode query at position L - 1 sees, as one run of visible
 // indices 0 .. count - 1: the first `sink` positions, then the last `window`
@@ -83,7 +95,20 @@ struct ExtendCopyArgs {
   int batch, kv_heads, max_T, row_bytes, T;
 };
 
+// Prefill rows [0, T) of each (sequence, KV head) copied into a paged
+// cache's blocks (bit copies); len[b] = T.
+struct PagedWriteArgs {
+  char *k_pool;         // layer's K blocks (num_blocks, Hkv, 2^block_log2, D)
+  char *v_pool;
+  const char *k_new;    // (B, Hkv, T, D)
+  const char *v_new;
+  int32_t *len;         // layer's lengths [B]
+  const int32_t *table; // [B][max_blocks]
+  int batch, kv_heads, T, row_bytes, block_log2, max_blocks;
+};
+
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+hipError_t launch_paged_write(const PagedWriteArgs &a, hipStream_t s);
 hipError_t launch_set_lengths(int32_t *dst, int layers, int batch, const int32_t *host_lens,
                               hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);

@@ -102,7 +102,7 @@ __device__ __forceinline__ void store_out(void *o, size_t idx, float x, kvattn_d
 // `chunk` keys of one KV head, for GT query heads of its group.  LPR lanes
 // share one key row, each holding NV 16-byte slices of it (columns cl + v *
 // LPR * EPL), so one load instruction reads RPW whole rows.
-template <class Tag, int D, int GT, int U, int NV, int NW>
+template <class Tag, int D, int GT, int U, int NV, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   constexpr int EPL = Tag::EPL;
   constexpr int LPR = D / (EPL * NV);  // lanes that share one key row
@@ -132,12 +132,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int rg = lane / LPR;
   const int cl = (lane % LPR) * EPL;
 
-  const size_t head_off = (size_t)(b * a.kv_heads + kvh) * a.max_T * D;
-  const char *Kb = (const char *)a.k_layer + (head_off + (size_t)kb * D + cl) * ESZ;
-  const char *Vb = (const char *)a.v_layer + (head_off + (size_t)kb * D + cl) * ESZ;
+  // contiguous: this split's first row; paged: the pool (rows are found
+  // through the block table, whose entries for this split sit in LDS)
+  const size_t base = PAGED ? (size_t)cl : ((size_t)(b * a.kv_heads + kvh) * a.max_T + kb) * D + cl;
+  const char *Kb = (const char *)a.k_layer + base * ESZ;
+  const char *Vb = (const char *)a.v_layer + base * ESZ;
   // rows of this split at or past `jump` lie after the gap between sink and window
   const int jump = vk.first - kb;
   const int gap = vk.gap;
+  __shared__ int32_t s_tab[PAGED ? kPagedTab : 1];
+  int blk0 = 0;
+  if constexpr (PAGED) {  // no window with a paged cache: position = visible index
+    blk0 = kb >> a.block_log2;
+    const int nblk = ((kb + rows - 1) >> a.block_log2) - blk0 + 1;
+    for (int i = tid; i < nblk; i += NW * 64) s_tab[i] = a.table[(size_t)b * a.max_blocks + blk0 + i];
+    __syncthreads();
+  }
 
   uint4 qv[GT][NV];
 #pragma unroll
@@ -173,11 +183,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       int r = min(((ib * U + u) * NW + wave) * RPW + rg, rows - 1);
-      r += r >= jump ? gap : 0;
+      size_t row;
+      if constexpr (PAGED) {
+        const int pos = kb + r;
+        const int blk = s_tab[(pos >> a.block_log2) - blk0];
+        row = (((size_t)blk * a.kv_heads + kvh) << a.block_log2) + (pos & ((1 << a.block_log2) - 1));
+      } else {
+        row = (size_t)(r + (r >= jump ? gap : 0));
+      }
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         // streamed once: nontemporal loads (measured 5% faster than cached ones)
-        const size_t off = ((size_t)r * D + v * VSTRIDE) * ESZ;
+        const size_t off = (row * D + v * VSTRIDE) * ESZ;
         const u32x4 tk = __builtin_nontemporal_load((const u32x4 *)(Kb + off));
         const u32x4 tv = __builtin_nontemporal_load((const u32x4 *)(Vb + off));
         kr[u][v] = make_uint4(tk[0], tk[1], tk[2], tk[3]);
@@ -413,8 +430,8 @@ __global__ __launch_bounds__((merge_threads<D, GT>())) void decode_merge_kernel(
   }
 }
 
-template <class Tag, int D, int GT>
-static hipError_t launch_gt(const DecodeArgs &a, hipStream_t s) {
+template <class Tag, int D, int GT, bool PAGED>
+static hipError_t launch_gt_layout(const DecodeArgs &a, hipStream_t s) {
   // 16-byte K and V loads per lane per batch (two batches are in flight):
   // six for one to three query heads per workgroup, four for larger groups
   // (which hold GT accumulators; eight heads would not fit 256 registers
@@ -426,11 +443,17 @@ static hipError_t launch_gt(const DecodeArgs &a, hipStream_t s) {
   constexpr int NV = 1, NW = 4;
   constexpr int U = GT >= 4 ? 4 : 6;
   const int units = a.q_heads / GT;  // = Hkv * (G / GT)
-  decode_kernel<Tag, D, GT, U, NV, NW><<<dim3(a.n_splits, units, a.batch), NW * 64, 0, s>>>(a);
+  decode_kernel<Tag, D, GT, U, NV, NW, PAGED><<<dim3(a.n_splits, units, a.batch), NW * 64, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
   decode_merge_kernel<D, GT><<<dim3(units, a.batch), merge_threads<D, GT>(), 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <class Tag, int D, int GT>
+static hipError_t launch_gt(const DecodeArgs &a, hipStream_t s) {
+  if (a.table) return launch_gt_layout<Tag, D, GT, true>(a, s);
+  return launch_gt_layout<Tag, D, GT, false>(a, s);
 }
 
 template <class Tag, int D>

@@ -355,6 +355,9 @@ int kvattn_append(kvattn_cache *c, int layer, const void *k_new, const void *v_n
   a.kv_heads = c->kv_heads;
   a.max_T = c->max_T;
   a.row_bytes = c->head_dim * c->elem;
+  a.table = nullptr;
+  a.block_log2 = 0;
+  a.max_blocks = 0;
   hipError_t e = launch_append(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   for (int b = 0; b < c->batch; ++b) hl[b] += 1;
@@ -392,8 +395,353 @@ int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scal
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dt = c->dt;
   a.o_dt = o_dtype;
+  a.table = nullptr;
+  a.block_log2 = 0;
+  a.max_blocks = 0;
   hipError_t e = launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return KVATTN_OK;
+}
+
+// ---------------------------------------------------------------- paged cache
+// Inference chapter, section 9.6: the cache managed in fixed-size blocks
+// instead of one max-length region per sequence; llm-perf-lab README: vLLM
+// style paging with prefix sharing.  One pool allocation laid out
+// [layer][K|V][num_blocks][Hkv][block_size][D]; one block table per slot
+// (device, [slots][max_blocks], the same for every layer); lengths
+// [layer][slots] on the device with a host mirror.
+
+}  // extern "C"
+
+struct kvattn_paged {
+  int layers, slots, q_heads, kv_heads, head_dim;
+  int num_blocks, block_size, block_log2, max_blocks;
+  kvattn_dtype dt;
+  int elem;
+  size_t payload_bytes, layer_bytes;
+  char *base;
+  bool owns_base;
+  int32_t *d_len;              // [layers][slots]
+  std::vector<int32_t> h_len;  // host mirror
+  int32_t *d_table;            // [slots][max_blocks]
+  std::vector<int> h_nblk;     // table entries set per slot
+  float *d_ws;
+  int chunk, n_splits;
+  int device;
+};
+
+namespace {
+
+int paged_check_layer(const kvattn_paged *p, int layer) {
+  if (!p || layer < 0 || layer >= p->layers) return KVATTN_ERR_INVALID_ARG;
+  return KVATTN_OK;
+}
+
+int paged_check_device(const kvattn_paged *p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != p->device) {
+    std::snprintf(g_last_error, sizeof g_last_error,
+                  "paged cache lives on device %d but device %d is current", p->device, dev);
+    return KVATTN_ERR_STATE;
+  }
+  return KVATTN_OK;
+}
+
+char *paged_k(const kvattn_paged *p, int layer) { return p->base + (size_t)layer * p->layer_bytes; }
+char *paged_v(const kvattn_paged *p, int layer) { return paged_k(p, layer) + p->layer_bytes / 2; }
+int paged_capacity(const kvattn_paged *p, int slot) { return p->h_nblk[slot] * p->block_size; }
+
+}  // namespace
+
+extern "C" {
+
+size_t kvattn_paged_bytes(int layers, int num_blocks, int block_size, int kv_heads, int head_dim,
+                          kvattn_dtype dt) {
+  const int e = elem_bytes(dt);
+  if (layers <= 0 || num_blocks <= 0 || block_size <= 0 || kv_heads <= 0 || head_dim <= 0 || e == 0) return 0;
+  return (size_t)2 * layers * num_blocks * (size_t)block_size * kv_heads * head_dim * e;
+}
+
+int kvattn_paged_alloc(kvattn_paged **out, int layers, int slots, int max_blocks, int num_blocks,
+                       int block_size, int q_heads, int kv_heads, int head_dim, kvattn_dtype dt,
+                       void *device_buf, size_t device_buf_bytes) {
+  if (!out) return KVATTN_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (layers <= 0 || slots <= 0 || max_blocks <= 0 || num_blocks <= 0 || block_size <= 0 || q_heads <= 0 ||
+      kv_heads <= 0 || head_dim <= 0)
+    return KVATTN_ERR_INVALID_ARG;
+  if (elem_bytes(dt) == 0 || !supported_dim(head_dim) || q_heads % kv_heads != 0)
+    return KVATTN_ERR_UNSUPPORTED;
+  if (block_size < 16 || block_size > 4096 || (block_size & (block_size - 1)) != 0)
+    return KVATTN_ERR_UNSUPPORTED;
+  if ((long long)max_blocks * block_size > (1LL << 30)) return KVATTN_ERR_UNSUPPORTED;
+  const int capacity = max_blocks * block_size;
+  const int chunk = decode_chunk(head_dim, q_heads / kv_heads, capacity);
+  if (chunk / block_size + 2 > kPagedTab) return KVATTN_ERR_UNSUPPORTED;
+  const size_t bytes = kvattn_paged_bytes(layers, num_blocks, block_size, kv_heads, head_dim, dt);
+  if (device_buf) {
+    if (device_buf_bytes < bytes) return KVATTN_ERR_OOM;
+    if (((uintptr_t)device_buf & 255u) != 0) return KVATTN_ERR_INVALID_ARG;
+  }
+  kvattn_paged *p = new (std::nothrow) kvattn_paged();
+  if (!p) return KVATTN_ERR_OOM;
+  p->layers = layers;
+  p->slots = slots;
+  p->q_heads = q_heads;
+  p->kv_heads = kv_heads;
+  p->head_dim = head_dim;
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->block_log2 = __builtin_ctz((unsigned)block_size);
+  p->max_blocks = max_blocks;
+  p->dt = dt;
+  p->elem = elem_bytes(dt);
+  p->payload_bytes = bytes;
+  p->layer_bytes = bytes / layers;
+  p->chunk = chunk;
+  p->n_splits = (capacity + chunk - 1) / chunk;
+  p->h_len.assign((size_t)layers * slots, 0);
+  p->h_nblk.assign(slots, 0);
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipGetDevice");
+  }
+  if (device_buf) {
+    p->base = (char *)device_buf;
+    p->owns_base = false;
+  } else {
+    e = hipMalloc((void **)&p->base, bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      delete p;
+      std::snprintf(g_last_error, sizeof g_last_error, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+      return KVATTN_ERR_OOM;
+    }
+    p->owns_base = true;
+  }
+  const size_t len_bytes = sizeof(int32_t) * (size_t)layers * slots;
+  const size_t tab_bytes = sizeof(int32_t) * (size_t)slots * max_blocks;
+  const size_t ws_bytes = sizeof(float) * (size_t)slots * q_heads * p->n_splits * (head_dim + 2);
+  e = hipMalloc((void **)&p->d_len, len_bytes);
+  if (e == hipSuccess) e = hipMalloc((void **)&p->d_table, tab_bytes);
+  if (e == hipSuccess) e = hipMalloc((void **)&p->d_ws, ws_bytes);
+  if (e == hipSuccess) e = hipMemset(p->d_len, 0, len_bytes);
+  if (e == hipSuccess) e = hipMemset(p->d_table, 0, tab_bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    int rc = hip_fail(e, "paged cache side buffers");
+    (void)hipGetLastError();
+    if (p->d_len) (void)hipFree(p->d_len);
+    if (p->d_table) (void)hipFree(p->d_table);
+    if (p->d_ws) (void)hipFree(p->d_ws);
+    if (p->owns_base) (void)hipFree(p->base);
+    delete p;
+    return e == hipErrorOutOfMemory ? KVATTN_ERR_OOM : rc;
+  }
+  *out = p;
+  return KVATTN_OK;
+}
+
+int kvattn_paged_free(kvattn_paged *p) {
+  if (!p) return KVATTN_ERR_INVALID_ARG;
+  hipError_t e = hipDeviceSynchronize();
+  hipError_t e1 = hipFree(p->d_len);
+  hipError_t e2 = hipFree(p->d_table);
+  hipError_t e3 = hipFree(p->d_ws);
+  hipError_t e4 = p->owns_base ? hipFree(p->base) : hipSuccess;
+  delete p;
+  if (e != hipSuccess) return hip_fail(e, "kvattn_paged_free sync");
+  if (e1 != hipSuccess) return hip_fail(e1, "hipFree(lengths)");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipFree(block tables)");
+  if (e3 != hipSuccess) return hip_fail(e3, "hipFree(workspace)");
+  if (e4 != hipSuccess) return hip_fail(e4, "hipFree(pool)");
+  return KVATTN_OK;
+}
+
+int kvattn_paged_kv_ptr(const kvattn_paged *p, int layer, void **k, void **v) {
+  int rc = paged_check_layer(p, layer);
+  if (rc) return rc;
+  if (!k || !v) return KVATTN_ERR_INVALID_ARG;
+  *k = paged_k(p, layer);
+  *v = paged_v(p, layer);
+  return KVATTN_OK;
+}
+
+int kvattn_paged_set_blocks(kvattn_paged *p, int slot, const int32_t *host_block_ids, int n_blocks,
+                            void *stream) {
+  if (!p || slot < 0 || slot >= p->slots || n_blocks < 0 || n_blocks > p->max_blocks)
+    return KVATTN_ERR_INVALID_ARG;
+  if (n_blocks > 0 && !host_block_ids) return KVATTN_ERR_INVALID_ARG;
+  for (int i = 0; i < n_blocks; ++i)
+    if (host_block_ids[i] < 0 || host_block_ids[i] >= p->num_blocks) return KVATTN_ERR_INVALID_ARG;
+  for (int l = 0; l < p->layers; ++l)
+    if (p->h_len[(size_t)l * p->slots + slot] > n_blocks * p->block_size) return KVATTN_ERR_CAPACITY;
+  int rc = paged_check_device(p);
+  if (rc) return rc;
+  if (n_blocks > 0) {
+    hipError_t e = launch_set_lengths(p->d_table + (size_t)slot * p->max_blocks, 1, n_blocks, host_block_ids,
+                                      (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "block table upload");
+  }
+  p->h_nblk[slot] = n_blocks;
+  return KVATTN_OK;
+}
+
+int kvattn_paged_set_lengths(kvattn_paged *p, int layer, const int32_t *host_lens, void *stream) {
+  if (!p || !host_lens) return KVATTN_ERR_INVALID_ARG;
+  if (layer != -1 && (layer < 0 || layer >= p->layers)) return KVATTN_ERR_INVALID_ARG;
+  for (int s = 0; s < p->slots; ++s)
+    if (host_lens[s] < 0 || host_lens[s] > paged_capacity(p, s)) return KVATTN_ERR_CAPACITY;
+  int rc = paged_check_device(p);
+  if (rc) return rc;
+  const int first = layer < 0 ? 0 : layer;
+  const int count = layer < 0 ? p->layers : 1;
+  hipError_t e = launch_set_lengths(p->d_len + (size_t)first * p->slots, count, p->slots, host_lens,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "set_lengths launch");
+  for (int l = first; l < first + count; ++l)
+    std::memcpy(&p->h_len[(size_t)l * p->slots], host_lens, sizeof(int32_t) * p->slots);
+  return KVATTN_OK;
+}
+
+int kvattn_paged_get_lengths(const kvattn_paged *p, int layer, int32_t *host_lens) {
+  int rc = paged_check_layer(p, layer);
+  if (rc) return rc;
+  if (!host_lens) return KVATTN_ERR_INVALID_ARG;
+  std::memcpy(host_lens, &p->h_len[(size_t)layer * p->slots], sizeof(int32_t) * p->slots);
+  return KVATTN_OK;
+}
+
+int kvattn_paged_prefill(kvattn_paged *p, int layer, const void *q, const void *k, const void *v, void *o,
+                         int T, float scale, kvattn_dtype o_dtype, void *stream) {
+  int rc = paged_check_layer(p, layer);
+  if (rc) return rc;
+  if (!q || !k || !v || !o) return KVATTN_ERR_INVALID_ARG;
+  if (T <= 0 || !(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
+  if (o_dtype != p->dt && o_dtype != KVATTN_F32) return KVATTN_ERR_UNSUPPORTED;
+  const int32_t *hl = &p->h_len[(size_t)layer * p->slots];
+  for (int s = 0; s < p->slots; ++s)
+    if (hl[s] != 0) return KVATTN_ERR_STATE;
+  for (int s = 0; s < p->slots; ++s)
+    if (T > paged_capacity(p, s)) return KVATTN_ERR_CAPACITY;
+  rc = paged_check_device(p);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t *len = p->d_len + (size_t)layer * p->slots;
+
+  // 1. causal attention over the prompt (the prefill kernels, cache copy off)
+  PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.cache_k = paged_k(p, layer);
+  a.cache_v = paged_v(p, layer);
+  a.len = len;
+  a.offsets = nullptr;
+  a.batch = p->slots;
+  a.q_heads = p->q_heads;
+  a.kv_heads = p->kv_heads;
+  a.head_dim = p->head_dim;
+  a.T = T;
+  a.max_T = T;
+  a.kv_rows = T;
+  a.write_cache = 0;
+  a.window = 0;
+  a.sink = 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dt = p->dt;
+  a.o_dt = o_dtype;
+  hipError_t e = launch_prefill(a, st);
+  if (e != hipSuccess) return hip_fail(e, "paged prefill attention launch");
+
+  // 2. the prompt rows to their blocks; len = T
+  PagedWriteArgs w;
+  w.k_pool = paged_k(p, layer);
+  w.v_pool = paged_v(p, layer);
+  w.k_new = (const char *)k;
+  w.v_new = (const char *)v;
+  w.len = len;
+  w.table = p->d_table;
+  w.batch = p->slots;
+  w.kv_heads = p->kv_heads;
+  w.T = T;
+  w.row_bytes = p->head_dim * p->elem;
+  w.block_log2 = p->block_log2;
+  w.max_blocks = p->max_blocks;
+  e = launch_paged_write(w, st);
+  if (e != hipSuccess) return hip_fail(e, "paged prefill write launch");
+  for (int s = 0; s < p->slots; ++s) p->h_len[(size_t)layer * p->slots + s] = T;
+  return KVATTN_OK;
+}
+
+int kvattn_paged_append(kvattn_paged *p, int layer, const void *k_new, const void *v_new, void *stream) {
+  int rc = paged_check_layer(p, layer);
+  if (rc) return rc;
+  if (!k_new || !v_new) return KVATTN_ERR_INVALID_ARG;
+  int32_t *hl = &p->h_len[(size_t)layer * p->slots];
+  for (int s = 0; s < p->slots; ++s)
+    if (hl[s] >= paged_capacity(p, s)) return KVATTN_ERR_CAPACITY;
+  rc = paged_check_device(p);
+  if (rc) return rc;
+  AppendArgs a;
+  a.k_layer = paged_k(p, layer);
+  a.v_layer = paged_v(p, layer);
+  a.k_new = (const char *)k_new;
+  a.v_new = (const char *)v_new;
+  a.len = p->d_len + (size_t)layer * p->slots;
+  a.batch = p->slots;
+  a.kv_heads = p->kv_heads;
+  a.max_T = 0;
+  a.row_bytes = p->head_dim * p->elem;
+  a.table = p->d_table;
+  a.block_log2 = p->block_log2;
+  a.max_blocks = p->max_blocks;
+  hipError_t e = launch_append(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "paged append launch");
+  for (int s = 0; s < p->slots; ++s) hl[s] += 1;
+  return KVATTN_OK;
+}
+
+int kvattn_paged_decode(kvattn_paged *p, int layer, const void *q, void *o, float scale, kvattn_dtype o_dtype,
+                        void *stream) {
+  int rc = paged_check_layer(p, layer);
+  if (rc) return rc;
+  if (!q || !o) return KVATTN_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
+  if (o_dtype != p->dt && o_dtype != KVATTN_F32) return KVATTN_ERR_UNSUPPORTED;
+  const int32_t *hl = &p->h_len[(size_t)layer * p->slots];
+  for (int s = 0; s < p->slots; ++s)
+    if (hl[s] <= 0) return KVATTN_ERR_STATE;
+  rc = paged_check_device(p);
+  if (rc) return rc;
+  DecodeArgs a;
+  a.k_layer = paged_k(p, layer);
+  a.v_layer = paged_v(p, layer);
+  a.q = q;
+  a.o = o;
+  a.ws = p->d_ws;
+  a.len = p->d_len + (size_t)layer * p->slots;
+  a.batch = p->slots;
+  a.q_heads = p->q_heads;
+  a.kv_heads = p->kv_heads;
+  a.head_dim = p->head_dim;
+  a.max_T = p->max_blocks * p->block_size;
+  a.chunk = p->chunk;
+  a.n_splits = p->n_splits;
+  a.window = 0;
+  a.sink = 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dt = p->dt;
+  a.o_dt = o_dtype;
+  a.table = p->d_table;
+  a.block_log2 = p->block_log2;
+  a.max_blocks = p->max_blocks;
+  hipError_t e = launch_decode(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "paged decode launch");
   return KVATTN_OK;
 }
 

@@ -481,7 +481,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
   T *ckb = (T *)a.cache_k + (size_t)(b * a.kv_heads + g) * a.max_T * D;
   T *cvb = (T *)a.cache_v + (size_t)(b * a.kv_heads + g) * a.max_T * D;
 
-  if (qt == 0 && h == 0 && tid == 0) a.len[b] = Tn;
+  // the cache copy of the prompt rows (skipped when another kernel places them)
+  const bool writer_c = writer && a.write_cache;
+  if (a.write_cache && qt == 0 && h == 0 && tid == 0) a.len[b] = Tn;
 
   vec8 qf[NT][KS];
 #pragma unroll
@@ -541,7 +543,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
         const int idx = c * 256 + stid;
         *(u32x4 *)(Ks + (idx / (D / 8)) * LDS::KSTR + (idx % (D / 8)) * 8) = kreg[c];
       }
-      if (writer && t * BN + BN > q0) {  // workgroup-uniform
+      if (writer_c && t * BN + BN > q0) {  // workgroup-uniform
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
           const int idx = c * 256 + stid;
@@ -569,7 +571,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
         }
         *(u32x2 *)(Vt + (v_ds * 8 + e) * LDS::VSTR + 4 * v_kg) = out;
       }
-      if (writer && t * BN + BN > q0) {
+      if (writer_c && t * BN + BN > q0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = t * BN + 4 * v_kg + r;

@@ -38,6 +38,24 @@ def test_binding_signatures_cover_header():
     assert set(declared_functions()) == set(kv._SIGS)
 
 
+def declared_arity():
+    """Parameter count of every declared function, from the headers' text."""
+    arity = {}
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for name, params in re.findall(r"\b(kvattn_\w+)\s*\(([^;{]*?)\)\s*;", text, flags=re.S):
+            params = params.strip()
+            arity[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return arity
+
+
+def test_binding_argument_counts_match_header():
+    arity = declared_arity()
+    assert set(arity) == set(declared_functions())
+    wrong = {n: (len(kv._SIGS[n][1]), a) for n, a in arity.items() if len(kv._SIGS[n][1]) != a}
+    assert not wrong, wrong
+
+
 def test_cache_bytes_matches_worked_example():
     with open(os.path.join(ROOT, "tests", "golden", "kv_bytes_worked_example.json")) as f:
         gold = json.load(f)
@@ -120,3 +138,46 @@ def test_window_calls_reject_null_cache_without_a_device():
     assert lib.kvattn_cache_set_window(None, -1, 0, 0) == -1
     w, s = ctypes.c_int(), ctypes.c_int()
     assert lib.kvattn_cache_get_window(None, 0, ctypes.byref(w), ctypes.byref(s)) == -1
+
+
+def test_paged_bytes_is_the_capacity_formula():
+    lib = kv.lib()
+    # 32 layers, 512 blocks of 64 positions (= one 32768-position sequence), 8 KV heads, D=128, bf16
+    assert lib.kvattn_paged_bytes(32, 512, 64, 8, 128, 2) == 2 * 32 * 8 * 128 * 32768 * 2
+    assert lib.kvattn_paged_bytes(32, 512, 64, 8, 128, 2) == lib.kvattn_cache_bytes(32, 1, 8, 128, 32768, 2)
+    assert lib.kvattn_paged_bytes(0, 512, 64, 8, 128, 2) == 0
+    assert lib.kvattn_paged_bytes(1, 512, 64, 8, 128, 7) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 2, 4, 8, 16, 4, 4, 64, 1), 0),          # valid shape (not allocated: null out)
+    ((1, 2, 4, 8, 24, 4, 4, 64, 1), -2),         # block size not a power of two
+    ((1, 2, 4, 8, 8, 4, 4, 64, 1), -2),          # block size below 16
+    ((1, 2, 4, 8, 16, 4, 4, 48, 1), -2),         # head dim
+    ((1, 2, 4, 8, 16, 6, 4, 64, 1), -2),         # H % Hkv
+    ((0, 2, 4, 8, 16, 4, 4, 64, 1), -1),
+    ((1, 2, 0, 8, 16, 4, 4, 64, 1), -1),
+])
+def test_paged_alloc_validation_before_any_device_call(args, status):
+    lib = kv.lib()
+    if status == 0:
+        # a null out pointer is rejected first, so nothing touches the device
+        assert lib.kvattn_paged_alloc(None, *args, None, 0) == -1
+    else:
+        out = ctypes.c_void_p()
+        assert lib.kvattn_paged_alloc(ctypes.byref(out), *args, None, 0) == status
+        assert not out.value
+
+
+def test_paged_calls_reject_null_object_without_a_device():
+    lib = kv.lib()
+    p = ctypes.c_void_p(0)
+    assert lib.kvattn_paged_free(None) == -1
+    assert lib.kvattn_paged_prefill(None, 0, p, p, p, p, 8, 0.1, 1, None) == -1
+    assert lib.kvattn_paged_append(None, 0, p, p, None) == -1
+    assert lib.kvattn_paged_decode(None, 0, p, p, 0.1, 1, None) == -1
+    assert lib.kvattn_paged_set_blocks(None, 0, (ctypes.c_int32 * 1)(0), 1, None) == -1
+    assert lib.kvattn_paged_set_lengths(None, 0, (ctypes.c_int32 * 1)(0), None) == -1
+    assert lib.kvattn_paged_get_lengths(None, 0, (ctypes.c_int32 * 1)()) == -1
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.kvattn_paged_kv_ptr(None, 0, ctypes.byref(k), ctypes.byref(v)) == -1
