@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--skip-gqa", action="store_true")
     p.add_argument("--only", choices=["prefill", "decode", "gqa"], default=None,
                    help="time one phase only (for profiling runs)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the windowed, paged and extend measurements (profiling runs: their launches "
+                        "share kernel names with the headline ones)")
     p.add_argument("--calibrate", action="store_true",
                    help="also run a plain 4 GiB read and a 4 GiB fill, whose FETCH_SIZE / WRITE_SIZE counter "
                         "readings calibrate the counters (for the --pmc runs that produce profiles/traffic.json)")
@@ -79,8 +82,10 @@ PREFILL_SOURCES = ["prefill.hip", "common.hpp"]
 CALIB_BYTES = 4 << 30
 # kernels of each measured launch, by a substring of the demangled or mangled name
 TRAFFIC_KERNELS = {
-    "decode_ragged_b32": (DECODE_SOURCES, ["decode_kernel<kvattn::TagF16, 128, 1,", "decode_merge_kernel<128, 1>"]),
-    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4,", "decode_merge_kernel<128, 4>"]),
+    "decode_ragged_b32": (DECODE_SOURCES, ["decode_kernel<kvattn::TagF16, 128, 1, 6, 1, 4, false>",
+                                           "decode_merge_kernel<128, 1>"]),
+    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4, 4, 1, 4, false>",
+                                        "decode_merge_kernel<128, 4>"]),
     "prefill_t8192": (PREFILL_SOURCES, ["prefill_pipe_kernelIDF16_Li128"]),
 }
 
@@ -601,12 +606,12 @@ def main():
                      "prefill_batch": 1, "prefill_T": w5.extra_prefill_T, "dtype": "f16"}
     out["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                      "cus": props.multi_processor_count}
-    if dec is not None:
+    if dec is not None and not args.no_extras:
         log("decode under a sliding window")
         out["decode_window"] = window_measurements(kv, w5, dec, out["roofline"]["mean_launch_ms"] * 1e3)
         log("decode from a paged cache")
         out["decode_paged"] = paged_measurements(kv, w5, dec, out["roofline"]["mean_launch_ms"] * 1e3)
-    if dec is not None and pre is not None:
+    if dec is not None and pre is not None and not args.no_extras:
         log("extend: chunked prefill and 4-token verification")
         out["extend"] = extend_measurements(kv, w5, dec, pre)
     # free the big caches before the GQA workload
