@@ -16,3 +16,4 @@ from .attention import (  # noqa: F401
     visible,
     visible_keys,
 )
+from . import model  # noqa: F401,E402

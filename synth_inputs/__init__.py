@@ -229,3 +229,73 @@ def decode_step_inputs(w: Workload, layer: int, step: int, contexts=None):
             L = int(contexts[b])
             k[b] = _apply_heavy(w, k[b], layer, 0, b, L, L - 1)
     return q, k, v
+
+
+# --------------------------------------------------------------------------
+# random-weight decoder (the README's minimal decoder-only model: 8 layers,
+# 512 wide, 16 heads, vocabulary 4096)
+# --------------------------------------------------------------------------
+MODEL_CFG = 6  # config id of the model's seed streams
+W_TOK, W_POS, W_LN1, W_QKV, W_O, W_LN2, W_UP, W_DOWN, W_LNF, W_HEAD, W_TOKENS = range(11)
+
+
+@dataclass(frozen=True)
+class ModelSpec:
+    layers: int = 8
+    d_model: int = 512
+    heads: int = 16
+    vocab: int = 4096
+    max_T: int = 4224      # prompt 4096 + 128 generated tokens
+    mlp_mult: int = 4
+
+    @property
+    def head_dim(self) -> int:
+        return self.d_model // self.heads
+
+    @property
+    def d_mlp(self) -> int:
+        return self.mlp_mult * self.d_model
+
+
+TINYGPT = ModelSpec()
+
+
+def model_weight_shapes(s: ModelSpec):
+    """(name, shape) of every weight in packing order: token and position
+    embeddings, then per layer norm-1 gain, fused QKV (3d x d, rows q | k | v,
+    head-major inside each), output projection (d x d), norm-2 gain, MLP up
+    (4d x d) and down (d x 4d), then the final norm gain and the LM head
+    (vocab x d).  Matrices are (out, in), row-major."""
+    d = s.d_model
+    out = [("tok_emb", (s.vocab, d)), ("pos_emb", (s.max_T, d))]
+    for l in range(s.layers):
+        out += [(f"ln1.{l}", (d,)), (f"wqkv.{l}", (3 * d, d)), (f"wo.{l}", (d, d)),
+                (f"ln2.{l}", (d,)), (f"w_up.{l}", (s.d_mlp, d)), (f"w_down.{l}", (d, s.d_mlp))]
+    out += [("ln_f", (d,)), ("lm_head", (s.vocab, d))]
+    return out
+
+
+def model_weights(s: ModelSpec, dtype: str = "f16", seed: int = 0) -> dict:
+    """Random weights: matrices and embeddings N(0, 0.02^2), norm gains 1 + N(0, 0.1^2),
+    rounded to ``dtype``.  Seeded per tensor (``seed`` selects an independent model)."""
+    ids = {"tok_emb": W_TOK, "pos_emb": W_POS, "ln1": W_LN1, "wqkv": W_QKV, "wo": W_O, "ln2": W_LN2,
+           "w_up": W_UP, "w_down": W_DOWN, "ln_f": W_LNF, "lm_head": W_HEAD}
+    w = {}
+    for name, shape in model_weight_shapes(s):
+        base, _, layer = name.partition(".")
+        g = generator(MODEL_CFG, int(layer or 0), -1, ids[base], seed)
+        x = g.standard_normal(shape)
+        x = 1.0 + 0.1 * x if base.startswith("ln") else 0.02 * x
+        w[name] = round_to(x, dtype)
+    return w
+
+
+def pack_model_weights(s: ModelSpec, w: dict) -> np.ndarray:
+    """All weights concatenated in packing order (one flat array)."""
+    return np.concatenate([np.ascontiguousarray(w[name]).reshape(-1) for name, _ in model_weight_shapes(s)])
+
+
+def model_tokens(s: ModelSpec, batch: int, T: int, seed: int = 0) -> np.ndarray:
+    """Seeded prompt token ids (batch, T), uniform over the vocabulary."""
+    g = generator(MODEL_CFG, 0, -1, W_TOKENS, seed)
+    return g.integers(0, s.vocab, size=(batch, T)).astype(np.int32)
