@@ -435,6 +435,48 @@ def paged_measurements(kv, w, dec, full_us, block_size=64, layers=4, reps=5):
     return out
 
 
+def decoder_measurements(kv, dev, prompt=4096, new_tokens=128):
+    """The README's 8-layer, 512-wide, 16-head decoder (vocabulary 4096) with random
+    weights: prompt of `prompt` tokens, then `new_tokens` greedy tokens, batch 1 (the
+    README's KV-cache table) and batch 8.  The step is replayed from a HIP graph."""
+    spec = si.TINYGPT
+    flat = torch.from_numpy(si.pack_model_weights(spec, si.model_weights(spec))).to(dev)
+    out = {"workload": f"{spec.layers}L x {spec.d_model}d, {spec.heads} heads, vocab {spec.vocab}, fp16 weights; "
+                       f"prompt {prompt}, +{new_tokens} greedy tokens",
+           "context": "llm-perf-lab README: 41.2 tok/s with KV cache after a 4096-token prompt "
+                      "(RTX 3090, PyTorch eager, 128 new tokens)"}
+    for batch in (1, 8):
+        m = kv.Decoder(spec.layers, spec.d_model, spec.heads, spec.vocab, spec.max_T, spec.mlp_mult, batch, flat)
+        tokens = torch.from_numpy(si.model_tokens(spec, batch, prompt)).to(dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for rep in range(2):  # the first pass captures the step graph and warms rocBLAS
+            m.reset()
+            ev[0].record()
+            _, nxt = m.prefill(tokens)
+            ev[1].record()
+            m.generate(new_tokens, nxt)
+            ev[2].record()
+            torch.cuda.synchronize()
+        pre_ms, dec_ms = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+        m.reset()
+        _, nxt = m.prefill(tokens)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(32):
+            _, nxt = m.step(nxt)
+        b.record()
+        torch.cuda.synchronize()
+        eager_ms = a.elapsed_time(b) / 32
+        out[f"batch{batch}"] = {
+            "prefill_ms": round(pre_ms, 3), "decode_ms_per_token": round(dec_ms / new_tokens, 4),
+            "decode_tok_s": round(batch * new_tokens / (dec_ms * 1e-3), 1),
+            "end_to_end_tok_s": round(batch * new_tokens / ((pre_ms + dec_ms) * 1e-3), 1),
+            "eager_step_ms": round(eager_ms, 4)}
+        m.close()
+    return out
+
+
 def timed(fn, steps, warmup):
     for _ in range(warmup):
         fn(None)
@@ -638,6 +680,9 @@ def main():
         if args.only == "gqa":
             out["value"], out["unit"] = out["decode_gqa"]["value"], "GB/s"
 
+    if args.only is None and not args.no_extras:
+        log("random-weight decoder: prompt 4096 + 128 greedy tokens")
+        out["decoder"] = decoder_measurements(kv, dev)
     if args.only is None:
         ceil = measure_read_ceiling(kv, dev)
         out["hbm_read_ceiling"] = {"value": round(ceil, 1), "unit": "GB/s", "kernel": "kvattn_measure_stream_read",

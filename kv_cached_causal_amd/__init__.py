@@ -17,7 +17,7 @@ import os
 
 import torch
 
-__all__ = ["KVCache", "PagedKVCache", "KVAttnError", "cache_bytes", "paged_bytes", "lib", "LIB_PATH"]
+__all__ = ["KVCache", "PagedKVCache", "Decoder", "KVAttnError", "cache_bytes", "paged_bytes", "lib", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # KVATTN_LIB names another build of the library (for example a tuning variant)
@@ -69,6 +69,16 @@ _SIGS = {
                                            ctypes.c_void_p]),
     "kvattn_paged_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "kvattn_model_weight_elems": (ctypes.c_size_t, [ctypes.c_int] * 5),
+    "kvattn_model_create": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p)] + [ctypes.c_int] * 7 + [ctypes.c_void_p]),
+    "kvattn_model_free": (ctypes.c_int, [ctypes.c_void_p]),
+    "kvattn_model_reset": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "kvattn_model_positions": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
+    "kvattn_model_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]),
+    "kvattn_model_step": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 4),
+    "kvattn_model_generate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 3),
+    "kvattn_model_last_error": (ctypes.c_char_p, []),
     "kvattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvattn_measure_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                                   ctypes.c_void_p]),
@@ -468,3 +478,79 @@ class PagedKVCache:
 
     def __exit__(self, *exc):
         self.close()
+
+
+class Decoder:
+    """The random-weight decoder of kvattn_model.h on one GPU: packed fp16
+    weights (a flat device tensor the caller keeps alive), ``batch`` sequences
+    of up to ``max_T`` positions, greedy decoding."""
+
+    def __init__(self, layers: int, d_model: int, heads: int, vocab: int, max_T: int, mlp_mult: int, batch: int,
+                 weights: torch.Tensor):
+        self.device = weights.device
+        self.layers, self.d_model, self.heads, self.vocab = layers, d_model, heads, vocab
+        self.max_T, self.mlp_mult, self.batch = max_T, mlp_mult, batch
+        need = int(lib().kvattn_model_weight_elems(layers, d_model, vocab, max_T, mlp_mult))
+        if weights.dtype != torch.float16 or weights.numel() != need or not weights.is_contiguous():
+            raise ValueError(f"weights must be a contiguous fp16 tensor of {need} elements")
+        self._weights = weights
+        self._handle = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_model_create(ctypes.byref(self._handle), layers, d_model, heads, vocab, max_T,
+                                             mlp_mult, batch, _ptr(weights)), "kvattn_model_create")
+
+    def _ints(self, t: torch.Tensor, shape, name):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.device != self.device:
+            raise TypeError(f"{name} must be an int32 tensor on {self.device}")
+        if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with shape {tuple(shape)}")
+
+    def prefill(self, tokens: torch.Tensor):
+        """Prompt (batch, T) int32 -> (logits of the last position (batch, vocab) fp32, greedy next (batch,))."""
+        T = tokens.shape[1] if tokens.dim() == 2 else -1
+        self._ints(tokens, (self.batch, T), "tokens")
+        logits = torch.empty((self.batch, self.vocab), dtype=torch.float32, device=self.device)
+        nxt = torch.empty((self.batch,), dtype=torch.int32, device=self.device)
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_model_prefill(self._handle, _ptr(tokens), T, _ptr(logits), _ptr(nxt),
+                                              _stream_ptr(self.device)), "kvattn_model_prefill")
+        return logits, nxt
+
+    def step(self, tokens: torch.Tensor):
+        """Feed tokens (batch,) int32 at the current positions -> (logits, greedy next)."""
+        self._ints(tokens, (self.batch,), "tokens")
+        logits = torch.empty((self.batch, self.vocab), dtype=torch.float32, device=self.device)
+        nxt = torch.empty((self.batch,), dtype=torch.int32, device=self.device)
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_model_step(self._handle, _ptr(tokens), _ptr(logits), _ptr(nxt),
+                                           _stream_ptr(self.device)), "kvattn_model_step")
+        return logits, nxt
+
+    def generate(self, n_steps: int, tokens: torch.Tensor) -> torch.Tensor:
+        """Greedy: n_steps tokens per sequence from the current tokens (updated in place) -> (n_steps, batch)."""
+        self._ints(tokens, (self.batch,), "tokens")
+        out = torch.empty((n_steps, self.batch), dtype=torch.int32, device=self.device)
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_model_generate(self._handle, n_steps, _ptr(tokens), _ptr(out),
+                                               _stream_ptr(self.device)), "kvattn_model_generate")
+        return out
+
+    def positions(self) -> list:
+        arr = (ctypes.c_int32 * self.batch)()
+        _check(lib().kvattn_model_positions(self._handle, arr), "kvattn_model_positions")
+        return list(arr)
+
+    def reset(self) -> None:
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_model_reset(self._handle, _stream_ptr(self.device)), "kvattn_model_reset")
+
+    def close(self) -> None:
+        if self._handle and self._handle.value:
+            _check(lib().kvattn_model_free(self._handle), "kvattn_model_free")
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -13,26 +13,12 @@
 #include <new>
 #include <vector>
 
+#include "cache.hpp"
 #include "common.hpp"
 #include "kvattn.h"
 
 using namespace kvattn;
 
-struct kvattn_cache {
-  int layers, batch, q_heads, kv_heads, head_dim, max_T;
-  kvattn_dtype dt;
-  int elem;               // bytes per element
-  size_t payload_bytes;   // = kvattn_cache_bytes(...)
-  size_t layer_bytes;     // K block + V block of one layer
-  char *base;             // payload (device)
-  bool owns_base;
-  int32_t *d_len;         // [layers][batch] (device)
-  std::vector<int32_t> h_len;  // host mirror
-  std::vector<int> window, sink;  // per layer: sliding window (0: none), sink positions
-  float *d_ws;            // decode split-K workspace (device)
-  int chunk, n_splits;
-  int device;
-};
 
 namespace {
 

@@ -1,0 +1,729 @@
+// A random-weight decoder around the attention path (the llm-perf-lab
+// README's minimal decoder-only Transformer: RMSNorm, GELU MLP, incremental
+// decoding), driven end to end on one GPU.
+//
+// Decode step (batch <= 8): the projections are matrix-vector products bound
+// by reading the weights, so they are hand-written streaming kernels (no
+// matrix cores): each wave owns output rows and reads them with 16-byte
+// loads, the RMSNorm of the input is folded into the kernel's prologue, and
+// the GELU or the residual add into its epilogue.  The attention is the
+// library's own append and decode kernels.  A HIP graph of the whole step
+// removes the per-kernel launch cost when tokens are generated in a loop.
+//
+// Prompt: the projections are plain GEMMs (rocBLAS, fp16 inputs, fp32
+// accumulation; the residual stream stays fp32 through beta = 1 updates); the
+// attention is the library's prefill kernel, which also fills the cache.
+#include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "cache.hpp"
+#include "common.hpp"
+#include "kvattn_model.h"
+
+using namespace kvattn;
+
+namespace kvattn {
+namespace {
+
+constexpr int kMaxBatch = 8;
+constexpr float kEps = 1e-5f;
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ float gelu_exact(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
+
+// x[r] = tok_emb[tokens[r]] + pos_emb[position]: grid (T, B), rows r = b * T + t.
+// With `pos` (decode) the position of sequence b is pos[b]; else it is t.
+// Token ids outside [0, vocab) are clamped into it (never an address outside
+// the table).
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t *tokens, const int32_t *pos, const half_t *tok_emb,
+                                                    const half_t *pos_emb, float *x, int T, int d, int vocab) {
+  const int t = blockIdx.x, b = blockIdx.y;
+  const size_t r = (size_t)b * T + t;
+  const int p = pos ? pos[b] : t;
+  const int id = min(max(tokens[r], 0), vocab - 1);
+  const half_t *te = tok_emb + (size_t)id * d;
+  const half_t *pe = pos_emb + (size_t)p * d;
+  for (int i = threadIdx.x; i < d; i += 256) x[r * d + i] = (float)te[i] + (float)pe[i];
+}
+
+enum Epilogue { EPI_QKV = 0, EPI_RESIDUAL = 1, EPI_GELU = 2, EPI_STORE = 3 };
+
+struct GemvArgs {
+  const half_t *W;     // (N, K) row-major
+  const float *in;     // (B, K): the residual stream (normalised first when gain != null) or a hidden vector
+  const half_t *gain;  // RMSNorm gain (K) or null
+  float *out;          // EPI_RESIDUAL: out += W in; EPI_GELU / EPI_STORE: out = ... ; (B, N)
+  half_t *q, *k, *v;   // EPI_QKV: rows [0, d) -> q (B, d), [d, 2d) -> k, [2d, 3d) -> v
+  int B, N, K, d;
+};
+
+// y[b][n] = sum_k W[n][k] * h[b][k], h = in (or rmsnorm(in) * gain).  4 waves
+// per workgroup, RPW rows per wave; lane l holds columns c * 512 + 8 l .. +8
+// of each 512-column chunk c.  The weight loads are issued first; the
+// normalised input sits in LDS (B * K floats, K <= 1024 when normalised).
+template <int EPI, bool NORM, int KC>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+  constexpr int RPW = 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row0 = (blockIdx.x * 4 + wave) * RPW;
+  const int K = a.K;
+  u32x4 w[RPW][KC];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int n = min(row0 + r, a.N - 1);  // clamped: rows past N are never stored
+#pragma unroll
+    for (int c = 0; c < KC; ++c) w[r][c] = *(const u32x4 *)(a.W + (size_t)n * K + c * 512 + lane * 8);
+  }
+  __shared__ float s_in[NORM ? kMaxBatch * 1024 : 1];
+  __shared__ float s_inv[kMaxBatch];
+  if constexpr (NORM) {
+    for (int i = tid; i < a.B * K; i += 256) s_in[i] = a.in[i];
+    __syncthreads();
+    for (int b = wave; b < a.B; b += 4) {
+      float ss = 0.f;
+      for (int i = lane; i < K; i += 64) ss += s_in[b * K + i] * s_in[b * K + i];
+      ss = wave_sum(ss);
+      if (lane == 0) s_inv[b] = 1.0f / sqrtf(ss / (float)K + kEps);
+    }
+    __syncthreads();
+    for (int i = tid; i < a.B * K; i += 256) {
+      const int b = i / K;
+      s_in[i] *= s_inv[b] * (float)a.gain[i - b * K];
+    }
+    __syncthreads();
+  }
+  for (int b = 0; b < a.B; ++b) {
+    float acc[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const int k0 = c * 512 + lane * 8;
+      float h[8];
+      if constexpr (NORM) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = s_in[b * K + k0 + e];
+      } else {
+        const float4 h0 = *(const float4 *)(a.in + (size_t)b * K + k0);
+        const float4 h1 = *(const float4 *)(a.in + (size_t)b * K + k0 + 4);
+        h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w;
+        h[4] = h1.x; h[5] = h1.y; h[6] = h1.z; h[7] = h1.w;
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const half8_t wv = __builtin_bit_cast(half8_t, w[r][c]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r] = fmaf((float)wv[e], h[e], acc[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const float y = wave_sum(acc[r]);
+      const int n = row0 + r;
+      if (lane != 0 || n >= a.N) continue;
+      if constexpr (EPI == EPI_QKV) {
+        const int seg = n / a.d, j = n - seg * a.d;
+        half_t *dst = seg == 0 ? a.q : (seg == 1 ? a.k : a.v);
+        dst[(size_t)b * a.d + j] = (half_t)y;
+      } else if constexpr (EPI == EPI_RESIDUAL) {
+        a.out[(size_t)b * a.N + n] += y;
+      } else if constexpr (EPI == EPI_GELU) {
+        a.out[(size_t)b * a.N + n] = gelu_exact(y);
+      } else {
+        a.out[(size_t)b * a.N + n] = y;
+      }
+    }
+  }
+}
+
+// Greedy choice per sequence (lowest index among equal maxima): one
+// workgroup for the whole batch.  With `out`, also writes the token to
+// out[step * B + b] and advances the device step counter.
+__global__ __launch_bounds__(256) void argmax_kernel(const float *logits, int B, int V, int32_t *next, int32_t *out,
+                                                     int32_t *step) {
+  __shared__ float s_v[4];
+  __shared__ int s_i[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int b = 0; b < B; ++b) {
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int i = tid; i < V; i += 256) {
+      const float x = logits[(size_t)b * V + i];
+      if (x > best) {  // i increases per thread, so the first maximum is kept
+        best = x;
+        bi = i;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(best, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ov > best || (ov == best && oi < bi)) {
+        best = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) {
+      s_v[wave] = best;
+      s_i[wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < 4; ++w)
+        if (s_v[w] > best || (s_v[w] == best && s_i[w] < bi)) {
+          best = s_v[w];
+          bi = s_i[w];
+        }
+      if (bi >= V) bi = 0;  // no comparable value (all NaN): token 0
+      next[b] = bi;
+      if (out) out[(size_t)(*step) * B + b] = bi;
+    }
+    __syncthreads();
+  }
+  if (out && tid == 0) *step += 1;
+}
+
+__global__ void set_int_kernel(int32_t *p, int v) { *p = v; }
+
+// RMSNorm of R rows of x (fp32) into fp16: grid R.
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *x, const half_t *gain, half_t *out, int d) {
+  __shared__ float s_part[4];
+  const size_t r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float ss = 0.f;
+  for (int i = tid; i < d; i += 256) ss += x[r * d + i] * x[r * d + i];
+  ss = wave_sum(ss);
+  if (lane == 0) s_part[wave] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf((s_part[0] + s_part[1] + s_part[2] + s_part[3]) / (float)d + kEps);
+  for (int i = tid; i < d; i += 256) out[r * d + i] = (half_t)(x[r * d + i] * inv * (float)gain[i]);
+}
+
+// (B*T, 3d) fused projection rows -> q, k, v (B, H, T, D): grid (B*T, ceil(3d / 256)).
+__global__ __launch_bounds__(256) void split_qkv_kernel(const half_t *qkv, half_t *q, half_t *k, half_t *v, int T,
+                                                        int H, int D) {
+  const int d = H * D;
+  const int j = blockIdx.y * 256 + threadIdx.x;
+  if (j >= 3 * d) return;
+  const size_t r = blockIdx.x;
+  const int b = (int)(r / T), t = (int)(r - (size_t)b * T);
+  const int seg = j / d, rem = j - seg * d, h = rem / D, e = rem - h * D;
+  half_t *dst = seg == 0 ? q : (seg == 1 ? k : v);
+  dst[(((size_t)b * H + h) * T + t) * D + e] = qkv[r * 3 * d + j];
+}
+
+// o (B, H, T, D) -> rows (B*T, d): grid (B*T, ceil(d / 256)).
+__global__ __launch_bounds__(256) void merge_heads_kernel(const half_t *o, half_t *flat, int T, int H, int D) {
+  const int d = H * D;
+  const int j = blockIdx.y * 256 + threadIdx.x;
+  if (j >= d) return;
+  const size_t r = blockIdx.x;
+  const int b = (int)(r / T), t = (int)(r - (size_t)b * T);
+  const int h = j / D, e = j - h * D;
+  flat[r * d + j] = o[(((size_t)b * H + h) * T + t) * D + e];
+}
+
+__global__ __launch_bounds__(256) void gelu_half_kernel(half_t *x, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) x[i] = (half_t)gelu_exact((float)x[i]);
+}
+
+// the last prompt position of every sequence: rows b * T + T - 1 -> (B, d)
+__global__ __launch_bounds__(256) void gather_last_kernel(const float *x, float *out, int T, int d) {
+  const int b = blockIdx.x;
+  for (int i = threadIdx.x; i < d; i += 256) out[(size_t)b * d + i] = x[((size_t)b * T + T - 1) * d + i];
+}
+
+}  // namespace
+}  // namespace kvattn
+
+struct kvattn_model {
+  int layers, d, heads, D, vocab, max_T, mlp, batch;
+  const half_t *tok_emb, *pos_emb, *ln_f, *lm_head;
+  std::vector<const half_t *> ln1, wqkv, wo, ln2, wup, wdown;
+  kvattn_cache *cache;
+  // decode-step buffers (device)
+  float *x, *att, *hid, *logits;
+  half_t *q, *k, *v;
+  int32_t *tok, *gen_out, *step_ctr;
+  // prompt buffers (device), sized for prompt_rows rows
+  size_t prompt_rows;
+  float *px;
+  half_t *ph, *pqkv, *pq, *pk, *pv, *po, *pflat, *pup;
+  rocblas_handle blas;
+  hipStream_t gs;
+  hipGraphExec_t graph;
+  hipEvent_t ev_in, ev_out;
+  int device;
+};
+
+namespace {
+
+thread_local char g_model_error[256] = "";
+
+int model_hip_fail(hipError_t e, const char *where) {
+  std::snprintf(g_model_error, sizeof g_model_error, "%s: %s", where, hipGetErrorString(e));
+  std::fprintf(stderr, "kvattn_model: %s\n", g_model_error);
+  return KVATTN_ERR_HIP;
+}
+
+hipError_t launch_gemv(int epi, bool norm, const GemvArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.N + 7) / 8));
+  const int kc = a.K / 512;
+#define KVATTN_GEMV(E, NRM, KCV) gemv_kernel<E, NRM, KCV><<<grid, 256, 0, s>>>(a)
+  if (norm) {
+    if (epi == EPI_QKV && kc == 1) KVATTN_GEMV(EPI_QKV, true, 1);
+    else if (epi == EPI_QKV && kc == 2) KVATTN_GEMV(EPI_QKV, true, 2);
+    else if (epi == EPI_GELU && kc == 1) KVATTN_GEMV(EPI_GELU, true, 1);
+    else if (epi == EPI_GELU && kc == 2) KVATTN_GEMV(EPI_GELU, true, 2);
+    else if (epi == EPI_STORE && kc == 1) KVATTN_GEMV(EPI_STORE, true, 1);
+    else if (epi == EPI_STORE && kc == 2) KVATTN_GEMV(EPI_STORE, true, 2);
+    else return hipErrorInvalidValue;
+  } else {
+    if (epi != EPI_RESIDUAL) return hipErrorInvalidValue;
+    switch (kc) {
+      case 1: KVATTN_GEMV(EPI_RESIDUAL, false, 1); break;
+      case 2: KVATTN_GEMV(EPI_RESIDUAL, false, 2); break;
+      case 4: KVATTN_GEMV(EPI_RESIDUAL, false, 4); break;
+      case 8: KVATTN_GEMV(EPI_RESIDUAL, false, 8); break;
+      case 16: KVATTN_GEMV(EPI_RESIDUAL, false, 16); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef KVATTN_GEMV
+  return hipGetLastError();
+}
+
+// C (M x N, row-major) = A (M x K, row-major) * W^T, W (N x K, row-major):
+// column-major C^T = W^T(op) * A^T with no copies.  fp16 inputs, fp32
+// accumulation; C fp16, or fp32 with C = beta * C + A W^T.
+rocblas_status gemm_rows(rocblas_handle h, const half_t *A, const half_t *W, void *C, int M, int N, int K,
+                         bool c_f32, float beta) {
+  const float alpha = 1.f;
+  const rocblas_datatype ct = c_f32 ? rocblas_datatype_f32_r : rocblas_datatype_f16_r;
+  return rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &alpha, W,
+                         rocblas_datatype_f16_r, K, A, rocblas_datatype_f16_r, K, &beta, C, ct, N, C, ct, N,
+                         rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+}
+
+template <typename P>
+hipError_t dev_alloc(P **p, size_t elems) {
+  return hipMalloc((void **)p, elems * sizeof(P));
+}
+
+void free_prompt_buffers(kvattn_model *m) {
+  for (void *p : {(void *)m->px, (void *)m->ph, (void *)m->pqkv, (void *)m->pq, (void *)m->pk, (void *)m->pv,
+                  (void *)m->po, (void *)m->pflat, (void *)m->pup})
+    if (p) (void)hipFree(p);
+  m->px = nullptr;
+  m->ph = m->pqkv = m->pq = m->pk = m->pv = m->po = m->pflat = m->pup = nullptr;
+  m->prompt_rows = 0;
+}
+
+hipError_t ensure_prompt_buffers(kvattn_model *m, size_t rows) {
+  if (rows <= m->prompt_rows) return hipSuccess;
+  hipError_t e = hipDeviceSynchronize();  // buffers of an earlier prompt may still be in use
+  if (e != hipSuccess) return e;
+  free_prompt_buffers(m);
+  const size_t d = m->d;
+  e = dev_alloc(&m->px, rows * d);
+  if (e == hipSuccess) e = dev_alloc(&m->ph, rows * d);
+  if (e == hipSuccess) e = dev_alloc(&m->pqkv, rows * 3 * d);
+  if (e == hipSuccess) e = dev_alloc(&m->pq, rows * d);
+  if (e == hipSuccess) e = dev_alloc(&m->pk, rows * d);
+  if (e == hipSuccess) e = dev_alloc(&m->pv, rows * d);
+  if (e == hipSuccess) e = dev_alloc(&m->po, rows * d);
+  if (e == hipSuccess) e = dev_alloc(&m->pflat, rows * d);
+  if (e == hipSuccess) e = dev_alloc(&m->pup, rows * (size_t)m->mlp);
+  if (e != hipSuccess) {
+    free_prompt_buffers(m);
+    return e;
+  }
+  m->prompt_rows = rows;
+  return hipSuccess;
+}
+
+// final norm, LM head and greedy choice of the (B, d) rows in m->x
+hipError_t enqueue_head(kvattn_model *m, float *logits, int32_t *next, int32_t *out, hipStream_t s) {
+  GemvArgs g{};
+  g.W = m->lm_head;
+  g.in = m->x;
+  g.gain = m->ln_f;
+  g.out = logits;
+  g.B = m->batch;
+  g.N = m->vocab;
+  g.K = m->d;
+  g.d = m->d;
+  hipError_t e = launch_gemv(EPI_STORE, true, g, s);
+  if (e != hipSuccess) return e;
+  argmax_kernel<<<1, 256, 0, s>>>(logits, m->batch, m->vocab, next, out, m->step_ctr);
+  return hipGetLastError();
+}
+
+// One decode step of every sequence (no host-side state is touched, so the
+// same launches can be captured into a graph): the embedding reads each
+// sequence's position from layer 0's device lengths before that layer's append.
+hipError_t enqueue_step(kvattn_model *m, const int32_t *tokens, float *logits, int32_t *next, int32_t *out,
+                        hipStream_t s) {
+  kvattn_cache *c = m->cache;
+  const int B = m->batch, d = m->d;
+  embed_kernel<<<dim3(1, B), 256, 0, s>>>(tokens, c->d_len, m->tok_emb, m->pos_emb, m->x, 1, d, m->vocab);
+  hipError_t e = hipGetLastError();
+  for (int l = 0; l < m->layers && e == hipSuccess; ++l) {
+    GemvArgs g{};
+    g.W = m->wqkv[l];
+    g.in = m->x;
+    g.gain = m->ln1[l];
+    g.q = m->q;
+    g.k = m->k;
+    g.v = m->v;
+    g.B = B;
+    g.N = 3 * d;
+    g.K = d;
+    g.d = d;
+    e = launch_gemv(EPI_QKV, true, g, s);
+    if (e != hipSuccess) break;
+
+    AppendArgs ap;
+    ap.k_layer = cache_layer_k(c, l);
+    ap.v_layer = cache_layer_v(c, l);
+    ap.k_new = (const char *)m->k;
+    ap.v_new = (const char *)m->v;
+    ap.len = c->d_len + (size_t)l * B;
+    ap.batch = B;
+    ap.kv_heads = m->heads;
+    ap.max_T = m->max_T;
+    ap.row_bytes = m->D * 2;
+    ap.table = nullptr;
+    ap.block_log2 = 0;
+    ap.max_blocks = 0;
+    e = launch_append(ap, s);
+    if (e != hipSuccess) break;
+
+    DecodeArgs da;
+    da.k_layer = cache_layer_k(c, l);
+    da.v_layer = cache_layer_v(c, l);
+    da.q = m->q;
+    da.o = m->att;
+    da.ws = c->d_ws;
+    da.len = c->d_len + (size_t)l * B;
+    da.batch = B;
+    da.q_heads = m->heads;
+    da.kv_heads = m->heads;
+    da.head_dim = m->D;
+    da.max_T = m->max_T;
+    da.chunk = c->chunk;
+    da.n_splits = c->n_splits;
+    da.window = 0;
+    da.sink = 0;
+    da.scale_log2 = (float)(1.0 / std::sqrt((double)m->D)) * 1.4426950408889634f;
+    da.dt = KVATTN_F16;
+    da.o_dt = KVATTN_F32;
+    da.table = nullptr;
+    da.block_log2 = 0;
+    da.max_blocks = 0;
+    e = launch_decode(da, s);
+    if (e != hipSuccess) break;
+
+    GemvArgs go{};
+    go.W = m->wo[l];
+    go.in = m->att;
+    go.out = m->x;
+    go.B = B;
+    go.N = d;
+    go.K = d;
+    go.d = d;
+    e = launch_gemv(EPI_RESIDUAL, false, go, s);
+    if (e != hipSuccess) break;
+
+    GemvArgs gu{};
+    gu.W = m->wup[l];
+    gu.in = m->x;
+    gu.gain = m->ln2[l];
+    gu.out = m->hid;
+    gu.B = B;
+    gu.N = m->mlp;
+    gu.K = d;
+    gu.d = d;
+    e = launch_gemv(EPI_GELU, true, gu, s);
+    if (e != hipSuccess) break;
+
+    GemvArgs gd{};
+    gd.W = m->wdown[l];
+    gd.in = m->hid;
+    gd.out = m->x;
+    gd.B = B;
+    gd.N = d;
+    gd.K = m->mlp;
+    gd.d = d;
+    e = launch_gemv(EPI_RESIDUAL, false, gd, s);
+  }
+  if (e != hipSuccess) return e;
+  return enqueue_head(m, logits, next, out, s);
+}
+
+int check_model_device(const kvattn_model *m) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return model_hip_fail(e, "hipGetDevice");
+  if (dev != m->device) return KVATTN_ERR_STATE;
+  return KVATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvattn_model_weight_elems(int layers, int d_model, int vocab, int max_T, int mlp_mult) {
+  if (layers <= 0 || d_model <= 0 || vocab <= 0 || max_T <= 0 || mlp_mult <= 0) return 0;
+  const size_t d = d_model, mlp = (size_t)mlp_mult * d_model;
+  const size_t per_layer = d + 3 * d * d + d * d + d + mlp * d + d * mlp;
+  return (size_t)vocab * d + (size_t)max_T * d + (size_t)layers * per_layer + d + (size_t)vocab * d;
+}
+
+int kvattn_model_create(kvattn_model **out, int layers, int d_model, int heads, int vocab, int max_T,
+                        int mlp_mult, int batch, const void *weights) {
+  if (!out) return KVATTN_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!weights || layers <= 0 || d_model <= 0 || heads <= 0 || vocab <= 0 || max_T <= 0 || mlp_mult <= 0 ||
+      batch <= 0)
+    return KVATTN_ERR_INVALID_ARG;
+  if (batch > kMaxBatch || d_model % heads != 0 || d_model % 512 != 0 || d_model > 1024 ||
+      (long long)mlp_mult * d_model > 8192)
+    return KVATTN_ERR_UNSUPPORTED;
+  const int D = d_model / heads;
+  if (D != 32 && D != 64 && D != 128) return KVATTN_ERR_UNSUPPORTED;
+
+  kvattn_model *m = new (std::nothrow) kvattn_model();
+  if (!m) return KVATTN_ERR_OOM;
+  m->layers = layers;
+  m->d = d_model;
+  m->heads = heads;
+  m->D = D;
+  m->vocab = vocab;
+  m->max_T = max_T;
+  m->mlp = mlp_mult * d_model;
+  m->batch = batch;
+  const half_t *p = (const half_t *)weights;
+  const size_t d = d_model;
+  m->tok_emb = p;
+  p += (size_t)vocab * d;
+  m->pos_emb = p;
+  p += (size_t)max_T * d;
+  for (int l = 0; l < layers; ++l) {
+    m->ln1.push_back(p);
+    p += d;
+    m->wqkv.push_back(p);
+    p += 3 * d * d;
+    m->wo.push_back(p);
+    p += d * d;
+    m->ln2.push_back(p);
+    p += d;
+    m->wup.push_back(p);
+    p += (size_t)m->mlp * d;
+    m->wdown.push_back(p);
+    p += d * m->mlp;
+  }
+  m->ln_f = p;
+  p += d;
+  m->lm_head = p;
+
+  hipError_t e = hipGetDevice(&m->device);
+  if (e != hipSuccess) {
+    delete m;
+    return model_hip_fail(e, "hipGetDevice");
+  }
+  int rc = kvattn_cache_alloc(&m->cache, layers, batch, heads, heads, D, max_T, KVATTN_F16, nullptr, 0);
+  if (rc) {
+    delete m;
+    return rc;
+  }
+  e = dev_alloc(&m->x, (size_t)batch * d);
+  if (e == hipSuccess) e = dev_alloc(&m->att, (size_t)batch * d);
+  if (e == hipSuccess) e = dev_alloc(&m->hid, (size_t)batch * m->mlp);
+  if (e == hipSuccess) e = dev_alloc(&m->logits, (size_t)batch * vocab);
+  if (e == hipSuccess) e = dev_alloc(&m->q, (size_t)batch * d);
+  if (e == hipSuccess) e = dev_alloc(&m->k, (size_t)batch * d);
+  if (e == hipSuccess) e = dev_alloc(&m->v, (size_t)batch * d);
+  if (e == hipSuccess) e = dev_alloc(&m->tok, (size_t)batch);
+  if (e == hipSuccess) e = dev_alloc(&m->gen_out, (size_t)max_T * batch);
+  if (e == hipSuccess) e = dev_alloc(&m->step_ctr, 1);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->gs, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_in, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_out, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess || rocblas_create_handle(&m->blas) != rocblas_status_success) {
+    int r = e != hipSuccess ? model_hip_fail(e, "model buffers") : KVATTN_ERR_HIP;
+    kvattn_model_free(m);
+    return e == hipErrorOutOfMemory ? KVATTN_ERR_OOM : r;
+  }
+  *out = m;
+  return KVATTN_OK;
+}
+
+int kvattn_model_free(kvattn_model *m) {
+  if (!m) return KVATTN_ERR_INVALID_ARG;
+  hipError_t e = hipDeviceSynchronize();
+  if (m->graph) (void)hipGraphExecDestroy(m->graph);
+  if (m->blas) (void)rocblas_destroy_handle(m->blas);
+  free_prompt_buffers(m);
+  for (void *p : {(void *)m->x, (void *)m->att, (void *)m->hid, (void *)m->logits, (void *)m->q, (void *)m->k,
+                  (void *)m->v, (void *)m->tok, (void *)m->gen_out, (void *)m->step_ctr})
+    if (p) (void)hipFree(p);
+  if (m->ev_in) (void)hipEventDestroy(m->ev_in);
+  if (m->ev_out) (void)hipEventDestroy(m->ev_out);
+  if (m->gs) (void)hipStreamDestroy(m->gs);
+  int rc = m->cache ? kvattn_cache_free(m->cache) : KVATTN_OK;
+  delete m;
+  if (e != hipSuccess) return model_hip_fail(e, "kvattn_model_free sync");
+  return rc;
+}
+
+int kvattn_model_reset(kvattn_model *m, void *stream) {
+  if (!m) return KVATTN_ERR_INVALID_ARG;
+  std::vector<int32_t> zeros(m->batch, 0);
+  return kvattn_cache_set_lengths(m->cache, -1, zeros.data(), stream);
+}
+
+int kvattn_model_positions(const kvattn_model *m, int32_t *host_pos) {
+  if (!m || !host_pos) return KVATTN_ERR_INVALID_ARG;
+  return kvattn_cache_get_lengths(m->cache, 0, host_pos);
+}
+
+int kvattn_model_prefill(kvattn_model *m, const int32_t *tokens, int T, float *logits, int32_t *next,
+                         void *stream) {
+  if (!m || !tokens || !next || T <= 0) return KVATTN_ERR_INVALID_ARG;
+  kvattn_cache *c = m->cache;
+  for (size_t i = 0; i < c->h_len.size(); ++i)
+    if (c->h_len[i] != 0) return KVATTN_ERR_STATE;
+  if (T > m->max_T) return KVATTN_ERR_CAPACITY;
+  int rc = check_model_device(m);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const int B = m->batch, d = m->d, H = m->heads, D = m->D;
+  const size_t R = (size_t)B * T;
+  hipError_t e = ensure_prompt_buffers(m, R);
+  if (e != hipSuccess) return e == hipErrorOutOfMemory ? KVATTN_ERR_OOM : model_hip_fail(e, "prompt buffers");
+  if (rocblas_set_stream(m->blas, s) != rocblas_status_success) return KVATTN_ERR_HIP;
+
+  embed_kernel<<<dim3(T, B), 256, 0, s>>>(tokens, nullptr, m->tok_emb, m->pos_emb, m->px, T, d, m->vocab);
+  e = hipGetLastError();
+  for (int l = 0; l < m->layers && e == hipSuccess; ++l) {
+    rmsnorm_rows_kernel<<<dim3((unsigned)R), 256, 0, s>>>(m->px, m->ln1[l], m->ph, d);
+    if (gemm_rows(m->blas, m->ph, m->wqkv[l], m->pqkv, (int)R, 3 * d, d, false, 0.f) != rocblas_status_success)
+      return KVATTN_ERR_HIP;
+    split_qkv_kernel<<<dim3((unsigned)R, (3 * d + 255) / 256), 256, 0, s>>>(m->pqkv, m->pq, m->pk, m->pv, T, H, D);
+    PrefillArgs a;
+    a.q = m->pq;
+    a.k = m->pk;
+    a.v = m->pv;
+    a.o = m->po;
+    a.cache_k = cache_layer_k(c, l);
+    a.cache_v = cache_layer_v(c, l);
+    a.len = c->d_len + (size_t)l * B;
+    a.offsets = nullptr;
+    a.batch = B;
+    a.q_heads = H;
+    a.kv_heads = H;
+    a.head_dim = D;
+    a.T = T;
+    a.max_T = m->max_T;
+    a.kv_rows = T;
+    a.write_cache = 1;
+    a.window = 0;
+    a.sink = 0;
+    a.scale_log2 = (float)(1.0 / std::sqrt((double)D)) * 1.4426950408889634f;
+    a.dt = KVATTN_F16;
+    a.o_dt = KVATTN_F16;
+    e = launch_prefill(a, s);
+    if (e != hipSuccess) break;
+    merge_heads_kernel<<<dim3((unsigned)R, (d + 255) / 256), 256, 0, s>>>(m->po, m->pflat, T, H, D);
+    if (gemm_rows(m->blas, m->pflat, m->wo[l], m->px, (int)R, d, d, true, 1.f) != rocblas_status_success)
+      return KVATTN_ERR_HIP;
+    rmsnorm_rows_kernel<<<dim3((unsigned)R), 256, 0, s>>>(m->px, m->ln2[l], m->ph, d);
+    if (gemm_rows(m->blas, m->ph, m->wup[l], m->pup, (int)R, m->mlp, d, false, 0.f) != rocblas_status_success)
+      return KVATTN_ERR_HIP;
+    const size_t n_up = R * (size_t)m->mlp;
+    gelu_half_kernel<<<dim3((unsigned)((n_up + 255) / 256)), 256, 0, s>>>(m->pup, n_up);
+    if (gemm_rows(m->blas, m->pup, m->wdown[l], m->px, (int)R, d, m->mlp, true, 1.f) != rocblas_status_success)
+      return KVATTN_ERR_HIP;
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    gather_last_kernel<<<dim3(B), 256, 0, s>>>(m->px, m->x, T, d);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = enqueue_head(m, logits ? logits : m->logits, next, nullptr, s);
+  if (e != hipSuccess) return model_hip_fail(e, "model prefill launch");
+  for (size_t i = 0; i < c->h_len.size(); ++i) c->h_len[i] = T;
+  return KVATTN_OK;
+}
+
+int kvattn_model_step(kvattn_model *m, const int32_t *tokens, float *logits, int32_t *next, void *stream) {
+  if (!m || !tokens || !next) return KVATTN_ERR_INVALID_ARG;
+  kvattn_cache *c = m->cache;
+  for (size_t i = 0; i < c->h_len.size(); ++i)
+    if (c->h_len[i] >= m->max_T) return KVATTN_ERR_CAPACITY;
+  int rc = check_model_device(m);
+  if (rc) return rc;
+  hipError_t e = enqueue_step(m, tokens, logits ? logits : m->logits, next, nullptr, (hipStream_t)stream);
+  if (e != hipSuccess) return model_hip_fail(e, "model step launch");
+  for (size_t i = 0; i < c->h_len.size(); ++i) c->h_len[i] += 1;
+  return KVATTN_OK;
+}
+
+int kvattn_model_generate(kvattn_model *m, int n_steps, int32_t *tokens, int32_t *out_tokens, void *stream) {
+  if (!m || !tokens || !out_tokens || n_steps <= 0) return KVATTN_ERR_INVALID_ARG;
+  kvattn_cache *c = m->cache;
+  for (size_t i = 0; i < c->h_len.size(); ++i)
+    if (c->h_len[i] + n_steps > m->max_T) return KVATTN_ERR_CAPACITY;
+  int rc = check_model_device(m);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t tok_bytes = sizeof(int32_t) * m->batch;
+  hipError_t e = hipEventRecord(m->ev_in, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(m->gs, m->ev_in, 0);
+  if (e == hipSuccess) e = hipMemcpyAsync(m->tok, tokens, tok_bytes, hipMemcpyDeviceToDevice, m->gs);
+  if (e == hipSuccess) {
+    set_int_kernel<<<1, 1, 0, m->gs>>>(m->step_ctr, 0);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && !m->graph) {
+    // the step on fixed internal buffers: tokens in m->tok (overwritten by the
+    // argmax), every generated token appended to m->gen_out through the
+    // device step counter
+    hipGraph_t g = nullptr;
+    e = hipStreamBeginCapture(m->gs, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      hipError_t e1 = enqueue_step(m, m->tok, m->logits, m->tok, m->gen_out, m->gs);
+      e = hipStreamEndCapture(m->gs, &g);
+      if (e1 != hipSuccess) e = e1;
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&m->graph, g, nullptr, nullptr, 0);
+    if (g) (void)hipGraphDestroy(g);
+  }
+  for (int i = 0; i < n_steps && e == hipSuccess; ++i) e = hipGraphLaunch(m->graph, m->gs);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(out_tokens, m->gen_out, tok_bytes * n_steps, hipMemcpyDeviceToDevice, m->gs);
+  if (e == hipSuccess) e = hipMemcpyAsync(tokens, m->tok, tok_bytes, hipMemcpyDeviceToDevice, m->gs);
+  if (e == hipSuccess) e = hipEventRecord(m->ev_out, m->gs);
+  if (e == hipSuccess) e = hipStreamWaitEvent(s, m->ev_out, 0);
+  if (e != hipSuccess) return model_hip_fail(e, "model generate");
+  for (size_t i = 0; i < c->h_len.size(); ++i) c->h_len[i] += n_steps;
+  return KVATTN_OK;
+}
+
+const char *kvattn_model_last_error(void) { return g_model_error; }
+
+}  // extern "C"

@@ -4,6 +4,7 @@ import json
 import os
 import re
 
+import numpy as np
 import pytest
 
 import kv_cached_causal_amd as kv
@@ -181,3 +182,42 @@ def test_paged_calls_reject_null_object_without_a_device():
     assert lib.kvattn_paged_get_lengths(None, 0, (ctypes.c_int32 * 1)()) == -1
     k, v = ctypes.c_void_p(), ctypes.c_void_p()
     assert lib.kvattn_paged_kv_ptr(None, 0, ctypes.byref(k), ctypes.byref(v)) == -1
+
+
+def test_model_weight_elems_matches_the_packing_order():
+    import dataclasses
+    import synth_inputs as si
+    lib = kv.lib()
+    for spec in (si.TINYGPT, dataclasses.replace(si.TINYGPT, layers=2, d_model=1024, heads=8, vocab=300, max_T=77)):
+        n = sum(int(np.prod(shape)) for _, shape in si.model_weight_shapes(spec))
+        assert lib.kvattn_model_weight_elems(spec.layers, spec.d_model, spec.vocab, spec.max_T, spec.mlp_mult) == n
+    assert lib.kvattn_model_weight_elems(0, 512, 10, 10, 4) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((2, 512, 16, 100, 64, 4, 1), -1),   # null weights (checked first)
+    ((2, 500, 10, 100, 64, 4, 1), -2),   # width not a multiple of 512
+    ((2, 512, 5, 100, 64, 4, 1), -2),    # heads do not divide the width
+    ((2, 512, 8, 100, 64, 4, 9), -2),    # batch above 8
+    ((2, 2048, 16, 100, 64, 4, 1), -2),  # width above 1024
+    ((2, 512, 2, 100, 64, 4, 1), -2),    # head dim 256
+    ((0, 512, 16, 100, 64, 4, 1), -1),
+])
+def test_model_create_validation_before_any_device_call(args, status):
+    lib = kv.lib()
+    out = ctypes.c_void_p()
+    weights = None if status == -1 and args[0] == 2 else ctypes.c_void_p(1 << 20)  # never dereferenced
+    assert lib.kvattn_model_create(ctypes.byref(out), *args, weights) == status
+    assert not out.value
+    assert lib.kvattn_model_create(None, *args, weights) == -1
+
+
+def test_model_calls_reject_null_model_without_a_device():
+    lib = kv.lib()
+    p = ctypes.c_void_p(0)
+    assert lib.kvattn_model_free(None) == -1
+    assert lib.kvattn_model_reset(None, None) == -1
+    assert lib.kvattn_model_prefill(None, p, 4, p, p, None) == -1
+    assert lib.kvattn_model_step(None, p, p, p, None) == -1
+    assert lib.kvattn_model_generate(None, 4, p, p, None) == -1
+    assert lib.kvattn_model_positions(None, (ctypes.c_int32 * 1)()) == -1
