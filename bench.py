@@ -438,7 +438,8 @@ def paged_measurements(kv, w, dec, full_us, block_size=64, layers=4, reps=5):
 def decoder_measurements(kv, dev, prompt=4096, new_tokens=128):
     """The README's 8-layer, 512-wide, 16-head decoder (vocabulary 4096) with random
     weights: prompt of `prompt` tokens, then `new_tokens` greedy tokens, batch 1 (the
-    README's KV-cache table) and batch 8.  The step is replayed from a HIP graph."""
+    README's KV-cache table) and batch 8.  Generation enqueues the steps back to back with
+    the token kept on the device."""
     spec = si.TINYGPT
     flat = torch.from_numpy(si.pack_model_weights(spec, si.model_weights(spec))).to(dev)
     out = {"workload": f"{spec.layers}L x {spec.d_model}d, {spec.heads} heads, vocab {spec.vocab}, fp16 weights; "
@@ -449,7 +450,7 @@ def decoder_measurements(kv, dev, prompt=4096, new_tokens=128):
         m = kv.Decoder(spec.layers, spec.d_model, spec.heads, spec.vocab, spec.max_T, spec.mlp_mult, batch, flat)
         tokens = torch.from_numpy(si.model_tokens(spec, batch, prompt)).to(dev)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        for rep in range(2):  # the first pass captures the step graph and warms rocBLAS
+        for rep in range(2):  # the first pass warms rocBLAS and the kernels
             m.reset()
             ev[0].record()
             _, nxt = m.prefill(tokens)

@@ -44,7 +44,7 @@ size_t kvattn_model_weight_elems(int layers, int d_model, int vocab, int max_T, 
  * d_model / heads must be 32, 64 or 128 and d_model a multiple of 512, at
  * most 1024 (UNSUPPORTED otherwise).  Allocates the model's KV cache
  * (kvattn_cache_alloc), activation buffers, a rocBLAS handle for the
- * prompt's projections and a stream for its step graph. */
+ * prompt's projections and a stream for generation. */
 int kvattn_model_create(kvattn_model **out, int layers, int d_model, int heads, int vocab, int max_T,
                         int mlp_mult, int batch, const void *weights);
 
@@ -77,10 +77,10 @@ int kvattn_model_step(kvattn_model *m, const int32_t *tokens, float *logits, int
 /* Greedy generation of n_steps tokens per sequence: tokens (device int32,
  * batch) holds each sequence's current token and ends holding its last
  * generated one; out_tokens (device int32, n_steps x batch) receives every
- * generated token.  The step is captured once into a HIP graph (on the
- * model's own stream, ordered after `stream` by events) and replayed
- * n_steps times; `stream` is ordered after the replays.  CAPACITY if a
- * sequence would pass max_T. */
+ * generated token.  The steps are enqueued back to back on the model's own
+ * stream (ordered after `stream` by events) with the tokens kept on the
+ * device; `stream` is ordered after the last step.  CAPACITY if a sequence
+ * would pass max_T. */
 int kvattn_model_generate(kvattn_model *m, int n_steps, int32_t *tokens, int32_t *out_tokens, void *stream);
 
 /* Text of the last HIP error this thread's model calls saw ("" if none). */

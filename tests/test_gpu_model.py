@@ -87,12 +87,13 @@ def test_prefill_and_decode_match_oracle(name, batch):
     m.close()
 
 
-def test_generate_graph_equals_eager_steps():
-    """Greedy generation through the captured step graph gives the tokens of the
-    eager step loop on an identical model, over two generate calls."""
+def test_generate_equals_single_steps():
+    """Greedy generation (steps enqueued back to back, tokens kept on the device)
+    gives the tokens of a loop of single steps on an identical model, over two
+    generate calls."""
     kv = _kv()
     spec = SPECS["2L_d512_h16"]
-    say("graph generation vs eager steps")
+    say("generation vs single steps")
     tokens = torch.from_numpy(si.model_tokens(spec, 2, 30, seed=9)).cuda()
     a, _, wa = _model(kv, spec, 2, seed=9)
     b, _, wb = _model(kv, spec, 2, seed=9)
