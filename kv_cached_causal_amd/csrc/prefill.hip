@@ -21,6 +21,7 @@
 // store that K/V tile into the cache from the registers it was loaded into.
 //
 // F32 takes a plain vector-ALU kernel (one lane per query row).
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -872,13 +873,20 @@ struct PrefillConfig {
   static constexpr int BN = (!kPipe && D == 32) ? 128 : 64;
 };
 
+// Launch with `lds` bytes of dynamic LDS.  The kernel's maximum dynamic LDS
+// attribute is set once per device (bit d of `attr_done`; always for device
+// ids past 63).
 template <typename KernelT>
-static hipError_t launch_with_lds(KernelT kern, dim3 grid, int threads, size_t lds, hipStream_t s, bool &attr_done,
-                                  const PrefillArgs &a) {
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+static hipError_t launch_with_lds(KernelT kern, dim3 grid, int threads, size_t lds, hipStream_t s,
+                                  std::atomic<uint64_t> &attr_done, const PrefillArgs &a) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_done = true;
+    attr_done.fetch_or(bit, std::memory_order_release);
   }
   kern<<<grid, threads, lds, s>>>(a);
   return hipGetLastError();
@@ -893,7 +901,7 @@ static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
   constexpr int BM = C::NW * C::QW;
   const int n_qt = (a.T + BM - 1) / BM;
   const dim3 grid((unsigned)n_qt * a.batch * a.q_heads);
-  static bool attr_done = false;
+  static std::atomic<uint64_t> attr_done{0};
   if constexpr (C::kPipe) {
     if (a.window > 0) return launch_extend_mfma<T, D>(a, s);  // the plain kernel takes the window mask
     return launch_with_lds(prefill_pipe_kernel<T, D, C::QW, C::BN, C::NW>, grid, C::NW * 64,
@@ -917,7 +925,7 @@ template <typename T, int D>
 static hipError_t launch_extend_mfma(const PrefillArgs &a, hipStream_t s) {
   constexpr int NW = 4, QW = 32, BN = D == 32 ? 128 : 64, BM = NW * QW;
   const int n_qt = (a.T + BM - 1) / BM;
-  static bool attr_done = false;
+  static std::atomic<uint64_t> attr_done{0};
   return launch_with_lds(prefill_mfma_kernel<T, D, QW, BN, NW>, dim3((unsigned)n_qt * a.batch * a.q_heads),
                          NW * 64, PrefillLds<D, BN>::BYTES, s, attr_done, a);
 }
