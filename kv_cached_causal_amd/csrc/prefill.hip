@@ -705,6 +705,10 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
       vec8 pb[PS][NT];
       vec8 pl[Mfma<T>::kSplitP ? PS : 1][NT];
       float al[NT];
+      // Raised priority for the tile's math and back to normal for the
+      // staging stores: when both waves of a SIMD are ready, the one with
+      // matrix work issues first (about 2% faster on MI355X, T = 8192).
+      __builtin_amdgcn_s_setprio(2);
       const bool any_resc = stats(cur, al);
       // The next tile's scores are computed unconditionally (on the wave's
       // diagonal tile they go unused: the slot then holds finite stale data
@@ -743,6 +747,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
         mask(t, nxt);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (j + 2 < n_tiles) store_k(j + 2, j & 1);
     if (j + 1 < n_tiles) store_v(j + 1, (j + 1) & 1);
     __syncthreads();
