@@ -171,7 +171,8 @@ int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scal
  * block must be the same for every slot that writes them.  Calls cover every
  * slot, like the contiguous cache (slots = batch); lengths are per (layer,
  * slot) with a host mirror; a slot holds at most n_blocks * block_size
- * positions.  No sliding window on a paged cache. */
+ * positions.  Sliding window and sink masks as for the contiguous cache
+ * (kvattn_paged_set_window). */
 typedef struct kvattn_paged kvattn_paged; /* opaque, library-owned */
 
 /* Pool bytes: 2 * layers * num_blocks * block_size * kv_heads * head_dim *
@@ -208,6 +209,15 @@ int kvattn_paged_set_blocks(kvattn_paged *p, int slot, const int32_t *host_block
 int kvattn_paged_set_lengths(kvattn_paged *p, int layer, const int32_t *host_lens, void *stream);
 int kvattn_paged_get_lengths(const kvattn_paged *p, int layer, int32_t *host_lens);
 
+/* Window and sink of one layer (>= 0) or of every layer (-1), with the
+ * meaning of kvattn_cache_set_window; later prefill, extend and decode calls
+ * on the layer use them, and decode reads only the visible rows' blocks.
+ * UNSUPPORTED when a windowed decode split would stage more block-table
+ * entries than its on-chip table holds (2 * (split / block_size + 2) > 512;
+ * only for very small blocks with very long capacities).  Host-only. */
+int kvattn_paged_set_window(kvattn_paged *p, int layer, int window, int sink);
+int kvattn_paged_get_window(const kvattn_paged *p, int layer, int *window, int *sink);
+
 /* Prefill of one layer: causal attention of the T prompt queries of every
  * slot (q (slots,H,T,D), k/v (slots,Hkv,T,D), o in o_dtype) as
  * kvattn_prefill, then a bit-exact copy of k, v into each slot's blocks at
@@ -221,8 +231,15 @@ int kvattn_paged_prefill(kvattn_paged *p, int layer, const void *q, const void *
  * blocks are full. */
 int kvattn_paged_append(kvattn_paged *p, int layer, const void *k_new, const void *v_new, void *stream);
 
+/* Extend over the paged cache: as kvattn_extend (chunked prefill, multi-token
+ * verification), with the new rows written to positions [len, len + T) of
+ * each slot's blocks and the attention reading every key through the slot's
+ * block table; len += T.  CAPACITY if len + T exceeds a slot's blocks. */
+int kvattn_paged_extend(kvattn_paged *p, int layer, const void *q, const void *k, const void *v, void *o,
+                        int T, float scale, kvattn_dtype o_dtype, void *stream);
+
 /* Decode over the paged cache: as kvattn_decode, each slot's query attending
- * its len positions, read through its block table. */
+ * its len positions (or its window and sink), read through its block table. */
 int kvattn_paged_decode(kvattn_paged *p, int layer, const void *q, void *o, float scale,
                         kvattn_dtype o_dtype, void *stream);
 

@@ -67,6 +67,11 @@ _SIGS = {
                              + [ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_paged_append": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p]),
+    "kvattn_paged_set_window": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "kvattn_paged_get_window": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                               ctypes.POINTER(ctypes.c_int)]),
+    "kvattn_paged_extend": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 4
+                            + [ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_paged_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_model_weight_elems": (ctypes.c_size_t, [ctypes.c_int] * 5),
@@ -409,6 +414,17 @@ class PagedKVCache:
         _check(lib().kvattn_paged_get_lengths(self._handle, layer, arr), "kvattn_paged_get_lengths")
         return list(arr)
 
+    def set_window(self, window: int, sink: int = 0, layer: int = -1) -> None:
+        """Sliding window W (0: none) and sink S of one layer, or of all (-1)."""
+        _check(lib().kvattn_paged_set_window(self._handle, layer, int(window), int(sink)),
+               "kvattn_paged_set_window")
+
+    def window(self, layer: int) -> tuple:
+        w, s = ctypes.c_int(), ctypes.c_int()
+        _check(lib().kvattn_paged_get_window(self._handle, layer, ctypes.byref(w), ctypes.byref(s)),
+               "kvattn_paged_get_window")
+        return w.value, s.value
+
     def _tensor(self, t, shape, name, dtype=None):
         KVCache._tensor(self, t, shape, name, dtype)
 
@@ -429,6 +445,23 @@ class PagedKVCache:
             _check(lib().kvattn_paged_prefill(self._handle, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(out), T,
                                               self._scale(scale), _DT[od], _stream_ptr(self.device)),
                    "kvattn_paged_prefill")
+        return out
+
+    def extend(self, layer: int, q, k, v, out=None, scale=None, out_dtype=None) -> torch.Tensor:
+        """T new positions per slot after its cached prefix, read and written through the block tables."""
+        S, H, Hkv, D = self.slots, self.q_heads, self.kv_heads, self.head_dim
+        T = q.shape[2] if q.dim() == 4 else -1
+        self._tensor(q, (S, H, T, D), "q")
+        self._tensor(k, (S, Hkv, T, D), "k")
+        self._tensor(v, (S, Hkv, T, D), "v")
+        od = out_dtype or self.dtype
+        if out is None:
+            out = torch.empty((S, H, T, D), dtype=od, device=self.device)
+        self._tensor(out, (S, H, T, D), "out", od)
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_paged_extend(self._handle, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(out), T,
+                                             self._scale(scale), _DT[od], _stream_ptr(self.device)),
+                   "kvattn_paged_extend")
         return out
 
     def append(self, layer: int, k_new, v_new) -> None:

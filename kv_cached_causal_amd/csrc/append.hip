@@ -43,7 +43,7 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
 }
 
 // Extend: T rows per (sequence, KV head) copied to cache rows [len[b], len[b] + T)
-// (bit copies); grid (row chunks, Hkv, B).  The lengths are only read here and
+// (bit copies; through the block table for a paged cache); grid (row chunks, Hkv, B).  The lengths are only read here and
 // advanced by add_lengths_kernel once the attention over them has run.
 __global__ __launch_bounds__(256) void extend_copy_kernel(ExtendCopyArgs a) {
   const int b = blockIdx.z;
@@ -55,7 +55,9 @@ __global__ __launch_bounds__(256) void extend_copy_kernel(ExtendCopyArgs a) {
   const int w = idx - t * vec_per_row;
   const int pos = a.len[b] + t;
   const size_t src = ((size_t)(b * a.kv_heads + h) * a.T + t) * a.row_bytes + (size_t)w * 16;
-  const size_t dst = ((size_t)(b * a.kv_heads + h) * a.max_T + pos) * a.row_bytes + (size_t)w * 16;
+  const size_t row = a.table ? paged_row(a.table, b, a.max_blocks, a.block_log2, a.kv_heads, h, pos)
+                             : (size_t)(b * a.kv_heads + h) * a.max_T + pos;
+  const size_t dst = row * a.row_bytes + (size_t)w * 16;
   *reinterpret_cast<uint4 *>(a.k_layer + dst) = *reinterpret_cast<const uint4 *>(a.k_new + src);
   *reinterpret_cast<uint4 *>(a.v_layer + dst) = *reinterpret_cast<const uint4 *>(a.v_new + src);
 }

@@ -51,9 +51,21 @@ struct DecodeArgs {
   int block_log2, max_blocks;
 };
 
-// table entries a paged decode split stages in LDS: one split spans at most
-// chunk / block_size + 1 blocks
+// Row index (in rows of D elements) of position `pos` of KV head g of
+// sequence b in a paged pool [num_blocks][Hkv][2^block_log2][D].
+__device__ inline size_t paged_row(const int32_t *table, int b, int max_blocks, int block_log2, int kv_heads,
+                                   int g, int pos) {
+  const int blk = table[(size_t)b * max_blocks + (pos >> block_log2)];
+  return (((size_t)blk * kv_heads + g) << block_log2) + (pos & ((1 << block_log2) - 1));
+}
+
+// table entries a paged decode split stages in LDS: a run of `chunk` positions
+// spans at most chunk / block_size + 2 blocks (+1 when unaligned), and under a
+// window a split may hold two runs (sink rows, then window rows)
 constexpr int kPagedTab = 512;
+inline int paged_tab_entries(int chunk, int block_size, bool window) {
+  return (window ? 2 : 1) * (chunk / block_size + 2);
+}
 
 // The keys a decode query at position L - 1 sees, as one run of visible
 // indices 0 .. count - 1: the first `sink` positions, then the last `window`
@@ -84,15 +96,22 @@ struct PrefillArgs {
   int window, sink;     // sliding window (0: none) and attention-sink positions
   float scale_log2;
   kvattn_dtype dt, o_dt;
+  // paged cache (extend): k/v are the layer's block pools (num_blocks, Hkv,
+  // 2^block_log2, D) and key j of sequence b sits in block
+  // table[b * max_blocks + (j >> block_log2)]; null for the layouts above
+  const int32_t *table = nullptr;
+  int block_log2 = 0, max_blocks = 0;
 };
 
 struct ExtendCopyArgs {
-  char *k_layer;        // layer's K block (B, Hkv, max_T, D)
+  char *k_layer;        // layer's K block (B, Hkv, max_T, D), or the block pools with a table
   char *v_layer;
   const char *k_new;    // (B, Hkv, T, D)
   const char *v_new;
   const int32_t *len;   // layer's lengths [B] (not modified)
   int batch, kv_heads, max_T, row_bytes, T;
+  const int32_t *table = nullptr;  // paged: [B][max_blocks] block ids
+  int block_log2 = 0, max_blocks = 0;
 };
 
 // Prefill rows [0, T) of each (sequence, KV head) copied into a paged

@@ -141,11 +141,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int jump = vk.first - kb;
   const int gap = vk.gap;
   __shared__ int32_t s_tab[PAGED ? kPagedTab : 1];
-  int blk0 = 0;
-  if constexpr (PAGED) {  // no window with a paged cache: position = visible index
-    blk0 = kb >> a.block_log2;
-    const int nblk = ((kb + rows - 1) >> a.block_log2) - blk0 + 1;
-    for (int i = tid; i < nblk; i += NW * 64) s_tab[i] = a.table[(size_t)b * a.max_blocks + blk0 + i];
+  // paged: the table entries of this split's rows, staged in LDS.  Rows
+  // before `jump` (sink run) sit at position kb + r, the others (window run)
+  // at kb + r + gap; entry (pos >> block_log2) + shift_a (resp. shift_b).
+  int shift_a = 0, shift_b = 0;
+  if constexpr (PAGED) {
+    const int n_sink = max(0, min(rows, jump));  // rows of the sink run
+    const int blk_a = kb >> a.block_log2;
+    const int n_a = n_sink > 0 ? ((kb + n_sink - 1) >> a.block_log2) - blk_a + 1 : 0;
+    const int pos_b = kb + n_sink + gap;
+    const int blk_b = pos_b >> a.block_log2;
+    const int n_b = n_sink < rows ? ((kb + rows - 1 + gap) >> a.block_log2) - blk_b + 1 : 0;
+    const int32_t *tab = a.table + (size_t)b * a.max_blocks;
+    for (int i = tid; i < n_a + n_b; i += NW * 64) s_tab[i] = i < n_a ? tab[blk_a + i] : tab[blk_b + i - n_a];
+    shift_a = -blk_a;
+    shift_b = n_a - blk_b;
     __syncthreads();
   }
 
@@ -185,8 +195,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       int r = min(((ib * U + u) * NW + wave) * RPW + rg, rows - 1);
       size_t row;
       if constexpr (PAGED) {
-        const int pos = kb + r;
-        const int blk = s_tab[(pos >> a.block_log2) - blk0];
+        const bool in_b = r >= jump;
+        const int pos = kb + r + (in_b ? gap : 0);
+        const int blk = s_tab[(pos >> a.block_log2) + (in_b ? shift_b : shift_a)];
         row = (((size_t)blk * a.kv_heads + kvh) << a.block_log2) + (pos & ((1 << a.block_log2) - 1));
       } else {
         row = (size_t)(r + (r >= jump ? gap : 0));

@@ -411,6 +411,7 @@ struct kvattn_paged {
   std::vector<int32_t> h_len;  // host mirror
   int32_t *d_table;            // [slots][max_blocks]
   std::vector<int> h_nblk;     // table entries set per slot
+  std::vector<int> window, sink;  // per layer; window 0 = none
   float *d_ws;
   int chunk, n_splits;
   int device;
@@ -465,7 +466,7 @@ int kvattn_paged_alloc(kvattn_paged **out, int layers, int slots, int max_blocks
   if ((long long)max_blocks * block_size > (1LL << 30)) return KVATTN_ERR_UNSUPPORTED;
   const int capacity = max_blocks * block_size;
   const int chunk = decode_chunk(head_dim, q_heads / kv_heads, capacity);
-  if (chunk / block_size + 2 > kPagedTab) return KVATTN_ERR_UNSUPPORTED;
+  if (paged_tab_entries(chunk, block_size, false) > kPagedTab) return KVATTN_ERR_UNSUPPORTED;
   const size_t bytes = kvattn_paged_bytes(layers, num_blocks, block_size, kv_heads, head_dim, dt);
   if (device_buf) {
     if (device_buf_bytes < bytes) return KVATTN_ERR_OOM;
@@ -490,6 +491,8 @@ int kvattn_paged_alloc(kvattn_paged **out, int layers, int slots, int max_blocks
   p->n_splits = (capacity + chunk - 1) / chunk;
   p->h_len.assign((size_t)layers * slots, 0);
   p->h_nblk.assign(slots, 0);
+  p->window.assign(layers, 0);
+  p->sink.assign(layers, 0);
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) {
     delete p;
@@ -601,6 +604,30 @@ int kvattn_paged_get_lengths(const kvattn_paged *p, int layer, int32_t *host_len
   return KVATTN_OK;
 }
 
+int kvattn_paged_set_window(kvattn_paged *p, int layer, int window, int sink) {
+  if (!p) return KVATTN_ERR_INVALID_ARG;
+  if (layer != -1 && (layer < 0 || layer >= p->layers)) return KVATTN_ERR_INVALID_ARG;
+  if (window < 0 || sink < 0) return KVATTN_ERR_INVALID_ARG;
+  // a windowed decode split may stage the table entries of two runs
+  if (window > 0 && paged_tab_entries(p->chunk, p->block_size, true) > kPagedTab) return KVATTN_ERR_UNSUPPORTED;
+  const int first = layer < 0 ? 0 : layer;
+  const int count = layer < 0 ? p->layers : 1;
+  for (int l = first; l < first + count; ++l) {
+    p->window[l] = window;
+    p->sink[l] = window > 0 ? sink : 0;
+  }
+  return KVATTN_OK;
+}
+
+int kvattn_paged_get_window(const kvattn_paged *p, int layer, int *window, int *sink) {
+  int rc = paged_check_layer(p, layer);
+  if (rc) return rc;
+  if (!window || !sink) return KVATTN_ERR_INVALID_ARG;
+  *window = p->window[layer];
+  *sink = p->sink[layer];
+  return KVATTN_OK;
+}
+
 int kvattn_paged_prefill(kvattn_paged *p, int layer, const void *q, const void *k, const void *v, void *o,
                          int T, float scale, kvattn_dtype o_dtype, void *stream) {
   int rc = paged_check_layer(p, layer);
@@ -636,8 +663,8 @@ int kvattn_paged_prefill(kvattn_paged *p, int layer, const void *q, const void *
   a.max_T = T;
   a.kv_rows = T;
   a.write_cache = 0;
-  a.window = 0;
-  a.sink = 0;
+  a.window = p->window[layer];
+  a.sink = p->sink[layer];
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dt = p->dt;
   a.o_dt = o_dtype;
@@ -692,6 +719,76 @@ int kvattn_paged_append(kvattn_paged *p, int layer, const void *k_new, const voi
   return KVATTN_OK;
 }
 
+int kvattn_paged_extend(kvattn_paged *p, int layer, const void *q, const void *k, const void *v, void *o, int T,
+                        float scale, kvattn_dtype o_dtype, void *stream) {
+  int rc = paged_check_layer(p, layer);
+  if (rc) return rc;
+  if (!q || !k || !v || !o) return KVATTN_ERR_INVALID_ARG;
+  if (T <= 0 || !(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
+  if (o_dtype != p->dt && o_dtype != KVATTN_F32) return KVATTN_ERR_UNSUPPORTED;
+  int32_t *hl = &p->h_len[(size_t)layer * p->slots];
+  for (int s = 0; s < p->slots; ++s)
+    if (hl[s] > paged_capacity(p, s) - T) return KVATTN_ERR_CAPACITY;
+  rc = paged_check_device(p);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t *len = p->d_len + (size_t)layer * p->slots;
+
+  // 1. the new K/V rows go to positions [len[b], len[b] + T) of their blocks
+  ExtendCopyArgs cp;
+  cp.k_layer = paged_k(p, layer);
+  cp.v_layer = paged_v(p, layer);
+  cp.k_new = (const char *)k;
+  cp.v_new = (const char *)v;
+  cp.len = len;
+  cp.batch = p->slots;
+  cp.kv_heads = p->kv_heads;
+  cp.max_T = 0;
+  cp.row_bytes = p->head_dim * p->elem;
+  cp.T = T;
+  cp.table = p->d_table;
+  cp.block_log2 = p->block_log2;
+  cp.max_blocks = p->max_blocks;
+  hipError_t e = launch_extend_copy(cp, st);
+  if (e != hipSuccess) return hip_fail(e, "paged extend copy launch");
+
+  // 2. attention of the T new queries over positions [0, len[b] + T), rows
+  //    found through the block table
+  PrefillArgs a;
+  a.q = q;
+  a.k = paged_k(p, layer);
+  a.v = paged_v(p, layer);
+  a.o = o;
+  a.cache_k = paged_k(p, layer);
+  a.cache_v = paged_v(p, layer);
+  a.len = len;
+  a.offsets = len;
+  a.batch = p->slots;
+  a.q_heads = p->q_heads;
+  a.kv_heads = p->kv_heads;
+  a.head_dim = p->head_dim;
+  a.T = T;
+  a.max_T = 0;
+  a.kv_rows = 0;
+  a.write_cache = 0;
+  a.window = p->window[layer];
+  a.sink = p->sink[layer];
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dt = p->dt;
+  a.o_dt = o_dtype;
+  a.table = p->d_table;
+  a.block_log2 = p->block_log2;
+  a.max_blocks = p->max_blocks;
+  e = launch_extend_attention(a, st);
+  if (e != hipSuccess) return hip_fail(e, "paged extend attention launch");
+
+  // 3. commit: len[b] += T
+  e = launch_add_lengths(len, p->slots, T, st);
+  if (e != hipSuccess) return hip_fail(e, "paged extend length update launch");
+  for (int s = 0; s < p->slots; ++s) hl[s] += T;
+  return KVATTN_OK;
+}
+
 int kvattn_paged_decode(kvattn_paged *p, int layer, const void *q, void *o, float scale, kvattn_dtype o_dtype,
                         void *stream) {
   int rc = paged_check_layer(p, layer);
@@ -718,8 +815,8 @@ int kvattn_paged_decode(kvattn_paged *p, int layer, const void *q, void *o, floa
   a.max_T = p->max_blocks * p->block_size;
   a.chunk = p->chunk;
   a.n_splits = p->n_splits;
-  a.window = 0;
-  a.sink = 0;
+  a.window = p->window[layer];
+  a.sink = p->sink[layer];
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dt = p->dt;
   a.o_dt = o_dtype;

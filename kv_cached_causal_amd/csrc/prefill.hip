@@ -102,7 +102,7 @@ constexpr float kLazyMax = 8.0f;
 // 1-D grid over (q-tile, b, h), heaviest (last) query tiles first.  With NW = 4
 // every thread stages both K and V; with NW = 8 waves 0-3 stage K and waves 4-7
 // stage V.
-template <typename T, int D, int QW, int BN, int NW>
+template <typename T, int D, int QW, int BN, int NW, bool PAGED = false>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(PrefillArgs a) {
   typedef typename Mfma<T>::vec vec8;
   typedef PrefillLds<D, BN> LDS;
@@ -150,8 +150,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
   // query row i sits at absolute position off + i and sees keys 0 .. off + i
   const int off = a.offsets ? a.offsets[b] : 0;
   const int last_key = off + Tn - 1;
-  const T *kb = (const T *)a.k + (size_t)(b * a.kv_heads + g) * a.kv_rows * D;
-  const T *vb = (const T *)a.v + (size_t)(b * a.kv_heads + g) * a.kv_rows * D;
+  // paged (extend over a paged cache): k/v are the block pools and a key's
+  // row is found through the sequence's block table
+  const T *kb = (const T *)a.k + (PAGED ? 0 : (size_t)(b * a.kv_heads + g) * a.kv_rows * D);
+  const T *vb = (const T *)a.v + (PAGED ? 0 : (size_t)(b * a.kv_heads + g) * a.kv_rows * D);
+  auto row_of = [&](int key) -> size_t {
+    if constexpr (PAGED) return paged_row(a.table, b, a.max_blocks, a.block_log2, a.kv_heads, g, key);
+    return (size_t)key;
+  };
   T *ckb = (T *)a.cache_k + (size_t)(b * a.kv_heads + g) * a.max_T * D;
   T *cvb = (T *)a.cache_v + (size_t)(b * a.kv_heads + g) * a.max_T * D;
 
@@ -205,14 +211,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
       for (int c = 0; c < KCH; ++c) {
         const int idx = c * 256 + stid;
         const int key = min(k0 + idx / (D / 8), last_key);
-        kreg[c] = *(const u32x4 *)(kb + (size_t)key * D + (idx % (D / 8)) * 8);
+        kreg[c] = *(const u32x4 *)(kb + row_of(key) * D + (idx % (D / 8)) * 8);
       }
     }
     if (stage_v) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = min(k0 + 4 * v_kg + r, last_key);
-        vreg[r] = *(const u32x4 *)(vb + (size_t)key * D + v_ds * 8);
+        vreg[r] = *(const u32x4 *)(vb + row_of(key) * D + v_ds * 8);
       }
     }
   };
@@ -794,8 +800,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 
   const float *qb = (const float *)a.q + (size_t)bh * Tn * D;
   const int off = a.offsets ? a.offsets[b] : 0;  // absolute position of query row 0
-  const float *kb = (const float *)a.k + (size_t)(b * a.kv_heads + g) * a.kv_rows * D;
-  const float *vb = (const float *)a.v + (size_t)(b * a.kv_heads + g) * a.kv_rows * D;
+  // with a block table, k/v are the paged pools and rows are looked up per key
+  const float *kb = (const float *)a.k + (a.table ? 0 : (size_t)(b * a.kv_heads + g) * a.kv_rows * D);
+  const float *vb = (const float *)a.v + (a.table ? 0 : (size_t)(b * a.kv_heads + g) * a.kv_rows * D);
   float *ckb = (float *)a.cache_k + (size_t)(b * a.kv_heads + g) * a.max_T * D;
   float *cvb = (float *)a.cache_v + (size_t)(b * a.kv_heads + g) * a.max_T * D;
   if (a.write_cache && qt == 0 && h == 0 && threadIdx.x == 0) a.len[b] = Tn;
@@ -819,8 +826,10 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
       const int key = k0 + r;
       float kx = 0.f, vx = 0.f;
       if (key < off + Tn) {
-        kx = kb[(size_t)key * D + d];
-        vx = vb[(size_t)key * D + d];
+        const size_t rk = a.table ? paged_row(a.table, b, a.max_blocks, a.block_log2, a.kv_heads, g, key)
+                                  : (size_t)key;
+        kx = kb[rk * D + d];
+        vx = vb[rk * D + d];
         if (a.write_cache && writer && key >= q0) {
           // bit copy: reinterpret, never round
           ((uint32_t *)ckb)[(size_t)key * D + d] = __float_as_uint(kx);
@@ -930,9 +939,15 @@ template <typename T, int D>
 static hipError_t launch_extend_mfma(const PrefillArgs &a, hipStream_t s) {
   constexpr int NW = 4, QW = 32, BN = D == 32 ? 128 : 64, BM = NW * QW;
   const int n_qt = (a.T + BM - 1) / BM;
+  const dim3 grid((unsigned)n_qt * a.batch * a.q_heads);
+  if (a.table) {
+    static std::atomic<uint64_t> attr_paged{0};
+    return launch_with_lds(prefill_mfma_kernel<T, D, QW, BN, NW, true>, grid, NW * 64, PrefillLds<D, BN>::BYTES, s,
+                           attr_paged, a);
+  }
   static std::atomic<uint64_t> attr_done{0};
-  return launch_with_lds(prefill_mfma_kernel<T, D, QW, BN, NW>, dim3((unsigned)n_qt * a.batch * a.q_heads),
-                         NW * 64, PrefillLds<D, BN>::BYTES, s, attr_done, a);
+  return launch_with_lds(prefill_mfma_kernel<T, D, QW, BN, NW>, grid, NW * 64, PrefillLds<D, BN>::BYTES, s,
+                         attr_done, a);
 }
 
 hipError_t launch_extend_attention(const PrefillArgs &a, hipStream_t s) {

@@ -9,6 +9,7 @@ from .attention import (  # noqa: F401
     decode_paged,
     decode_recompute,
     extend,
+    extend_paged,
     kv_bytes,
     kv_head_of,
     naive_causal,

@@ -431,6 +431,19 @@ class PagedCacheModel:
             self._write(layer, s, int(self.lengths[layer, s]), k_new[s, :, 0], v_new[s, :, 0])
         self.lengths[layer] += 1
 
+    def extend(self, layer, k_new, v_new):
+        """T rows per slot (k_new/v_new (slots, Hkv, T, D)) written at logical
+        positions [len, len + T) of each slot, then len += T."""
+        T = k_new.shape[2]
+        for s in range(len(self.tables)):
+            if self.lengths[layer, s] + T > self.capacity(s):
+                raise RuntimeError("slot full")
+        for s in range(len(self.tables)):
+            L = int(self.lengths[layer, s])
+            for t in range(T):
+                self._write(layer, s, L + t, k_new[s, :, t], v_new[s, :, t])
+        self.lengths[layer] += T
+
     def set_lengths(self, layer, lengths):
         lengths = np.asarray(lengths, dtype=np.int64)
         for s, L in enumerate(lengths):
@@ -452,15 +465,33 @@ class PagedCacheModel:
 
 
 def decode_paged(q: np.ndarray, model: PagedCacheModel, layer: int, scale: float, dtype: str,
-                 to_f64) -> np.ndarray:
+                 to_f64, window: int = 0, sink: int = 0) -> np.ndarray:
     """Decode step over a paged cache: each slot's rows gathered in logical
-    order, then the contiguous decode (``decode_cached``).  ``to_f64`` widens
-    the raw storage values (bf16 bits included) to float64."""
+    order, then the contiguous decode (``decode_cached``, with the same window
+    and sink).  ``to_f64`` widens the raw storage values (bf16 bits included)
+    to float64."""
     q = np.asarray(q, dtype=np.float64)
     B, H, D = q.shape
     out = np.empty((B, H, D), dtype=np.float64)
     for s in range(B):
         kg, vg = model.gather(layer, s)
         L = kg.shape[1]
-        out[s:s + 1] = decode_cached(q[s:s + 1], to_f64(kg[None], dtype), to_f64(vg[None], dtype), [L], scale)
+        out[s:s + 1] = decode_cached(q[s:s + 1], to_f64(kg[None], dtype), to_f64(vg[None], dtype), [L], scale,
+                                     window, sink)
+    return out
+
+
+def extend_paged(q_new: np.ndarray, model: PagedCacheModel, layer: int, scale: float, dtype: str,
+                 to_f64, window: int = 0, sink: int = 0) -> np.ndarray:
+    """Extend over a paged cache, after ``model.extend`` has written the T new
+    rows: each slot's rows gathered in logical order, then ``extend`` with
+    the slot's prefix length len - T as its offset."""
+    q_new = np.asarray(q_new, dtype=np.float64)
+    B, H, T, D = q_new.shape
+    out = np.empty((B, H, T, D), dtype=np.float64)
+    for s in range(B):
+        kg, vg = model.gather(layer, s)
+        off = kg.shape[1] - T
+        out[s:s + 1] = extend(q_new[s:s + 1], to_f64(kg[None], dtype), to_f64(vg[None], dtype), [off], scale,
+                              window, sink)
     return out

@@ -440,6 +440,51 @@ def check_paged_prefix_sharing(PagedCacheModel=oracle.PagedCacheModel, decode_pa
     assert not shared.k[0, [1, 3]].any(), "shared prefix was written twice"
 
 
+def check_paged_extend_and_window(PagedCacheModel=oracle.PagedCacheModel, extend_paged=oracle.extend_paged,
+                                  decode_paged=oracle.decode_paged, dtype="f16"):
+    """Ragged extends (rollback to lengths 5, 2, 7, then 6 new rows) through a
+    paged cache with permuted 4-position blocks and through the contiguous
+    cache model: the slots gather to the contiguous rows bit for bit; the
+    paged extend equals ``extend`` on the contiguous rows exactly, with and
+    without a window and sink; a windowed paged decode equals the windowed
+    contiguous decode exactly."""
+    storage = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
+    B, H, Hkv, D, T0, T, bs = 3, 4, 2, 8, 8, 6, 4
+    max_T = T0 + T + 1
+    nb = -(-max_T // bs)
+    rng = np.random.default_rng(331)
+    perm = rng.permutation(B * nb + 2)
+    tables = [list(perm[s * nb:(s + 1) * nb]) for s in range(B)]
+    kh = round_to(rng.standard_normal((B, Hkv, max_T, D)), dtype)
+    vh = round_to(rng.standard_normal((B, Hkv, max_T, D)), dtype)
+    qn = round_to(rng.standard_normal((B, H, T, D)), dtype)
+    qd = round_to(rng.standard_normal((B, H, D)), dtype)
+    base = [5, 2, 7]
+    for W, S in ((0, 0), (4, 2)):
+        paged = PagedCacheModel(1, B, B * nb + 2, bs, Hkv, D, storage)
+        for s in range(B):
+            paged.set_blocks(s, tables[s])
+        flat = oracle.CacheModel(1, B, Hkv, D, max_T, storage)
+        for c in (paged, flat):
+            c.prefill(0, kh[:, :, :T0], vh[:, :, :T0])
+            c.set_lengths(0, base)
+        kn = np.stack([kh[s, :, base[s]:base[s] + T] for s in range(B)])
+        vn = np.stack([vh[s, :, base[s]:base[s] + T] for s in range(B)])
+        for c in (paged, flat):
+            c.extend(0, kn, vn)
+        for s in range(B):
+            kg, vg = paged.gather(0, s)
+            L = base[s] + T
+            assert np.array_equal(kg, flat.k[0, s, :, :L]) and np.array_equal(vg, flat.v[0, s, :, :L])
+        got = extend_paged(to_f64(qn, dtype), paged, 0, 0.3, dtype, to_f64, W, S)
+        ref = oracle.extend(to_f64(qn, dtype), to_f64(flat.k[0], dtype), to_f64(flat.v[0], dtype), base, 0.3, W, S)
+        assert np.array_equal(got, ref), f"paged extend differs (window {W}, sink {S})"
+        got = decode_paged(to_f64(qd, dtype), paged, 0, 0.3, dtype, to_f64, W, S)
+        ref = oracle.decode_cached(to_f64(qd, dtype), to_f64(flat.k[0], dtype), to_f64(flat.v[0], dtype),
+                                   flat.lengths[0], 0.3, W, S)
+        assert np.array_equal(got, ref), f"paged decode differs (window {W}, sink {S})"
+
+
 ALL_CHECKS = [
     check_kv_bytes, check_brute, check_row0_is_v0, check_zero_query_prefix_mean,
     check_two_key_logistic, check_rows_sum_to_one, check_large_scores, check_causality,
@@ -448,5 +493,5 @@ ALL_CHECKS = [
     check_extend_matches_prefill_rows, check_chunked_prefill_by_extend, check_extend_brute,
     check_window_special_cases, check_window_brute, check_window_decode_and_extend_rows,
     check_window_ignores_hidden_keys, check_paged_addressing, check_paged_equals_contiguous,
-    check_paged_prefix_sharing,
+    check_paged_prefix_sharing, check_paged_extend_and_window,
 ]

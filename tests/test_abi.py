@@ -177,6 +177,10 @@ def test_paged_calls_reject_null_object_without_a_device():
     assert lib.kvattn_paged_prefill(None, 0, p, p, p, p, 8, 0.1, 1, None) == -1
     assert lib.kvattn_paged_append(None, 0, p, p, None) == -1
     assert lib.kvattn_paged_decode(None, 0, p, p, 0.1, 1, None) == -1
+    assert lib.kvattn_paged_extend(None, 0, p, p, p, p, 4, 0.1, 1, None) == -1
+    assert lib.kvattn_paged_set_window(None, 0, 64, 4) == -1
+    w, sk = ctypes.c_int(), ctypes.c_int()
+    assert lib.kvattn_paged_get_window(None, 0, ctypes.byref(w), ctypes.byref(sk)) == -1
     assert lib.kvattn_paged_set_blocks(None, 0, (ctypes.c_int32 * 1)(0), 1, None) == -1
     assert lib.kvattn_paged_set_lengths(None, 0, (ctypes.c_int32 * 1)(0), None) == -1
     assert lib.kvattn_paged_get_lengths(None, 0, (ctypes.c_int32 * 1)()) == -1

@@ -134,6 +134,9 @@ def _run_all(overrides):
             overrides.get("PagedCacheModel", oracle.PagedCacheModel), oracle.decode_paged, oracle.CacheModel),
         "check_paged_prefix_sharing": lambda: pins.check_paged_prefix_sharing(
             overrides.get("PagedCacheModel", oracle.PagedCacheModel), oracle.decode_paged),
+        "check_paged_extend_and_window": lambda: pins.check_paged_extend_and_window(
+            overrides.get("PagedCacheModel", oracle.PagedCacheModel),
+            overrides.get("extend_paged", oracle.extend_paged), overrides.get("decode_paged", oracle.decode_paged)),
     }
     with np.errstate(all="ignore"):
         for name, fn in calls.items():
@@ -171,6 +174,24 @@ def _extend_visible(count):
                     out[b, h, t] = oracle.attend_row(q_new[b, h, t], ck[b, g, :n], cv[b, g, :n], scale)
         return out
     return f
+
+
+def _extend_paged_offset(shift):
+    """extend_paged taking each slot's prefix as len - T + shift."""
+    def f(q_new, model, layer, scale, dtype, to_f64, window=0, sink=0):
+        B, H, T, D = q_new.shape
+        out = np.empty((B, H, T, D))
+        for s in range(B):
+            kg, vg = model.gather(layer, s)
+            off = min(max(kg.shape[1] - T + shift, 0), kg.shape[1] - T)
+            out[s:s + 1] = oracle.extend(q_new[s:s + 1], to_f64(kg[None], dtype), to_f64(vg[None], dtype),
+                                         [off], scale, window, sink)
+        return out
+    return f
+
+
+def _decode_paged_window_dropped(q, model, layer, scale, dtype, to_f64, window=0, sink=0):
+    return oracle.decode_paged(q, model, layer, scale, dtype, to_f64)
 
 
 def _paged_variant(where):
@@ -223,6 +244,9 @@ MUTANTS.update({
         lambda m, slot, pos: (m.tables[slot][pos % len(m.tables[slot])], (pos // len(m.tables[slot])) % m.block_size))},
     "paged_block_off_by_one": {"PagedCacheModel": _paged_variant(
         lambda m, slot, pos: (m.tables[slot][min((pos + 1) // m.block_size, len(m.tables[slot]) - 1)], pos % m.block_size))},
+    "paged_extend_offset_from_start": {"extend_paged": _extend_paged_offset(-99)},
+    "paged_extend_offset_one_short": {"extend_paged": _extend_paged_offset(-1)},
+    "paged_decode_window_dropped": {"decode_paged": _decode_paged_window_dropped},
     "window_not_causal": {"naive_windowed": _windowed_variant(
         lambda i, j, W, S: W <= 0 and j <= i or W > 0 and (abs(i - j) < W or j < S))},
 })
