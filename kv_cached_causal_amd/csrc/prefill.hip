@@ -522,24 +522,30 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
   const int v_kg = stid % (BN / 4);
   const int v_ds = stid / (BN / 4);
 
-  // ---- staging: global -> registers (keys past T clamped, masked later) -> LDS (+ cache rows)
+  // ---- staging: global -> registers (keys past T read as zeros, masked later) -> LDS (+ cache rows)
+  // Buffer loads over this (b, KV head)'s T x D slab: the per-tile offset is
+  // scalar and keys past T read as zeros (the range check of the buffer
+  // resource; they are masked in the scores and weigh 0 in P V), so the
+  // loads need no clamps and no 64-bit address arithmetic.
+  const int slab_bytes = Tn * D * (int)sizeof(T);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, slab_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, slab_bytes, 0x00020000);
+  const int k_voff = ((stid / (D / 8)) * D + (stid % (D / 8)) * 8) * (int)sizeof(T);
+  const int v_voff = ((4 * v_kg) * D + v_ds * 8) * (int)sizeof(T);
   auto load_k = [&](int t) {
     if (stage_k) {
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
-        const int idx = c * 256 + stid;
-        const int key = min(t * BN + idx / (D / 8), Tn - 1);
-        kreg[c] = *(const u32x4 *)(kb + (size_t)key * D + (idx % (D / 8)) * 8);
+        const int soff = (t * BN + c * (256 / (D / 8))) * D * (int)sizeof(T);
+        kreg[c] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff, soff, 0);
       }
     }
   };
   auto load_v = [&](int t) {
     if (stage_v) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = min(t * BN + 4 * v_kg + r, Tn - 1);
-        vreg[r] = *(const u32x4 *)(vb + (size_t)key * D + v_ds * 8);
-      }
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + r * D * (int)sizeof(T), t * BN * D * (int)sizeof(T), 0);
     }
   };
   auto store_k = [&](int t, int slot) {
@@ -917,7 +923,9 @@ static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)n_qt * a.batch * a.q_heads);
   static std::atomic<uint64_t> attr_done{0};
   if constexpr (C::kPipe) {
-    if (a.window > 0) return launch_extend_mfma<T, D>(a, s);  // the plain kernel takes the window mask
+    // the plain kernel takes the window mask, and prompts whose K/V slab does
+    // not fit the 32-bit range of the pipelined kernel's buffer loads
+    if (a.window > 0 || (size_t)a.T * D * sizeof(T) >= ((size_t)1 << 31)) return launch_extend_mfma<T, D>(a, s);
     return launch_with_lds(prefill_pipe_kernel<T, D, C::QW, C::BN, C::NW>, grid, C::NW * 64,
                            PipeLds<D, C::BN>::BYTES, s, attr_done, a);
   } else {
