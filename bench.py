@@ -156,6 +156,28 @@ def measure_read_ceiling(kv, dev, nbytes=CALIB_BYTES, reps=10):
     return rate
 
 
+def measure_mfma_ceiling(kv, dev, workgroups=1024, iters=20000, reps=5):
+    """fp16 MFMA rate of this device (plain matrix-core loop of the library), TFLOP/s."""
+    import ctypes
+    sink = torch.zeros(workgroups, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    fn = kv.lib().kvattn_measure_mfma_f16
+
+    def run():
+        if fn(workgroups, iters, ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+            raise RuntimeError("kvattn_measure_mfma_f16 failed")
+    for _ in range(3):
+        run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    flops = kv.lib().kvattn_measure_mfma_f16_flops(workgroups, iters)
+    return flops / (a.elapsed_time(b) / reps * 1e-3) / 1e12
+
+
 def calibration_kernels(kv, dev):
     """A plain read and a fill of CALIB_BYTES each (run under --pmc to calibrate the HBM counters)."""
     import ctypes
@@ -689,6 +711,10 @@ def main():
         out["hbm_read_ceiling"] = {"value": round(ceil, 1), "unit": "GB/s", "kernel": "kvattn_measure_stream_read",
                                    "bytes": CALIB_BYTES,
                                    "decode_frac_of_ceiling": round(out["roofline"]["achieved"] / ceil, 4)}
+        mceil = measure_mfma_ceiling(kv, dev)
+        out["mfma_f16_ceiling"] = {"value": round(mceil, 1), "unit": "TFLOP/s", "kernel": "kvattn_measure_mfma_f16",
+                                   "prefill_frac_of_ceiling":
+                                       round(out["prefill"]["roofline"]["achieved"] / mceil, 4)}
     if args.calibrate:
         calibration_kernels(kv, dev)
     if not args.no_cpu_baseline:

@@ -2,10 +2,11 @@
  * kvattn_measure.h -- a measurement aid shipped with libkvattn; not part of
  * the attention path.
  *
- * The decode kernels are bounded by HBM bandwidth.  Besides the published
- * peak, the benchmark reports the streaming-read rate this device actually
- * sustains, measured with the plain read kernel below, so that the decode
- * rate can be read against both.
+ * The decode kernels are bounded by HBM bandwidth and the prefill kernel by
+ * the matrix cores.  Besides the published peaks, the benchmark reports the
+ * streaming-read rate and the fp16 MFMA rate this device actually sustains,
+ * measured with the plain kernels below, so that each kernel's rate can be
+ * read against both.
  */
 #ifndef KVATTN_MEASURE_H
 #define KVATTN_MEASURE_H
@@ -27,6 +28,22 @@ extern "C" {
  * launch fails.  Time it with events on the same stream. */
 int kvattn_measure_stream_read(const void *buf, size_t bytes, int workgroups, uint32_t *sink,
                                void *stream);
+
+/* Enqueue on `stream` a plain matrix-core loop: `workgroups` workgroups of four
+ * waves, each wave running `iters` rounds of eight independent chains of
+ * v_mfma_f32_16x16x32_f16 (fp16 inputs, fp32 accumulation) on register
+ * operands, with no memory traffic in the loop.  The sums are written to
+ * sink[blockIdx] (a device array of at least `workgroups` floats) only if
+ * they equal an unlikely constant.  Returns 0, KVATTN_ERR_INVALID_ARG (-1) or
+ * KVATTN_ERR_HIP (-6).  Time it with events on the same stream and divide
+ * kvattn_measure_mfma_f16_flops(workgroups, iters) by the time: the fp16
+ * MFMA rate the device sustains (the prefill kernel's matrix work is of this
+ * instruction). */
+int kvattn_measure_mfma_f16(int workgroups, int iters, float *sink, void *stream);
+
+/* Floating-point operations of one such launch (0 for a non-positive
+ * argument).  Pure host function. */
+double kvattn_measure_mfma_f16_flops(int workgroups, int iters);
 
 #ifdef __cplusplus
 }

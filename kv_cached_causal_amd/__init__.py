@@ -85,6 +85,8 @@ _SIGS = {
     "kvattn_model_generate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 3),
     "kvattn_model_last_error": (ctypes.c_char_p, []),
     "kvattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kvattn_measure_mfma_f16": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
+    "kvattn_measure_mfma_f16_flops": (ctypes.c_double, [ctypes.c_int, ctypes.c_int]),
     "kvattn_measure_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                                   ctypes.c_void_p]),
     "kvattn_last_error": (ctypes.c_char_p, []),

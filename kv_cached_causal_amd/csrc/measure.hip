@@ -1,5 +1,7 @@
-// Measurement aid: a plain streaming-read kernel, used to report the HBM read
-// rate the device sustains next to the decode kernels' rate.
+// Measurement aids: a plain streaming-read kernel, used to report the HBM read
+// rate the device sustains next to the decode kernels' rate, and a plain
+// matrix-core loop, used to report the fp16 MFMA rate it sustains next to the
+// prefill kernel's rate.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -25,7 +27,43 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restric
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
 }
 
+// Each wave runs `iters` rounds of NCH independent accumulation chains of
+// v_mfma_f32_16x16x32_f16 on register operands (no memory traffic in the
+// loop); enough independent chains keep the matrix pipeline full.
+constexpr int kMfmaChains = 8;
+__global__ __launch_bounds__(256, 2) void mfma_loop_kernel(int iters, float *sink) {
+  const _Float16 x = (_Float16)(1.0f + (float)(threadIdx.x & 7) * 0.0078125f);
+  half8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = x;
+    b[i] = (_Float16)(0.5f) - x * (_Float16)(0.001f * (float)i);
+  }
+  float4_t acc[kMfmaChains];
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c) r += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  if (r == 1234.5f) sink[blockIdx.x] = r;
+}
+
 }  // namespace kvattn
+
+extern "C" int kvattn_measure_mfma_f16(int workgroups, int iters, float *sink, void *stream) {
+  if (!sink || workgroups <= 0 || iters <= 0) return KVATTN_ERR_INVALID_ARG;
+  kvattn::mfma_loop_kernel<<<dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream>>>(iters, sink);
+  return hipGetLastError() == hipSuccess ? KVATTN_OK : KVATTN_ERR_HIP;
+}
+
+extern "C" double kvattn_measure_mfma_f16_flops(int workgroups, int iters) {
+  if (workgroups <= 0 || iters <= 0) return 0.0;
+  return (double)workgroups * 4 /* waves */ * iters * kvattn::kMfmaChains * (16.0 * 16.0 * 32.0 * 2.0);
+}
 
 extern "C" int kvattn_measure_stream_read(const void *buf, size_t bytes, int workgroups, uint32_t *sink,
                                           void *stream) {

@@ -117,6 +117,17 @@ def test_status_strings():
     assert lib.kvattn_status_string(-99) == b"unknown status"
 
 
+def test_measure_mfma_validates_on_host_and_counts_flops():
+    lib = kv.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.kvattn_measure_mfma_f16(0, 10, fake, None) == -1
+    assert lib.kvattn_measure_mfma_f16(8, 0, fake, None) == -1
+    assert lib.kvattn_measure_mfma_f16(8, 10, None, None) == -1
+    # 4 waves x 8 chains x 16*16*32 multiply-adds per round
+    assert lib.kvattn_measure_mfma_f16_flops(3, 5) == 3 * 4 * 5 * 8 * 16 * 16 * 32 * 2
+    assert lib.kvattn_measure_mfma_f16_flops(0, 5) == 0.0
+
+
 def test_measure_stream_read_validates_on_host():
     lib = kv.lib()
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation first
