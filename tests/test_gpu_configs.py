@@ -122,7 +122,7 @@ def test_config3_8_layers_prompt4096_then_128_steps():
 
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_long_prefill_8192(cfg):
-    """B=1 causal prefill at T=8192 (config 3: H=16, D=32; config 5: H=32, D=128,
+    """B=1 causal prefill at T=8192 (8-layer H=16, D=32 workload; 32-layer H=32, D=128 workload,
     1% heavy keys), on layers 0 and 31 of the full cache; no T x T buffer."""
     kv = _kv()
     w = si.WORKLOADS[cfg]
@@ -155,7 +155,7 @@ def test_long_prefill_8192(cfg):
 
 @pytest.mark.parametrize("cfg", [4, 5])
 def test_batched_long_context_decode(cfg):
-    """Config 4 (bf16 GQA 32/8, B=16, context 4096) and config 5 (fp16 MHA, B=32,
+    """The bf16 GQA 32/8 workload (B=16, context 4096) and the fp16 MHA workload (B=32,
     ragged contexts in [512, 4096], 1% heavy keys): the full 32-layer cache, with
     layers 0 and 31 filled and checked over every (b, h); stale slots are NaN."""
     kv = _kv()

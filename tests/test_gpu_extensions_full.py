@@ -1,6 +1,6 @@
 """GPU parity of the extensions at the sizes bench.py times them.
 
-On one layer of config 5's decode shape (fp16, 32 heads of D=128, batch 32,
+On one layer of the batched ragged decode shape (fp16, 32 heads of D=128, batch 32,
 contexts uniform in [512, 4096], 1% heavy keys): decode under a 1024-key
 window with 4 sink positions, decode from a paged cache of 64-position blocks
 drawn from a shuffled pool, and a 4-token verification (extend) after rolling

@@ -166,7 +166,7 @@ def test_config1_end_to_end():
     against the cached oracle, the recompute oracle, and the GPU's own prefill row."""
     kv = _kv()
     w = si.WORKLOADS[1]
-    say(f"config 1 end to end: {w.name}")
+    say(f"fp32 workload end to end: {w.name}")
     T, S, dt = w.prompt, w.steps, w.dtype
     q, k, v = si.prefill_inputs(w, 0, T)
     steps = [si.decode_step_inputs(w, 0, s) for s in range(S)]
