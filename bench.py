@@ -65,6 +65,9 @@ def parse():
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="read the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE rocprofv3 run of "
                         "`bench.py --calibrate`, write profiles/traffic.json and exit (no GPU needed)")
+    p.add_argument("--trace-summary", nargs=2, metavar=("TRACE_CSV", "WARMUP_FRACTION"),
+                   help="summarise the kernel_trace.csv of a rocprofv3 --kernel-trace run: per library kernel, "
+                        "the dispatches after the first WARMUP_FRACTION of them (the warmup steps); print and exit")
     return p.parse_args()
 
 
@@ -575,8 +578,29 @@ def cpu_baseline():
     }
 
 
+def trace_summary(path, warm_frac):
+    """Per library kernel of a rocprofv3 kernel trace: dispatch count, mean and
+    median duration (us) over the dispatches after the first warm_frac of them."""
+    import csv
+    import statistics
+    durs = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if "kvattn" in r["Kernel_Name"]:
+                durs.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    for name, v in durs.items():
+        v.sort()
+        timed = [d for _, d in v[int(len(v) * warm_frac):]]
+        print(f"{name}\tdispatches={len(timed)}\tavg_us={statistics.mean(timed):.2f}\t"
+              f"median_us={statistics.median(timed):.2f}")
+
+
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary[0], float(args.trace_summary[1]))
+        return
     if args.traffic_from:
         write_traffic(*args.traffic_from)
         return
