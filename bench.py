@@ -85,9 +85,9 @@ PREFILL_SOURCES = ["prefill.hip", "common.hpp"]
 CALIB_BYTES = 4 << 30
 # kernels of each measured launch, by a substring of the demangled or mangled name
 TRAFFIC_KERNELS = {
-    "decode_ragged_b32": (DECODE_SOURCES, ["decode_kernel<kvattn::TagF16, 128, 1, 6, 1, 4, false>",
+    "decode_ragged_b32": (DECODE_SOURCES, ["decode_kernel<kvattn::TagF16, 128, 1, 6, 1, 4, false, false>",
                                            "decode_merge_kernel<128, 1>"]),
-    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4, 4, 1, 4, false>",
+    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4, 4, 1, 4, false, false>",
                                         "decode_merge_kernel<128, 4>"]),
     "prefill_t8192": (PREFILL_SOURCES, ["prefill_pipe_kernelIDF16_Li128"]),
 }

@@ -38,10 +38,10 @@ struct AppendArgs {
 struct DecodeArgs {
   const void *k_layer;  // (B, Hkv, max_T, D)
   const void *v_layer;
-  const void *q;        // (B, H, 1, D)
-  void *o;              // (B, H, 1, D) in o_dtype
-  float *ws;            // (B, H, n_splits, D + 2) fp32: m (log2 domain), l, u[D]
-  const int32_t *len;   // layer's lengths [B]
+  const void *q;        // (B, H, tokens, D)
+  void *o;              // (B, H, tokens, D) in o_dtype
+  float *ws;            // (B, H * tokens, n_splits, D + 2) fp32: m (log2 domain), l, u[D]
+  const int32_t *len;   // layer's lengths [B] (after the tokens' own rows were added)
   int batch, q_heads, kv_heads, head_dim, max_T, chunk, n_splits;
   int window, sink;     // sliding window (0: none) and attention-sink positions
   float scale_log2;     // scale * log2(e)
@@ -49,7 +49,22 @@ struct DecodeArgs {
   // paged cache (as in AppendArgs); null table for the contiguous cache
   const int32_t *table;
   int block_log2, max_blocks;
+  // query positions per sequence: 1 for decode; T for the short extend
+  // (multi-token verification), whose token t sits at position len - T + t
+  // and sees the keys up to it (no window)
+  int tokens = 1;
 };
+
+// the longest extend served by the decode kernels (its workspace is sized
+// for this many query positions per head)
+constexpr int kMaxVerifyTokens = 8;
+// An extend of T positions over a cache with G query heads per KV head runs
+// on the decode kernels when one workgroup can hold all G * T query rows of a
+// KV head (the instantiated row counts 2, 3, 4, 8) and no window is set.
+inline bool verify_on_decode(int G, int T, int window) {
+  const int r = G * T;
+  return T >= 2 && T <= kMaxVerifyTokens && window == 0 && (r == 2 || r == 3 || r == 4 || r == 8);
+}
 
 // Row index (in rows of D elements) of position `pos` of KV head g of
 // sequence b in a paged pool [num_blocks][Hkv][2^block_log2][D].

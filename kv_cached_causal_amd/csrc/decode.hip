@@ -102,7 +102,13 @@ __device__ __forceinline__ void store_out(void *o, size_t idx, float x, kvattn_d
 // `chunk` keys of one KV head, for GT query heads of its group.  LPR lanes
 // share one key row, each holding NV 16-byte slices of it (columns cl + v *
 // LPR * EPL), so one load instruction reads RPW whole rows.
-template <class Tag, int D, int GT, int U, int NV, int NW, bool PAGED>
+//
+// VER (the short extend, `tokens` = T > 1 query positions per head): the
+// query rows of a KV head are its G heads x T tokens, GT = G * T of them per
+// workgroup (grid (n_splits, Hkv, B)); token t sits at position L - T + t and
+// its scores past that position are masked, so each K/V byte is still read
+// once for all G * T rows.
+template <class Tag, int D, int GT, int U, int NV, int NW, bool PAGED, bool VER = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   constexpr int EPL = Tag::EPL;
   constexpr int LPR = D / (EPL * NV);  // lanes that share one key row
@@ -114,11 +120,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
   const int b = blockIdx.z;
   const int split = blockIdx.x;
-  const int G = a.q_heads / a.kv_heads;
-  const int subs = G / GT;
-  const int unit = blockIdx.y;  // (kv head, sub-group of GT query heads)
+  const int TK = VER ? a.tokens : 1;       // query positions per head
+  const int RS = a.q_heads * TK;            // query rows per sequence: (head, token)
+  const int RK = (a.q_heads / a.kv_heads) * TK;  // query rows per KV head
+  const int subs = RK / GT;
+  const int unit = blockIdx.y;  // (kv head, sub-group of GT query rows)
   const int kvh = unit / subs;
-  const int h0 = kvh * G + (unit - kvh * subs) * GT;
+  const int h0 = kvh * RK + (unit - kvh * subs) * GT;  // first query row
   // splits run over the visible keys (all L, or the sink and window ones)
   const VisibleKeys vk = visible_keys(a.len[b], a.window, a.sink);
   const int kb = split * a.chunk;  // first visible index of this split
@@ -165,7 +173,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int v = 0; v < NV; ++v)
       qv[g][v] = *(const uint4 *)((const char *)a.q +
-                                  ((size_t)(b * a.q_heads + h0 + g) * D + cl + v * VSTRIDE) * ESZ);
+                                  ((size_t)(b * RS + h0 + g) * D + cl + v * VSTRIDE) * ESZ);
+  // VER: the last key row (relative to this split) that query row g sees
+  int last_rel[VER ? GT : 1];
+  if constexpr (VER) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) last_rel[g] = vk.count - TK + (h0 + g) % TK - kb;
+  }
 
   // m: the row's reference point (log2 units), raised only when a score
   // exceeds it by more than kLazyMax, so P = exp2(s - m) <= 2^kLazyMax and the
@@ -217,14 +231,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     float sc[U][GT];  // raw q.k; the scale is applied inside the exponent
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool ok = ((ib * U + u) * NW + wave) * RPW + rg < rows;
+      const int r = ((ib * U + u) * NW + wave) * RPW + rg;
+      const bool ok = r < rows;
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
         float d = dot16(Tag{}, qv[g][0], kr[u][0]);
 #pragma unroll
         for (int v = 1; v < NV; ++v) d += dot16(Tag{}, qv[g][v], kr[u][v]);
         d = row_sum<LPR>(d);
-        sc[u][g] = ok ? d : -INFINITY;
+        if constexpr (VER)
+          sc[u][g] = ok && r <= last_rel[g] ? d : -INFINITY;
+        else
+          sc[u][g] = ok ? d : -INFINITY;
       }
     }
     float mx[GT];
@@ -334,7 +352,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         num = fmaf(al, s_acc[w][g][d], num);
         den = fmaf(al, s_l[w][g], den);
       }
-      store_out(a.o, (size_t)(b * a.q_heads + h0 + g) * D + d, num / den, a.o_dt);
+      store_out(a.o, (size_t)(b * RS + h0 + g) * D + d, num / den, a.o_dt);
     }
     return;
   }
@@ -346,14 +364,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     float M = s_m[0][g];
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
+    // VER: a token may see no key of this split (all its scores masked); it
+    // then contributes (-inf, 0, 0)
+    const float Ms = (VER && M == -INFINITY) ? 0.f : M;
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float al = fast_exp2(s_m[w][g] - M);
+      const float al = fast_exp2(s_m[w][g] - Ms);
       num = fmaf(al, s_acc[w][g][d], num);
       den = fmaf(al, s_l[w][g], den);
     }
-    float *dst = a.ws + ((size_t)(b * a.q_heads + h0 + g) * a.n_splits + split) * (D + 2);
+    float *dst = a.ws + ((size_t)(b * RS + h0 + g) * a.n_splits + split) * (D + 2);
     dst[2 + d] = num;
     if (d == 0) {
       dst[0] = M;
@@ -382,14 +403,15 @@ __global__ __launch_bounds__((merge_threads<D, GT>())) void decode_merge_kernel(
   static_assert(E * THREADS == GT * D, "outputs split evenly");
   constexpr int SB = 8;                // splits per round of loads
   const int b = blockIdx.y;
-  const int G = a.q_heads / a.kv_heads;
-  const int subs = G / GT;
+  const int RS = a.q_heads * a.tokens;                 // query rows per sequence
+  const int RK = (a.q_heads / a.kv_heads) * a.tokens;  // query rows per KV head
+  const int subs = RK / GT;
   const int unit = blockIdx.x;
   const int kvh = unit / subs;
-  const int h0 = kvh * G + (unit - kvh * subs) * GT;
+  const int h0 = kvh * RK + (unit - kvh * subs) * GT;
   const int ns = (visible_keys(a.len[b], a.window, a.sink).count + a.chunk - 1) / a.chunk;
   if (ns <= 1) return;
-  const float *ws_unit = a.ws + (size_t)(b * a.q_heads + h0) * a.n_splits * (D + 2);
+  const float *ws_unit = a.ws + (size_t)(b * RS + h0) * a.n_splits * (D + 2);
 
   float M[E], num[E], den[E];
 #pragma unroll
@@ -437,11 +459,11 @@ __global__ __launch_bounds__((merge_threads<D, GT>())) void decode_merge_kernel(
     const int t = e * THREADS + (int)threadIdx.x;
     const int g = t / D;
     const int d = t - g * D;
-    store_out(a.o, (size_t)(b * a.q_heads + h0 + g) * D + d, num[e] / den[e], a.o_dt);
+    store_out(a.o, (size_t)(b * RS + h0 + g) * D + d, num[e] / den[e], a.o_dt);
   }
 }
 
-template <class Tag, int D, int GT, bool PAGED>
+template <class Tag, int D, int GT, bool PAGED, bool VER>
 static hipError_t launch_gt_layout(const DecodeArgs &a, hipStream_t s) {
   // 16-byte K and V loads per lane per batch (two batches are in flight):
   // six for one to three query heads per workgroup, four for larger groups
@@ -453,23 +475,33 @@ static hipError_t launch_gt_layout(const DecodeArgs &a, hipStream_t s) {
   // left the time unchanged).
   constexpr int NV = 1, NW = 4;
   constexpr int U = GT >= 4 ? 4 : 6;
-  const int units = a.q_heads / GT;  // = Hkv * (G / GT)
-  decode_kernel<Tag, D, GT, U, NV, NW, PAGED><<<dim3(a.n_splits, units, a.batch), NW * 64, 0, s>>>(a);
+  const int units = a.q_heads * a.tokens / GT;  // = Hkv * (G * tokens / GT)
+  decode_kernel<Tag, D, GT, U, NV, NW, PAGED, VER><<<dim3(a.n_splits, units, a.batch), NW * 64, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
   decode_merge_kernel<D, GT><<<dim3(units, a.batch), merge_threads<D, GT>(), 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <class Tag, int D, int GT>
+template <class Tag, int D, int GT, bool VER = false>
 static hipError_t launch_gt(const DecodeArgs &a, hipStream_t s) {
-  if (a.table) return launch_gt_layout<Tag, D, GT, true>(a, s);
-  return launch_gt_layout<Tag, D, GT, false>(a, s);
+  if (a.table) return launch_gt_layout<Tag, D, GT, true, VER>(a, s);
+  return launch_gt_layout<Tag, D, GT, false, VER>(a, s);
 }
 
 template <class Tag, int D>
 static hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
   const int G = a.q_heads / a.kv_heads;
+  if (a.tokens > 1) {
+    // short extend: one workgroup per KV head and split holds all G * T rows
+    switch (G * a.tokens) {
+      case 8: return launch_gt<Tag, D, 8, true>(a, s);
+      case 4: return launch_gt<Tag, D, 4, true>(a, s);
+      case 3: return launch_gt<Tag, D, 3, true>(a, s);
+      case 2: return launch_gt<Tag, D, 2, true>(a, s);
+      default: return hipErrorInvalidValue;  // the host routes other shapes to the prefill kernels
+    }
+  }
   const int GT = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 3 == 0) ? 3 : (G % 2 == 0) ? 2 : 1;
   switch (GT) {
     case 8: return launch_gt<Tag, D, 8>(a, s);

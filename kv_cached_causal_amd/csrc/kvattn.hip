@@ -129,7 +129,9 @@ int kvattn_cache_alloc(kvattn_cache **out, int layers, int batch, int q_heads, i
     c->owns_base = true;
   }
   const size_t len_bytes = sizeof(int32_t) * (size_t)layers * batch;
-  const size_t ws_bytes = sizeof(float) * (size_t)batch * q_heads * c->n_splits * (head_dim + 2);
+  // split-K workspace for decode and for the short extends run on the decode
+  // kernels (up to kMaxVerifyTokens query positions per head)
+  const size_t ws_bytes = sizeof(float) * (size_t)batch * q_heads * kMaxVerifyTokens * c->n_splits * (head_dim + 2);
   e = hipMalloc((void **)&c->d_len, len_bytes);
   if (e == hipSuccess) e = hipMalloc((void **)&c->d_ws, ws_bytes);
   if (e == hipSuccess) e = hipMemset(c->d_len, 0, len_bytes);
@@ -288,6 +290,42 @@ int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, cons
   cp.T = T;
   hipError_t e = launch_extend_copy(cp, st);
   if (e != hipSuccess) return hip_fail(e, "extend copy launch");
+
+  const int G = c->q_heads / c->kv_heads;
+  if (T == 1 || verify_on_decode(G, T, c->window[layer])) {
+    // short extend (one decode step, or a multi-token verification): commit
+    // the lengths first, then the decode kernels with T query positions per
+    // head, token t at position len[b] - T + t
+    e = launch_add_lengths(len, c->batch, T, st);
+    if (e != hipSuccess) return hip_fail(e, "extend length update launch");
+    DecodeArgs d;
+    d.k_layer = layer_k(c, layer);
+    d.v_layer = layer_v(c, layer);
+    d.q = q;
+    d.o = o;
+    d.ws = c->d_ws;
+    d.len = len;
+    d.batch = c->batch;
+    d.q_heads = c->q_heads;
+    d.kv_heads = c->kv_heads;
+    d.head_dim = c->head_dim;
+    d.max_T = c->max_T;
+    d.chunk = c->chunk;
+    d.n_splits = c->n_splits;
+    d.window = c->window[layer];
+    d.sink = c->sink[layer];
+    d.scale_log2 = scale * 1.4426950408889634f;
+    d.dt = c->dt;
+    d.o_dt = o_dtype;
+    d.table = nullptr;
+    d.block_log2 = 0;
+    d.max_blocks = 0;
+    d.tokens = T;
+    e = launch_decode(d, st);
+    if (e != hipSuccess) return hip_fail(e, "extend (decode form) launch");
+    for (int b = 0; b < c->batch; ++b) hl[b] += T;
+    return KVATTN_OK;
+  }
 
   // 2. attention of the T new queries over cache rows [0, len[b] + T)
   PrefillArgs a;
@@ -513,7 +551,7 @@ int kvattn_paged_alloc(kvattn_paged **out, int layers, int slots, int max_blocks
   }
   const size_t len_bytes = sizeof(int32_t) * (size_t)layers * slots;
   const size_t tab_bytes = sizeof(int32_t) * (size_t)slots * max_blocks;
-  const size_t ws_bytes = sizeof(float) * (size_t)slots * q_heads * p->n_splits * (head_dim + 2);
+  const size_t ws_bytes = sizeof(float) * (size_t)slots * q_heads * kMaxVerifyTokens * p->n_splits * (head_dim + 2);
   e = hipMalloc((void **)&p->d_len, len_bytes);
   if (e == hipSuccess) e = hipMalloc((void **)&p->d_table, tab_bytes);
   if (e == hipSuccess) e = hipMalloc((void **)&p->d_ws, ws_bytes);
@@ -751,6 +789,40 @@ int kvattn_paged_extend(kvattn_paged *p, int layer, const void *q, const void *k
   cp.max_blocks = p->max_blocks;
   hipError_t e = launch_extend_copy(cp, st);
   if (e != hipSuccess) return hip_fail(e, "paged extend copy launch");
+
+  const int G = p->q_heads / p->kv_heads;
+  if (T == 1 || verify_on_decode(G, T, p->window[layer])) {
+    // short extend on the decode kernels, as for the contiguous cache
+    e = launch_add_lengths(len, p->slots, T, st);
+    if (e != hipSuccess) return hip_fail(e, "paged extend length update launch");
+    DecodeArgs d;
+    d.k_layer = paged_k(p, layer);
+    d.v_layer = paged_v(p, layer);
+    d.q = q;
+    d.o = o;
+    d.ws = p->d_ws;
+    d.len = len;
+    d.batch = p->slots;
+    d.q_heads = p->q_heads;
+    d.kv_heads = p->kv_heads;
+    d.head_dim = p->head_dim;
+    d.max_T = p->max_blocks * p->block_size;
+    d.chunk = p->chunk;
+    d.n_splits = p->n_splits;
+    d.window = p->window[layer];
+    d.sink = p->sink[layer];
+    d.scale_log2 = scale * 1.4426950408889634f;
+    d.dt = p->dt;
+    d.o_dt = o_dtype;
+    d.table = p->d_table;
+    d.block_log2 = p->block_log2;
+    d.max_blocks = p->max_blocks;
+    d.tokens = T;
+    e = launch_decode(d, st);
+    if (e != hipSuccess) return hip_fail(e, "paged extend (decode form) launch");
+    for (int s = 0; s < p->slots; ++s) hl[s] += T;
+    return KVATTN_OK;
+  }
 
   // 2. attention of the T new queries over positions [0, len[b] + T), rows
   //    found through the block table

@@ -72,6 +72,49 @@ def test_extend_matches_oracle(dtype, D, heads, T):
     c.close()
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("D", [32, 128])
+@pytest.mark.parametrize("GT", [(1, 2), (1, 3), (1, 4), (1, 8), (2, 2), (2, 4), (4, 2)],
+                         ids=lambda x: f"G{x[0]}T{x[1]}")
+def test_short_extend_on_decode_kernels(dtype, D, GT):
+    """Extends of T = 2..8 positions whose G * T query rows fit one workgroup run
+    on the decode kernels (token t of a sequence sees the keys up to its own
+    position).  Prefix lengths put the new tokens on both sides of split
+    boundaries (384 / 512 / 1024 keys) and start one sequence empty."""
+    kv = _kv()
+    G, T = GT
+    Hkv = 2
+    H = G * Hkv
+    lengths = [0, 381, 510, 1022, 1500]
+    B = len(lengths)
+    max_T = max(lengths) + 2 * T + 3
+    say(f"short extend dtype={dtype} D={D} G={G} T={T}")
+    seed = 7000 + 100 * D + 10 * G + T
+    k_hist = _rand((B, Hkv, max_T, D), dtype, seed)
+    v_hist = _rand((B, Hkv, max_T, D), dtype, seed + 1)
+    q = _rand((B, H, T, D), dtype, seed + 2)
+    k_new = np.stack([k_hist[b, :, L:L + T] for b, L in enumerate(lengths)])
+    v_new = np.stack([v_hist[b, :, L:L + T] for b, L in enumerate(lengths)])
+    c = kv.KVCache(1, B, H, Hkv, D, max_T, TORCH_DT[dtype])
+    _fill_prefix(c, 0, k_hist, v_hist, dtype, lengths)
+    o = c.extend(0, to_dev(q, dtype), to_dev(k_new, dtype), to_dev(v_new, dtype), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    f = lambda a: si.to_f64(a, dtype)
+    ref = oracle.extend(f(q), f(k_hist), f(v_hist), lengths, float(np.float32(1.0 / np.sqrt(D))))
+    check_output(o, ref, dtype, "short extend")
+    assert c.lengths(0) == [L + T for L in lengths]
+    # the native output dtype too, and a second extend on top of the first
+    q2 = _rand((B, H, T, D), dtype, seed + 3)
+    k2 = np.stack([k_hist[b, :, L + T:L + 2 * T] for b, L in enumerate(lengths)])
+    v2 = np.stack([v_hist[b, :, L + T:L + 2 * T] for b, L in enumerate(lengths)])
+    o2 = c.extend(0, to_dev(q2, dtype), to_dev(k2, dtype), to_dev(v2, dtype))
+    torch.cuda.synchronize()
+    ref2 = oracle.extend(f(q2), f(k_hist), f(v_hist), [L + T for L in lengths], float(np.float32(1.0 / np.sqrt(D))))
+    check_output(o2, ref2, dtype, "second short extend, native dtype")
+    assert c.lengths(0) == [L + 2 * T for L in lengths]
+    c.close()
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_chunked_prefill_equals_one_shot(dtype):
     """A prompt fed through extend in uneven chunks equals one prefill (and the oracle)."""

@@ -199,13 +199,14 @@ def test_paged_prefix_sharing():
 @pytest.mark.parametrize("bs", [16, 64])
 def test_paged_extend_matches_oracle(dtype, bs):
     """Prefill 70 positions, roll the slots back to 70, 33 and 0, extend each
-    by 37 (crossing block boundaries; slot 2 starts empty, a prefill), then
-    extend by 5 more under a window: outputs match oracle.extend_paged, the
-    pool stays bit-identical to the model, and a windowed decode follows."""
+    by 37 (crossing block boundaries; slot 2 starts empty, a prefill), by 2
+    (on the decode kernels) and by 5 more under a window: outputs match
+    oracle.extend_paged, the pool stays bit-identical to the model, and a
+    windowed decode follows."""
     kv = _kv()
-    H, Hkv, D, T0, T1, T2 = 8, 2, 64, 70, 37, 5
+    H, Hkv, D, T0, T1, T2, T3 = 8, 2, 64, 70, 37, 2, 5
     slots = 3
-    nblk = -(-(T0 + T1 + T2) // bs)
+    nblk = -(-(T0 + T1 + T2 + T3) // bs)
     num_blocks = slots * nblk + 3
     say(f"paged extend dtype={dtype} bs={bs}")
     rng = np.random.default_rng(61 + bs)
@@ -224,7 +225,8 @@ def test_paged_extend_matches_oracle(dtype, bs):
     base = [70, 33, 0]
     c.set_lengths(base)
     model.set_lengths(0, base)
-    for T, (W, S), seed in ((T1, (0, 0), 65), (T2, (24, 3), 68)):
+    # 37 rows (prefill kernels), 2 rows (G * T = 8: the decode kernels), 5 rows under a window
+    for T, (W, S), seed in ((T1, (0, 0), 65), (T2, (0, 0), 75), (T3, (24, 3), 68)):
         c.set_window(W, S)
         q, kn, vn = (_rand((slots, n, T, D), dtype, seed + i) for i, n in enumerate((H, Hkv, Hkv)))
         o = c.extend(0, to_dev(q, dtype), to_dev(kn, dtype), to_dev(vn, dtype), out_dtype=torch.float32)
@@ -244,11 +246,13 @@ def test_paged_extend_matches_oracle(dtype, bs):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_paged_extend_equals_contiguous_bitwise(dtype):
+@pytest.mark.parametrize("heads", [(8, 2), (8, 8)], ids=lambda x: f"H{x[0]}kv{x[1]}")
+def test_paged_extend_equals_contiguous_bitwise(dtype, heads):
     """A 4-token verification after ragged prefixes, through shuffled 32-position
-    blocks and through a contiguous cache: bit-identical outputs."""
+    blocks and through a contiguous cache: bit-identical outputs (G = 4: the
+    prefill kernels; G = 1: the decode kernels' short-extend form)."""
     kv = _kv()
-    H, Hkv, D, bs, T = 8, 2, 128, 32, 4
+    (H, Hkv), D, bs, T = heads, 128, 32, 4
     lens = [5, 385, 999]
     slots = len(lens)
     nblk = -(-(max(lens) + T) // bs)
