@@ -161,6 +161,42 @@ def test_decode_matches_oracle(dtype, D, heads):
     c.close()
 
 
+@pytest.mark.parametrize("heads", [(4, 4), (4, 1)], ids=lambda x: f"H{x[0]}kv{x[1]}")
+def test_decode_split_merge_across_calls(heads):
+    """The last split of each (sequence, KV head) to finish merges all of them,
+    counted on per-unit counters that the merging split resets.  Successive
+    calls whose split counts differ (many, one, many, a few) on two layers of
+    one cache must each match the oracle, and a call repeated on the same
+    inputs must give the same bits (the merge runs in split order, whatever
+    order the splits finish in)."""
+    kv = _kv()
+    H, Hkv = heads
+    B, D, dtype = 3, 64, "f16"
+    max_T = 5000
+    scale = float(np.float32(1 / np.sqrt(D)))
+    hist_k = _rand((2, B, Hkv, max_T, D), dtype, 31)
+    hist_v = _rand((2, B, Hkv, max_T, D), dtype, 32)
+    c = kv.KVCache(2, B, H, Hkv, D, max_T, TORCH_DT[dtype])
+    for layer in range(2):
+        c.k_view(layer).copy_(to_dev(hist_k[layer], dtype))
+        c.v_view(layer).copy_(to_dev(hist_v[layer], dtype))
+    rounds = [[5000, 4097, 2999], [1, 7, 300], [4999, 5000, 1025], [385, 1024, 2048]]
+    for r, lens in enumerate(rounds):
+        for layer in range(2):
+            say(f"split merge H={H} Hkv={Hkv} round={r} layer={layer} lens={lens}")
+            c.set_lengths(lens, layer=layer)
+            q = _rand((B, H, 1, D), dtype, 100 + 2 * r + layer)
+            qd = to_dev(q, dtype)
+            o1 = c.decode(layer, qd, scale=scale, out_dtype=torch.float32)
+            o2 = c.decode(layer, qd, scale=scale, out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            assert np.array_equal(host_bits(o1), host_bits(o2)), "repeated decode differs"
+            ref = oracle.decode_cached(si.to_f64(q[:, :, 0], dtype), si.to_f64(hist_k[layer], dtype),
+                                       si.to_f64(hist_v[layer], dtype), lens, scale)
+            check_output(o1[:, :, 0], ref, dtype, f"decode round {r} layer {layer}")
+    c.close()
+
+
 def test_config1_end_to_end():
     """fp32, B=1, H=4, D=64: prefill 128 then 32 decode steps, every step checked
     against the cached oracle, the recompute oracle, and the GPU's own prefill row."""
