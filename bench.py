@@ -85,8 +85,10 @@ PREFILL_SOURCES = ["prefill.hip", "common.hpp"]
 CALIB_BYTES = 4 << 30
 # kernels of each measured launch, by a substring of the demangled or mangled name
 TRAFFIC_KERNELS = {
-    "decode_ragged_b32": (DECODE_SOURCES, ["decode_kernel<kvattn::TagF16, 128, 1, 6, 1, 4, false, false>"]),
-    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4, 4, 1, 4, false, false>"]),
+    "decode_ragged_b32": (DECODE_SOURCES, ["decode_kernel<kvattn::TagF16, 128, 1, 6, 1, 4, false, false>",
+                                           "decode_merge_kernel<128, 1>"]),
+    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4, 4, 1, 4, false, false>",
+                                        "decode_merge_kernel<128, 4>"]),
     "prefill_t8192": (PREFILL_SOURCES, ["prefill_pipe_kernelIDF16_Li128"]),
 }
 
@@ -669,7 +671,7 @@ def main():
         out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "traffic": traffic_from_profiles("decode_ragged_b32", dec_hash),
-                           "kernel": "kvattn_decode (split-K decode_kernel, last split of each unit merges) per layer",
+                           "kernel": "kvattn_decode (split-K partial + merge) per layer",
                            "algorithmic_bytes_per_launch": dec["bytes_kernel"],
                            "mean_launch_ms": round(k_ms, 5)}
         out["decode"] = {"ms_per_step": round(dec_ms, 4), "us_per_layer": round(dec_ms * 1e3 / w5.layers, 2),

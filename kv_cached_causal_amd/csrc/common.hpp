@@ -40,8 +40,7 @@ struct DecodeArgs {
   const void *v_layer;
   const void *q;        // (B, H, tokens, D)
   void *o;              // (B, H, tokens, D) in o_dtype
-  float *ws;            // (B, H * tokens, n_splits, D + 2) fp32: m (log2 domain), l, u[D]; then the
-                        // split counters (split_counters)
+  float *ws;            // (B, H * tokens, n_splits, D + 2) fp32: m (log2 domain), l, u[D]
   const int32_t *len;   // layer's lengths [B] (after the tokens' own rows were added)
   int batch, q_heads, kv_heads, head_dim, max_T, chunk, n_splits;
   int window, sink;     // sliding window (0: none) and attention-sink positions
@@ -62,19 +61,6 @@ constexpr int kMaxVerifyTokens = 8;
 // An extend of T positions over a cache with G query heads per KV head runs
 // on the decode kernels when one workgroup can hold all G * T query rows of a
 // KV head (the instantiated row counts 2, 3, 4, 8) and no window is set.
-// Decode workspace: the fp32 partials (m, l, u) of every split, then one
-// int32 counter per (sequence, unit of query rows) -- the splits of the unit
-// that have finished.  The counters are zeroed at allocation and the last
-// split of a unit resets its own, so every call finds them at zero.
-__host__ __device__ inline size_t ws_floats(int batch, int q_heads, int n_splits, int head_dim) {
-  return (size_t)batch * q_heads * kMaxVerifyTokens * n_splits * (head_dim + 2);
-}
-__host__ __device__ inline size_t ws_counters(int batch, int q_heads) {
-  return (size_t)batch * q_heads * kMaxVerifyTokens;
-}
-__host__ __device__ inline int32_t *split_counters(const DecodeArgs &a) {
-  return (int32_t *)(a.ws + ws_floats(a.batch, a.q_heads, a.n_splits, a.head_dim));
-}
 inline bool verify_on_decode(int G, int T, int window) {
   const int r = G * T;
   return T >= 2 && T <= kMaxVerifyTokens && window == 0 && (r == 2 || r == 3 || r == 4 || r == 8);

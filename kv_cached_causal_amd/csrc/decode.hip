@@ -7,9 +7,15 @@
 // with 16-byte loads, the G query heads that share a KV head (roadmap page,
 // project 12, MQA/GQA) are served by the same workgroup, and long contexts
 // are split across workgroups.  Each split keeps the online-softmax state
-// (m, l, u) -- the chunked-attention recurrence of the README -- and the last
-// split of each (sequence, KV head) to finish merges them all by log-sum-exp,
-// in the same launch.  Scores carry log2(e) inside the scale so that every
+// (m, l, u) -- the chunked-attention recurrence of the README -- and a small
+// second kernel merges the splits of each (sequence, KV head) by log-sum-exp.
+// Merging in the last-arriving workgroup instead was measured twice: with a
+// device-scope fence per workgroup (which on this multi-XCD part writes back
+// and invalidates the whole L2) ten times slower; with the partials written
+// and read by device-scope stores and loads and one atomic counter per unit
+// (no L2 flush) about 1 % slower on the ragged batch-32 decode and 2.5 % on
+// the 4-token verification, and level on the GQA batch-16 decode, whose
+// workgroups all finish together so that the merge is exposed either way.  Scores carry log2(e) inside the scale so that every
 // exponential is a single exp2.
 #include "common.hpp"
 
@@ -355,16 +361,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     return;
   }
 
-  // Publish this split's (m, l, u) for the GT heads, count it in, and let
-  // the unit's last split to arrive merge them all.  The L2 is per XCD, so
-  // the partials are written with device-scope stores (written through to the
-  // level every XCD shares) and read back with device-scope loads (which
-  // bypass the reader's L2); each thread waits for its stores to be
-  // acknowledged before the workgroup barrier, and only then is the split
-  // counted (a device-scope atomic).  Nothing else is written through, so no
-  // L2 writeback or invalidate is needed: a device-scope fence per workgroup
-  // (which does both for the whole L2) measured ten times slower.
-  float *const wsu = a.ws + (size_t)(b * RS + h0) * a.n_splits * (D + 2);
+  // write this split's (m, l, u) for the GT heads; decode_merge combines them
   for (int t = tid; t < GT * D; t += NW * 64) {
     const int g = t / D;
     const int d = t - g * D;
@@ -381,63 +378,92 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       num = fmaf(al, s_acc[w][g][d], num);
       den = fmaf(al, s_l[w][g], den);
     }
-    float *dst = wsu + ((size_t)g * a.n_splits + split) * (D + 2);
-    __hip_atomic_store(dst + 2 + d, num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float *dst = a.ws + ((size_t)(b * RS + h0 + g) * a.n_splits + split) * (D + 2);
+    dst[2 + d] = num;
     if (d == 0) {
-      __hip_atomic_store(dst, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(dst + 1, den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      dst[0] = M;
+      dst[1] = den;
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  __shared__ int s_last;
-  if (tid == 0) {
-    int32_t *cnt = split_counters(a) + (size_t)b * a.q_heads * kMaxVerifyTokens + unit;
-    const int done = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = done == n_valid - 1;
-    // every split of the unit has counted itself in: ready for the next call
-    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
+}
 
-  // The merge, bound by load latency: each thread owns whole output elements
-  // and issues the loads of eight splits (their m, l and its u column) at
-  // once, one dependent round trip per eight splits.
-  constexpr int SB = 8;
-  for (int t = tid; t < GT * D; t += NW * 64) {
-    const int g = t / D;
-    const int d = t - g * D;
-    const float *wsg = wsu + (size_t)g * a.n_splits * (D + 2);
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int s0 = 0; s0 < n_valid; s0 += SB) {
-      float ms[SB], ls[SB], us[SB];
+// threads of the merge kernel: one per output element up to 256, else a
+// block size that divides the GT * D outputs evenly
+template <int D, int GT>
+constexpr int merge_threads() {
+  return GT * D <= 256 ? GT * D : (GT * D % 256 == 0 ? 256 : 128);
+}
+
+// grid (Hkv * G/GT, B): log-sum-exp merge of the non-empty splits of one
+// (sequence, KV head, GT query heads) unit.  Units whose context fits one split
+// were finished by decode_kernel.  The kernel is bound by load latency, so
+// each thread owns whole output elements and issues the loads of eight
+// splits (their m, l and its u column) at once: one dependent round trip per
+// eight splits, no shared memory and no barrier.
+template <int D, int GT>
+__global__ __launch_bounds__((merge_threads<D, GT>())) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int THREADS = merge_threads<D, GT>();
+  constexpr int E = GT * D / THREADS;  // outputs per thread
+  static_assert(E * THREADS == GT * D, "outputs split evenly");
+  constexpr int SB = 8;                // splits per round of loads
+  const int b = blockIdx.y;
+  const int RS = a.q_heads * a.tokens;                 // query rows per sequence
+  const int RK = (a.q_heads / a.kv_heads) * a.tokens;  // query rows per KV head
+  const int subs = RK / GT;
+  const int unit = blockIdx.x;
+  const int kvh = unit / subs;
+  const int h0 = kvh * RK + (unit - kvh * subs) * GT;
+  const int ns = (visible_keys(a.len[b], a.window, a.sink).count + a.chunk - 1) / a.chunk;
+  if (ns <= 1) return;
+  const float *ws_unit = a.ws + (size_t)(b * RS + h0) * a.n_splits * (D + 2);
+
+  float M[E], num[E], den[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    M[e] = -INFINITY;
+    num[e] = 0.f;
+    den[e] = 0.f;
+  }
+  for (int s0 = 0; s0 < ns; s0 += SB) {
+    float ms[E][SB], ls[E][SB], us[E][SB];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int t = e * THREADS + (int)threadIdx.x;
+      const int g = t / D;
+      const int d = t - g * D;
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
         // clamped (always in bounds) and masked below
-        const float *st = wsg + (size_t)min(s0 + i, n_valid - 1) * (D + 2);
-        ms[i] = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ls[i] = __hip_atomic_load(st + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        us[i] = __hip_atomic_load(st + 2 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float *st = ws_unit + ((size_t)g * a.n_splits + min(s0 + i, ns - 1)) * (D + 2);
+        ms[e][i] = st[0];
+        ls[e][i] = st[1];
+        us[e][i] = st[2 + d];
       }
-      float mx = M;
+    }
 #pragma unroll
-      for (int i = 0; i < SB; ++i) mx = fmaxf(mx, s0 + i < n_valid ? ms[i] : -INFINITY);
-      // split 0 holds key 0, which every query row sees, so mx is finite
-      // from the first round on
-      const float f = fast_exp2(M - mx);
-      num *= f;
-      den *= f;
+    for (int e = 0; e < E; ++e) {
+      float mx = M[e];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) mx = fmaxf(mx, s0 + i < ns ? ms[e][i] : -INFINITY);
+      // split 0 holds at least one visible key, so mx is finite from the first round on
+      const float f = fast_exp2(M[e] - mx);
+      num[e] *= f;
+      den[e] *= f;
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
-        const float w = s0 + i < n_valid ? fast_exp2(ms[i] - mx) : 0.f;
-        num = fmaf(w, us[i], num);
-        den = fmaf(w, ls[i], den);
+        const float w = s0 + i < ns ? fast_exp2(ms[e][i] - mx) : 0.f;
+        num[e] = fmaf(w, us[e][i], num[e]);
+        den[e] = fmaf(w, ls[e][i], den[e]);
       }
-      M = mx;
+      M[e] = mx;
     }
-    store_out(a.o, (size_t)(b * RS + h0 + g) * D + d, num / den, a.o_dt);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int t = e * THREADS + (int)threadIdx.x;
+    const int g = t / D;
+    const int d = t - g * D;
+    store_out(a.o, (size_t)(b * RS + h0 + g) * D + d, num[e] / den[e], a.o_dt);
   }
 }
 
@@ -455,6 +481,9 @@ static hipError_t launch_gt_layout(const DecodeArgs &a, hipStream_t s) {
   constexpr int U = GT >= 4 ? 4 : 6;
   const int units = a.q_heads * a.tokens / GT;  // = Hkv * (G * tokens / GT)
   decode_kernel<Tag, D, GT, U, NV, NW, PAGED, VER><<<dim3(a.n_splits, units, a.batch), NW * 64, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_splits == 1) return e;
+  decode_merge_kernel<D, GT><<<dim3(units, a.batch), merge_threads<D, GT>(), 0, s>>>(a);
   return hipGetLastError();
 }
 

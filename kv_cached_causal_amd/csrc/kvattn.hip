@@ -131,12 +131,10 @@ int kvattn_cache_alloc(kvattn_cache **out, int layers, int batch, int q_heads, i
   const size_t len_bytes = sizeof(int32_t) * (size_t)layers * batch;
   // split-K workspace for decode and for the short extends run on the decode
   // kernels (up to kMaxVerifyTokens query positions per head)
-  const size_t ws_bytes = sizeof(float) * ws_floats(batch, q_heads, c->n_splits, head_dim);
-  const size_t cnt_bytes = sizeof(int32_t) * ws_counters(batch, q_heads);
+  const size_t ws_bytes = sizeof(float) * (size_t)batch * q_heads * kMaxVerifyTokens * c->n_splits * (head_dim + 2);
   e = hipMalloc((void **)&c->d_len, len_bytes);
-  if (e == hipSuccess) e = hipMalloc((void **)&c->d_ws, ws_bytes + cnt_bytes);
+  if (e == hipSuccess) e = hipMalloc((void **)&c->d_ws, ws_bytes);
   if (e == hipSuccess) e = hipMemset(c->d_len, 0, len_bytes);
-  if (e == hipSuccess) e = hipMemset((char *)c->d_ws + ws_bytes, 0, cnt_bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     int rc = hip_fail(e, "cache side buffers");
@@ -553,12 +551,10 @@ int kvattn_paged_alloc(kvattn_paged **out, int layers, int slots, int max_blocks
   }
   const size_t len_bytes = sizeof(int32_t) * (size_t)layers * slots;
   const size_t tab_bytes = sizeof(int32_t) * (size_t)slots * max_blocks;
-  const size_t ws_bytes = sizeof(float) * ws_floats(slots, q_heads, p->n_splits, head_dim);
-  const size_t cnt_bytes = sizeof(int32_t) * ws_counters(slots, q_heads);
+  const size_t ws_bytes = sizeof(float) * (size_t)slots * q_heads * kMaxVerifyTokens * p->n_splits * (head_dim + 2);
   e = hipMalloc((void **)&p->d_len, len_bytes);
   if (e == hipSuccess) e = hipMalloc((void **)&p->d_table, tab_bytes);
-  if (e == hipSuccess) e = hipMalloc((void **)&p->d_ws, ws_bytes + cnt_bytes);
-  if (e == hipSuccess) e = hipMemset((char *)p->d_ws + ws_bytes, 0, cnt_bytes);
+  if (e == hipSuccess) e = hipMalloc((void **)&p->d_ws, ws_bytes);
   if (e == hipSuccess) e = hipMemset(p->d_len, 0, len_bytes);
   if (e == hipSuccess) e = hipMemset(p->d_table, 0, tab_bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();

@@ -450,7 +450,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
   constexpr int VPAIRS = (BN / 4) * (D / 8);
   constexpr bool SPLIT_STAGE = NW == 8;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-  static_assert(QW <= BN && BN % QW == 0, "a wave's rows fall in one key tile");
+  static_assert(QW <= BN && BN % QW == 0, "a wave's rows span at most two key tiles");
   static_assert(KCH >= 1 && BN * D / 8 == KCH * 256, "K tile must split evenly over 256 threads");
   static_assert(VPAIRS <= 256 && VPAIRS % 64 == 0, "V tile must cover whole waves");
 
@@ -477,14 +477,19 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
   const int lg = lane >> 4;
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * QW;
-  const int dw = qw0 / BN;  // this wave's diagonal tile; tiles after it are never needed
+  // query row i sits at absolute position off + i and sees keys 0 .. off + i
+  // (off = 0 for a prompt; the cached prefix length for an extend)
+  const int off = a.offsets ? a.offsets[b] : 0;
+  // tiles dlo .. dhi hold this wave's diagonal (masked); later ones are never needed
+  const int dlo = (off + qw0) / BN;
+  const int dhi = (off + qw0 + QW - 1) / BN;
   const int stid = SPLIT_STAGE ? (tid & 255) : tid;
   const bool stage_k = SPLIT_STAGE ? (tid < 256) : true;
   const bool stage_v = (SPLIT_STAGE ? (tid >= 256) : true) && stid < VPAIRS;
 
   const T *qb = (const T *)a.q + (size_t)bh * Tn * D;
-  const T *kb = (const T *)a.k + (size_t)(b * a.kv_heads + g) * Tn * D;
-  const T *vb = (const T *)a.v + (size_t)(b * a.kv_heads + g) * Tn * D;
+  const T *kb = (const T *)a.k + (size_t)(b * a.kv_heads + g) * a.kv_rows * D;
+  const T *vb = (const T *)a.v + (size_t)(b * a.kv_heads + g) * a.kv_rows * D;
   T *ckb = (T *)a.cache_k + (size_t)(b * a.kv_heads + g) * a.max_T * D;
   T *cvb = (T *)a.cache_v + (size_t)(b * a.kv_heads + g) * a.max_T * D;
 
@@ -510,7 +515,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
     for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int kv_end = min(q0 + BM, Tn);
+  const int kv_end = off + min(q0 + BM, Tn);
   const int n_tiles = (kv_end + BN - 1) / BN;
 
   // staging registers: with split staging a thread holds either K or V chunks
@@ -522,12 +527,13 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
   const int v_kg = stid % (BN / 4);
   const int v_ds = stid / (BN / 4);
 
-  // ---- staging: global -> registers (keys past T read as zeros, masked later) -> LDS (+ cache rows)
-  // Buffer loads over this (b, KV head)'s T x D slab: the per-tile offset is
-  // scalar and keys past T read as zeros (the range check of the buffer
-  // resource; they are masked in the scores and weigh 0 in P V), so the
-  // loads need no clamps and no 64-bit address arithmetic.
-  const int slab_bytes = Tn * D * (int)sizeof(T);
+  // ---- staging: global -> registers (keys past the last one read as zeros, masked later) -> LDS (+ cache rows)
+  // Buffer loads over this (b, KV head)'s (off + T) x D slab of keys: the
+  // per-tile offset is scalar and keys past off + T - 1 read as zeros (the
+  // range check of the buffer resource; they are masked in the scores and
+  // weigh 0 in P V), so the loads need no clamps and no 64-bit address
+  // arithmetic.
+  const int slab_bytes = (off + Tn) * D * (int)sizeof(T);
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, slab_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, slab_bytes, 0x00020000);
   const int k_voff = ((stid / (D / 8)) * D + (stid % (D / 8)) * 8) * (int)sizeof(T);
@@ -612,7 +618,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
       }
     }
   };
-  // causal mask of the diagonal tile t: lane holds S^T[key = tBN + 16kt + 4lg + i][query = qw0 + 16nt + l16]
+  // causal mask of a diagonal tile t: lane holds S^T[key = tBN + 16kt + 4lg + i][query = qw0 + 16nt + l16]
   auto mask = [&](int t, float4_t (&s)[KT][NT]) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
@@ -620,7 +626,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (t * BN + kt * 16 + lg * 4 + i > qw0 + nt * 16 + l16) s[kt][nt][i] = -INFINITY;
+          if (t * BN + kt * 16 + lg * 4 + i > off + qw0 + nt * 16 + l16) s[kt][nt][i] = -INFINITY;
   };
   const float c = a.scale_log2;
   // Row statistics of a score tile: the new running max (raised lazily) and
@@ -706,14 +712,14 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
 
   float4_t sa[KT][NT], sb[KT][NT];
   scores(0, sa);
-  if (dw == 0) mask(0, sa);
+  if (dlo == 0) mask(0, sa);
 
   // one tile: softmax(cur) overlapped with nxt = K_{j+1} Q^T, then P V_j
   auto step = [&](int j, float4_t (&cur)[KT][NT], float4_t (&nxt)[KT][NT]) {
     if (j + 2 < n_tiles) load_k(j + 2);
     if (j + 1 < n_tiles) load_v(j + 1);
     __builtin_amdgcn_sched_barrier(0);
-    if (j <= dw) {  // wave-uniform
+    if (j <= dhi) {  // wave-uniform
       vec8 pb[PS][NT];
       vec8 pl[Mfma<T>::kSplitP ? PS : 1][NT];
       float al[NT];
@@ -723,8 +729,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
       __builtin_amdgcn_s_setprio(2);
       const bool any_resc = stats(cur, al);
       // The next tile's scores are computed unconditionally (on the wave's
-      // diagonal tile they go unused: the slot then holds finite stale data
-      // or is never read back), which keeps this block free of branches.
+      // last tile they go unused: the slot then holds finite stale data or
+      // is never read back), which keeps this block free of branches.
       scores((j + 1) & 1, nxt);
       expo(cur, pb, pl, al);
       {
@@ -751,9 +757,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
           for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] *= al[nt];
       }
       pv(j & 1, pb, pl);
-      if (j + 1 == dw) {
-        // once per wave; the opaque tile index keeps the compares from being
-        // hoisted out of the loop as invariants
+      if (j + 1 >= dlo && j + 1 <= dhi) {
+        // once or twice per wave; the opaque tile index keeps the compares
+        // from being hoisted out of the loop as invariants
         int t = j + 1;
         asm volatile("" : "+v"(t));
         mask(t, nxt);
@@ -941,10 +947,24 @@ static hipError_t launch_f32(const PrefillArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Extend (queries after a cached prefix, K/V read from the cache): the plain
-// kernel for every 16-bit type and head dim, the vector kernel for fp32.
+// Extend (queries after a cached prefix, K/V read from the cache): the
+// pipelined kernel where the prompt uses it (f16, D = 128; no window, no block
+// table), else the plain kernel for every 16-bit type and head dim, the vector
+// kernel for fp32.
 template <typename T, int D>
 static hipError_t launch_extend_mfma(const PrefillArgs &a, hipStream_t s) {
+  typedef PrefillConfig<T, D> C;
+  if constexpr (C::kPipe) {
+    // the pipelined kernel over the contiguous cache (no window; the key slab
+    // of one sequence and KV head within its buffer loads' 32-bit range)
+    if (!a.table && a.window == 0 && (size_t)a.kv_rows * D * sizeof(T) < ((size_t)1 << 31)) {
+      constexpr int PBM = C::NW * C::QW;
+      const dim3 pgrid((unsigned)((a.T + PBM - 1) / PBM) * a.batch * a.q_heads);
+      static std::atomic<uint64_t> attr_pipe{0};
+      return launch_with_lds(prefill_pipe_kernel<T, D, C::QW, C::BN, C::NW>, pgrid, C::NW * 64,
+                             PipeLds<D, C::BN>::BYTES, s, attr_pipe, a);
+    }
+  }
   constexpr int NW = 4, QW = 32, BN = D == 32 ? 128 : 64, BM = NW * QW;
   const int n_qt = (a.T + BM - 1) / BM;
   const dim3 grid((unsigned)n_qt * a.batch * a.q_heads);

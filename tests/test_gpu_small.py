@@ -162,13 +162,12 @@ def test_decode_matches_oracle(dtype, D, heads):
 
 
 @pytest.mark.parametrize("heads", [(4, 4), (4, 1)], ids=lambda x: f"H{x[0]}kv{x[1]}")
-def test_decode_split_merge_across_calls(heads):
-    """The last split of each (sequence, KV head) to finish merges all of them,
-    counted on per-unit counters that the merging split resets.  Successive
-    calls whose split counts differ (many, one, many, a few) on two layers of
-    one cache must each match the oracle, and a call repeated on the same
-    inputs must give the same bits (the merge runs in split order, whatever
-    order the splits finish in)."""
+def test_decode_split_workspace_across_calls(heads):
+    """Successive decode calls whose split counts differ (many, one, many, a
+    few) on two layers of one cache, sharing one split workspace, must each
+    match the oracle, and a call repeated on the same inputs must give the
+    same bits (the merge runs in split order, whatever order the splits
+    finish in)."""
     kv = _kv()
     H, Hkv = heads
     B, D, dtype = 3, 64, "f16"
