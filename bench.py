@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import math
+import statistics
 import os
 import sys
 import time
@@ -179,6 +180,64 @@ def measure_mfma_ceiling(kv, dev, workgroups=1024, iters=20000, reps=5):
     torch.cuda.synchronize()
     flops = kv.lib().kvattn_measure_mfma_f16_flops(workgroups, iters)
     return flops / (a.elapsed_time(b) / reps * 1e-3) / 1e12
+
+
+def measure_exp_ceiling(kv, dev, workgroups=1024, iters=20000, reps=5):
+    """exp2 rate of this device (plain v_exp_f32 loop of the library), exponentials per second."""
+    import ctypes
+    sink = torch.zeros(workgroups, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    fn = kv.lib().kvattn_measure_exp2
+
+    def run():
+        if fn(workgroups, iters, ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+            raise RuntimeError("kvattn_measure_exp2 failed")
+    for _ in range(3):
+        run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    n = kv.lib().kvattn_measure_exp2_count(workgroups, iters)
+    return n / (a.elapsed_time(b) / reps * 1e-3)
+
+
+def small_head_prefill(kv, dev, mceil, eceil, reps=20):
+    """The 8-layer x 512-wide model's attention prefill at T=8192 (B=1, 16 heads of D=32, fp16):
+    per-launch time against the MFMA peak and against the exponential ceiling (one exp2 per
+    unmasked score: at D=32 a score costs only 128 MFMA flops)."""
+    T, H, D = 8192, 16, 32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(32)
+    dt = torch.float16
+    q = torch.randn((1, H, T, D), generator=gen, device=dev).to(dt)
+    k = torch.randn((1, H, T, D), generator=gen, device=dev).to(dt)
+    v = torch.randn((1, H, T, D), generator=gen, device=dev).to(dt)
+    o = torch.empty_like(q)
+    c = kv.KVCache(1, 1, H, H, D, T, dt, device=dev)
+    call = c.bind_prefill(0, q, k, v, o, scale=D ** -0.5)
+    times = []
+    for i in range(reps + 3):
+        c.set_lengths([0])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            times.append(a.elapsed_time(b))
+    c.close()
+    med = statistics.median(times) * 1e-3
+    flops = 4.0 * H * D * T * (T + 1) / 2
+    exps = H * T * (T + 1) / 2
+    return {"workload": "T=8192 causal prefill, B=1, H=16, D=32, fp16 (the 8L x 512d model's attention)",
+            "us_per_layer": round(med * 1e6, 1), "value": round(flops / med / 1e12, 1), "unit": "TFLOP/s",
+            "frac_of_mfma_peak": round(flops / med / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "mfma_bound_us": round(flops / (mceil * 1e12) * 1e6, 1),
+            "exp_bound_us": round(exps / eceil * 1e6, 1), "exps_per_layer": int(exps),
+            "frac_of_exp_ceiling": round(exps / eceil / med, 4)}
 
 
 def calibration_kernels(kv, dev):
@@ -739,6 +798,11 @@ def main():
         out["mfma_f16_ceiling"] = {"value": round(mceil, 1), "unit": "TFLOP/s", "kernel": "kvattn_measure_mfma_f16",
                                    "prefill_frac_of_ceiling":
                                        round(out["prefill"]["roofline"]["achieved"] / mceil, 4)}
+        eceil = measure_exp_ceiling(kv, dev)
+        out["exp2_ceiling"] = {"value": round(eceil / 1e12, 3), "unit": "T exp2/s", "kernel": "kvattn_measure_exp2"}
+        if not args.no_extras:
+            log("small-head prefill (T=8192, 16 heads of D=32)")
+            out["prefill_d32"] = small_head_prefill(kv, dev, mceil, eceil)
     if args.calibrate:
         calibration_kernels(kv, dev)
     if not args.no_cpu_baseline:

@@ -3,10 +3,11 @@
  * the attention path.
  *
  * The decode kernels are bounded by HBM bandwidth and the prefill kernel by
- * the matrix cores.  Besides the published peaks, the benchmark reports the
- * streaming-read rate and the fp16 MFMA rate this device actually sustains,
- * measured with the plain kernels below, so that each kernel's rate can be
- * read against both.
+ * the matrix cores (at small head dims also by the one exponential each score
+ * needs).  Besides the published peaks, the benchmark reports the
+ * streaming-read rate, the fp16 MFMA rate and the exp2 rate this device
+ * actually sustains, measured with the plain kernels below, so that each
+ * kernel's rate can be read against them.
  */
 #ifndef KVATTN_MEASURE_H
 #define KVATTN_MEASURE_H
@@ -44,6 +45,22 @@ int kvattn_measure_mfma_f16(int workgroups, int iters, float *sink, void *stream
 /* Floating-point operations of one such launch (0 for a non-positive
  * argument).  Pure host function. */
 double kvattn_measure_mfma_f16_flops(int workgroups, int iters);
+
+/* Enqueue on `stream` a plain exponential loop: `workgroups` workgroups of 256
+ * threads, each thread running `iters` rounds of eight independent chains
+ * x <- exp2(-x) (one v_exp_f32 per exponential, fp32), with no memory
+ * traffic in the loop.  The sums are written to sink[blockIdx] (a device
+ * array of at least `workgroups` floats) only if they equal an unlikely
+ * constant.  Returns 0, KVATTN_ERR_INVALID_ARG (-1) or KVATTN_ERR_HIP (-6).
+ * Time it with events on the same stream and divide
+ * kvattn_measure_exp2_count(workgroups, iters) by the time: the exponential
+ * rate the device sustains (the prefill kernel's exponentials are of this
+ * instruction). */
+int kvattn_measure_exp2(int workgroups, int iters, float *sink, void *stream);
+
+/* Exponentials of one such launch (0 for a non-positive argument).  Pure host
+ * function. */
+double kvattn_measure_exp2_count(int workgroups, int iters);
 
 #ifdef __cplusplus
 }

@@ -87,6 +87,8 @@ _SIGS = {
     "kvattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvattn_measure_mfma_f16": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
     "kvattn_measure_mfma_f16_flops": (ctypes.c_double, [ctypes.c_int, ctypes.c_int]),
+    "kvattn_measure_exp2": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
+    "kvattn_measure_exp2_count": (ctypes.c_double, [ctypes.c_int, ctypes.c_int]),
     "kvattn_measure_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                                   ctypes.c_void_p]),
     "kvattn_last_error": (ctypes.c_char_p, []),

@@ -1,7 +1,8 @@
 // Measurement aids: a plain streaming-read kernel, used to report the HBM read
-// rate the device sustains next to the decode kernels' rate, and a plain
+// rate the device sustains next to the decode kernels' rate; a plain
 // matrix-core loop, used to report the fp16 MFMA rate it sustains next to the
-// prefill kernel's rate.
+// prefill kernel's rate; and a plain exp2 loop, used to report the rate of the
+// exponentials (one per score) that bound prefill at small head dims.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -52,7 +53,36 @@ __global__ __launch_bounds__(256, 2) void mfma_loop_kernel(int iters, float *sin
   if (r == 1234.5f) sink[blockIdx.x] = r;
 }
 
+// Each thread runs `iters` rounds of NCH independent chains x <- exp2(-x)
+// (v_exp_f32 with a negated source: one instruction per exponential; the
+// chains settle near 0.64, always normal numbers).
+constexpr int kExpChains = 8;
+__global__ __launch_bounds__(256, 2) void exp_loop_kernel(int iters, float *sink) {
+  float x[kExpChains];
+#pragma unroll
+  for (int c = 0; c < kExpChains; ++c) x[c] = (float)(threadIdx.x & 7) * 0.125f + (float)c * 0.01f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kExpChains; ++c) x[c] = fast_exp2(-x[c]);
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int c = 0; c < kExpChains; ++c) r += x[c];
+  if (r == 1234.5f) sink[blockIdx.x] = r;
+}
+
 }  // namespace kvattn
+
+extern "C" int kvattn_measure_exp2(int workgroups, int iters, float *sink, void *stream) {
+  if (!sink || workgroups <= 0 || iters <= 0) return KVATTN_ERR_INVALID_ARG;
+  kvattn::exp_loop_kernel<<<dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream>>>(iters, sink);
+  return hipGetLastError() == hipSuccess ? KVATTN_OK : KVATTN_ERR_HIP;
+}
+
+extern "C" double kvattn_measure_exp2_count(int workgroups, int iters) {
+  if (workgroups <= 0 || iters <= 0) return 0.0;
+  return (double)workgroups * 256 * iters * kvattn::kExpChains;
+}
 
 extern "C" int kvattn_measure_mfma_f16(int workgroups, int iters, float *sink, void *stream) {
   if (!sink || workgroups <= 0 || iters <= 0) return KVATTN_ERR_INVALID_ARG;

@@ -128,6 +128,17 @@ def test_measure_mfma_validates_on_host_and_counts_flops():
     assert lib.kvattn_measure_mfma_f16_flops(0, 5) == 0.0
 
 
+def test_measure_exp2_validates_on_host_and_counts():
+    lib = kv.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.kvattn_measure_exp2(0, 10, fake, None) == -1
+    assert lib.kvattn_measure_exp2(8, 0, fake, None) == -1
+    assert lib.kvattn_measure_exp2(8, 10, None, None) == -1
+    # 256 threads x 8 chains per round
+    assert lib.kvattn_measure_exp2_count(3, 5) == 3 * 256 * 5 * 8
+    assert lib.kvattn_measure_exp2_count(0, 5) == 0.0
+
+
 def test_measure_stream_read_validates_on_host():
     lib = kv.lib()
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation first

@@ -72,6 +72,36 @@ def test_extend_matches_oracle(dtype, D, heads, T):
     c.close()
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("heads", [(8, 8), (8, 2)], ids=lambda x: f"H{x[0]}kv{x[1]}")
+def test_extend_long_ragged_prefixes(dtype, heads):
+    """Extends after long cached prefixes whose lengths are not multiples of the
+    32-row wave slice or the 64-key tile (a wave's rows then straddle two key
+    tiles deep in the cache), with several 256-row query tiles per head; f16 at
+    D=128 runs the pipelined kernel, bf16 the plain one."""
+    kv = _kv()
+    H, Hkv = heads
+    B, D, T = 3, 128, 600
+    lengths = [1000, 3001, 77]
+    max_T = max(lengths) + T + 5
+    say(f"extend long prefixes dtype={dtype} H={H} Hkv={Hkv} T={T} lengths={lengths}")
+    seed = 7000 + 10 * H + Hkv
+    k_hist = _rand((B, Hkv, max_T, D), dtype, seed)
+    v_hist = _rand((B, Hkv, max_T, D), dtype, seed + 1)
+    q = _rand((B, H, T, D), dtype, seed + 2)
+    k_new = np.stack([k_hist[b, :, L:L + T] for b, L in enumerate(lengths)])
+    v_new = np.stack([v_hist[b, :, L:L + T] for b, L in enumerate(lengths)])
+    c = kv.KVCache(1, B, H, Hkv, D, max_T, TORCH_DT[dtype])
+    _fill_prefix(c, 0, k_hist, v_hist, dtype, lengths)
+    o = c.extend(0, to_dev(q, dtype), to_dev(k_new, dtype), to_dev(v_new, dtype), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    f = lambda a: si.to_f64(a, dtype)
+    ref = oracle.extend(f(q), f(k_hist), f(v_hist), lengths, 1.0 / np.sqrt(D))
+    check_output(o, ref, dtype, "extend after long prefixes")
+    assert c.lengths(0) == [L + T for L in lengths]
+    c.close()
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("D", [32, 128])
 @pytest.mark.parametrize("GT", [(1, 2), (1, 3), (1, 4), (1, 8), (2, 2), (2, 4), (4, 2)],
