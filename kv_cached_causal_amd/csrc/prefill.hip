@@ -411,13 +411,24 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
 }
 
 // ---------------------------------------------------------------- pipelined kernel
-// Software-pipelined variant: while the vector ALUs turn the scores of tile j
-// into P (max, exp2, rounding, row sums), the matrix cores already compute the
-// scores of tile j+1; then P_j V_j runs.  K and V live in separate two-deep
-// LDS rings: iteration j reads K_{j+1} and V_j and stages K_{j+2} and V_{j+1},
-// so a single barrier per tile suffices.  Cross-lane row maxima use the
-// permlane swaps (no LDS traffic).  The rare branches (lazy rescale of O, the
-// causal mask of a wave's diagonal tile) sit between the overlapped blocks.
+// Software-pipelined variant (f16): while the vector ALUs turn the scores of
+// tile j into P (max, exp2, rounding, row sums), the matrix cores already
+// compute the scores of tile j+1; then P_j V_j runs.  K and V live in separate
+// two-deep LDS rings: iteration j reads K_{j+1} and V_j and stages K_{j+2} and
+// V_{j+1}, so a single barrier per tile suffices.  The rare branches (lazy
+// rescale of O, the causal mask of a wave's diagonal tiles) sit between the
+// overlapped blocks.
+//
+// Both products run on v_mfma_f32_32x32x16_f16, whose 32 output columns are a
+// wave's 32 query rows: S^T = K Q^T (two 32-key blocks per 64-key tile, eight
+// k-steps over D = 128) and O^T += V^T P^T (four 32-wide d-blocks, four
+// 16-key k-steps).  A lane then holds one query column (lanes l and l ^ 32 the
+// same one), so the row maximum and sum take one permlane32 swap, and a lane's
+// scores of k-step ps are already its P^T operand of that step: the MFMA's
+// k-index 8 hh + i stands for key 16 ps + 8 (i / 4) + 4 hh + i % 4, and the
+// V^T operand is read with the same key order (two 8-byte LDS reads).  Half
+// as many matrix instructions as with the 16x16x32 shape, and per-lane row
+// statistics for one query instead of two.
 template <int D, int BN>
 struct PipeLds {
   static constexpr int KSTR = D + 8;   // K row stride (elements)
@@ -427,36 +438,35 @@ struct PipeLds {
   static constexpr size_t BYTES = (size_t)(2 * K_ELEMS + 2 * V_ELEMS) * 2;
 };
 
-// x combined over the four lanes l, l^16, l^32, l^48 (the lanes holding one query column)
+typedef float float16v_t __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ float16v_t mma32_f16(const half8_t &a, const half8_t &b, const float16v_t &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// x combined over lanes l and l ^ 32 (the two lanes holding one query column)
 template <bool MAX>
-__device__ __forceinline__ float across_lg(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = MAX ? fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])) : __uint_as_float(a[0]) + __uint_as_float(a[1]);
+__device__ __forceinline__ float across_h(float x) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return MAX ? fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])) : __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <typename T, int D, int QW, int BN, int NW>
-__global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefill_pipe_kernel(PrefillArgs a) {
-  typedef typename Mfma<T>::vec vec8;
+template <int D, int BN>
+__global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
+  typedef half_t T;
+  typedef half8_t vec8;
   typedef PipeLds<D, BN> LDS;
+  constexpr int NW = 8, QW = 32;
   constexpr int BM = NW * QW;
-  constexpr int NT = QW / 16;
-  constexpr int KT = BN / 16;
-  constexpr int KS = D / 32;
-  constexpr int DT = D / 16;
-  constexpr int PS = BN / 32;
+  constexpr int KB = BN / 32;    // key blocks of 32 per tile
+  constexpr int KS = D / 16;     // score k-steps over D
+  constexpr int DB = D / 32;     // output d-blocks
+  constexpr int PS = BN / 16;    // P V k-steps over keys
   constexpr int KCH = BN * D / 8 / 256;
   constexpr int VPAIRS = (BN / 4) * (D / 8);
-  constexpr bool SPLIT_STAGE = NW == 8;
-  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-  static_assert(QW <= BN && BN % QW == 0, "a wave's rows span at most two key tiles");
-  static_assert(KCH >= 1 && BN * D / 8 == KCH * 256, "K tile must split evenly over 256 threads");
-  static_assert(VPAIRS <= 256 && VPAIRS % 64 == 0, "V tile must cover whole waves");
+  static_assert(KCH == 4 && VPAIRS == 256, "one 16-byte chunk set per staging thread");
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  T *const Kbuf = reinterpret_cast<T *>(smem_raw);  // [2][BN][KSTR]
-  T *const Vbuf = Kbuf + 2 * LDS::K_ELEMS;         // [2][D][VSTR]
+  T *const Kbuf = reinterpret_cast<T *>(smem_raw);
+  T *const Vbuf = Kbuf + 2 * LDS::K_ELEMS;
 
   const int Tn = a.T;
   const int H = a.q_heads;
@@ -473,66 +483,44 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int l16 = lane & 15;
-  const int lg = lane >> 4;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * QW;
-  // query row i sits at absolute position off + i and sees keys 0 .. off + i
-  // (off = 0 for a prompt; the cached prefix length for an extend)
   const int off = a.offsets ? a.offsets[b] : 0;
-  // tiles dlo .. dhi hold this wave's diagonal (masked); later ones are never needed
   const int dlo = (off + qw0) / BN;
   const int dhi = (off + qw0 + QW - 1) / BN;
-  const int stid = SPLIT_STAGE ? (tid & 255) : tid;
-  const bool stage_k = SPLIT_STAGE ? (tid < 256) : true;
-  const bool stage_v = (SPLIT_STAGE ? (tid >= 256) : true) && stid < VPAIRS;
+  const int stid = tid & 255;
+  const bool stage_k = tid < 256;
 
   const T *qb = (const T *)a.q + (size_t)bh * Tn * D;
   const T *kb = (const T *)a.k + (size_t)(b * a.kv_heads + g) * a.kv_rows * D;
   const T *vb = (const T *)a.v + (size_t)(b * a.kv_heads + g) * a.kv_rows * D;
   T *ckb = (T *)a.cache_k + (size_t)(b * a.kv_heads + g) * a.max_T * D;
   T *cvb = (T *)a.cache_v + (size_t)(b * a.kv_heads + g) * a.max_T * D;
-
-  // the cache copy of the prompt rows (skipped when another kernel places them)
   const bool writer_c = writer && a.write_cache;
   if (a.write_cache && qt == 0 && h == 0 && tid == 0) a.len[b] = Tn;
 
-  vec8 qf[NT][KS];
+  // Q^T fragments (B operand): lane holds Q[qw0 + l32][16 ks + 8 hh .. + 7]
+  vec8 qf[KS];
+  {
+    const int row = min(qw0 + l32, Tn - 1);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int row = min(qw0 + nt * 16 + l16, Tn - 1);  // rows past T are never stored
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[nt][ks] = *(const vec8 *)(qb + (size_t)row * D + ks * 32 + lg * 8);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const vec8 *)(qb + (size_t)row * D + ks * 16 + hh * 8);
   }
-
-  float4_t oacc[DT][NT];
-  float mrow[NT], lrow[NT];
+  float16v_t oacc[DB];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    mrow[nt] = -INFINITY;
-    lrow[nt] = 0.f;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
+  float mrow = -INFINITY, lrow = 0.f;
 
   const int kv_end = off + min(q0 + BM, Tn);
   const int n_tiles = (kv_end + BN - 1) / BN;
 
-  // staging registers: with split staging a thread holds either K or V chunks
-  constexpr int SR = KCH > 4 ? KCH : 4;
-  u32x4 sreg_a[SPLIT_STAGE ? SR : KCH];
-  u32x4 sreg_b[SPLIT_STAGE ? 1 : 4];
-  u32x4 *const kreg = sreg_a;
-  u32x4 *const vreg = SPLIT_STAGE ? sreg_a : sreg_b;
+  u32x4 sreg[4];
   const int v_kg = stid % (BN / 4);
   const int v_ds = stid / (BN / 4);
-
-  // ---- staging: global -> registers (keys past the last one read as zeros, masked later) -> LDS (+ cache rows)
-  // Buffer loads over this (b, KV head)'s (off + T) x D slab of keys: the
-  // per-tile offset is scalar and keys past off + T - 1 read as zeros (the
-  // range check of the buffer resource; they are masked in the scores and
-  // weigh 0 in P V), so the loads need no clamps and no 64-bit address
-  // arithmetic.
   const int slab_bytes = (off + Tn) * D * (int)sizeof(T);
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, slab_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, slab_bytes, 0x00020000);
@@ -543,15 +531,15 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
         const int soff = (t * BN + c * (256 / (D / 8))) * D * (int)sizeof(T);
-        kreg[c] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff, soff, 0);
+        sreg[c] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff, soff, 0);
       }
     }
   };
   auto load_v = [&](int t) {
-    if (stage_v) {
+    if (!stage_k) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + r * D * (int)sizeof(T), t * BN * D * (int)sizeof(T), 0);
+        sreg[r] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + r * D * (int)sizeof(T), t * BN * D * (int)sizeof(T), 0);
     }
   };
   auto store_k = [&](int t, int slot) {
@@ -560,26 +548,26 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
         const int idx = c * 256 + stid;
-        *(u32x4 *)(Ks + (idx / (D / 8)) * LDS::KSTR + (idx % (D / 8)) * 8) = kreg[c];
+        *(u32x4 *)(Ks + (idx / (D / 8)) * LDS::KSTR + (idx % (D / 8)) * 8) = sreg[c];
       }
-      if (writer_c && t * BN + BN > q0) {  // workgroup-uniform
+      if (writer_c && t * BN + BN > q0) {
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
           const int idx = c * 256 + stid;
           const int key = t * BN + idx / (D / 8);
-          if (key >= q0 && key < Tn) *(u32x4 *)(ckb + (size_t)key * D + (idx % (D / 8)) * 8) = kreg[c];
+          if (key >= q0 && key < Tn) *(u32x4 *)(ckb + (size_t)key * D + (idx % (D / 8)) * 8) = sreg[c];
         }
       }
     }
   };
   auto store_v = [&](int t, int slot) {
-    if (stage_v) {
+    if (!stage_k) {
       T *Vt = Vbuf + slot * LDS::V_ELEMS;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1;
-        const uint32_t r0 = vreg[0][w], r1 = vreg[1][w];
-        const uint32_t r2 = vreg[2][w], r3 = vreg[3][w];
+        const uint32_t r0 = sreg[0][w], r1 = sreg[1][w];
+        const uint32_t r2 = sreg[2][w], r3 = sreg[3][w];
         u32x2 out;
         if (e & 1) {
           out[0] = (r0 >> 16) | (r1 & 0xffff0000u);
@@ -594,112 +582,77 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = t * BN + 4 * v_kg + r;
-          if (key >= q0 && key < Tn) *(u32x4 *)(cvb + (size_t)key * D + v_ds * 8) = vreg[r];
+          if (key >= q0 && key < Tn) *(u32x4 *)(cvb + (size_t)key * D + v_ds * 8) = sreg[r];
         }
       }
     }
   };
 
-  // ---- math pieces
-  // S^T (keys x queries) = K_t Q^T from K slot `slot`
-  auto scores = [&](int slot, float4_t (&s)[KT][NT]) {
+  // S^T (keys x queries) = K_t Q^T: lane holds S^T[key = 32 kb + 8 (j / 4) + 4 hh + j % 4][query = qw0 + l32]
+  auto scores = [&](int slot, float16v_t (&s)[KB]) {
     const T *Ks = Kbuf + slot * LDS::K_ELEMS;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int k2 = 0; k2 < KB; ++k2)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) s[kt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 16; ++j) s[k2][j] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const vec8 ka = *(const vec8 *)(Ks + (kt * 16 + l16) * LDS::KSTR + ks * 32 + lg * 8);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s[kt][nt] = Mfma<T>::mma(ka, qf[nt][ks], s[kt][nt]);
+      for (int k2 = 0; k2 < KB; ++k2) {
+        const vec8 ka = *(const vec8 *)(Ks + (k2 * 32 + l32) * LDS::KSTR + ks * 16 + hh * 8);
+        s[k2] = mma32_f16(ka, qf[ks], s[k2]);
       }
     }
   };
-  // causal mask of a diagonal tile t: lane holds S^T[key = tBN + 16kt + 4lg + i][query = qw0 + 16nt + l16]
-  auto mask = [&](int t, float4_t (&s)[KT][NT]) {
+  auto mask = [&](int t, float16v_t (&s)[KB]) {
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int k2 = 0; k2 < KB; ++k2)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t * BN + kt * 16 + lg * 4 + i > off + qw0 + nt * 16 + l16) s[kt][nt][i] = -INFINITY;
+      for (int j = 0; j < 16; ++j)
+        if (t * BN + k2 * 32 + 8 * (j / 4) + 4 * hh + (j % 4) > off + qw0 + l32) s[k2][j] = -INFINITY;
   };
   const float c = a.scale_log2;
-  // Row statistics of a score tile: the new running max (raised lazily) and
-  // the rescale factor of O per sub-tile.  Holds every cross-lane operation.
-  auto stats = [&](float4_t (&s)[KT][NT], float (&al)[NT]) -> bool {
-    bool any_resc = false;
+  auto stats = [&](float16v_t (&s)[KB], float &al) -> bool {
+    float mx = s[0][0];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mx = s[0][nt][0];
+    for (int k2 = 0; k2 < KB; ++k2)
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][nt][i]);
-      const float mx2 = across_lg<true>(mx) * c;
-      const bool resc = __any(mx2 > mrow[nt] + kLazyMax);  // wave-uniform
-      const float mn = resc ? fmaxf(mrow[nt], mx2) : mrow[nt];
-      al[nt] = fast_exp2(mrow[nt] - mn);
-      mrow[nt] = mn;
-      any_resc |= resc;
-    }
-    return any_resc;
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[k2][j]);
+    const float mx2 = across_h<true>(mx) * c;
+    const bool resc = __any(mx2 > mrow + kLazyMax);
+    const float mn = resc ? fmaxf(mrow, mx2) : mrow;
+    al = fast_exp2(mrow - mn);
+    mrow = mn;
+    return resc;
   };
-  // scores -> P (rounded to T; bf16 as hi + lo) and the row sums over the same P
-  auto expo = [&](float4_t (&s)[KT][NT], vec8 (&pb)[PS][NT], vec8 (&pl)[Mfma<T>::kSplitP ? PS : 1][NT],
-                  const float (&al)[NT]) {
+  // P for k-step ps: S elements 8 (ps % 2) .. + 7 of block ps / 2 -- the lane's
+  // keys 16 ps + 8 (i / 4) + 4 hh + i % 4, matched by the V^T fragment below
+  auto expo = [&](float16v_t (&s)[KB], vec8 (&pb)[PS], float al) {
+    float ls = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float mn = mrow[nt];
-      float ls = 0.f;
-      if constexpr (Mfma<T>::kSplitP) {
+    for (int ps = 0; ps < PS; ++ps) {
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = fast_exp2(fmaf(s[kt][nt][i], c, -mn));
-            const T hi = (T)p;
-            ls += p;
-            pb[kt >> 1][nt][(kt & 1) * 4 + i] = hi;
-            pl[kt >> 1][nt][(kt & 1) * 4 + i] = (T)(p - (float)hi);
-          }
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pb[kt >> 1][nt][(kt & 1) * 4 + i] = (T)fast_exp2(fmaf(s[kt][nt][i], c, -mn));
-#pragma unroll
-        for (int ps = 0; ps < PS; ++ps) ls = Mfma<T>::sum8(pb[ps][nt], ls);
-      }
-      lrow[nt] = fmaf(lrow[nt], al[nt], ls);
+      for (int i = 0; i < 8; ++i) pb[ps][i] = (T)fast_exp2(fmaf(s[ps / 2][8 * (ps % 2) + i], c, -mrow));
+      ls = Mfma<T>::sum8(pb[ps], ls);
     }
+    lrow = fmaf(lrow, al, ls);
   };
-  // O^T += V_t^T P^T from V slot `slot`
-  auto pv = [&](int slot, const vec8 (&pb)[PS][NT], const vec8 (&pl)[Mfma<T>::kSplitP ? PS : 1][NT]) {
+  // O^T += V_t^T P^T: A operand V^T[d = 32 db + l32][keys 16 ps + 4 hh + 0..3, 16 ps + 8 + 4 hh + 0..3]
+  auto pv = [&](int slot, const vec8 (&pb)[PS]) {
     const T *Vt = Vbuf + slot * LDS::V_ELEMS;
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const T *vrow = Vt + (dt * 16 + l16) * LDS::VSTR + ps * 32 + lg * 4;
+      for (int db = 0; db < DB; ++db) {
+        const T *vrow = Vt + (db * 32 + l32) * LDS::VSTR + ps * 16 + hh * 4;
         const u32x2 lo = *(const u32x2 *)vrow;
-        const u32x2 hi = *(const u32x2 *)(vrow + 16);
+        const u32x2 hi = *(const u32x2 *)(vrow + 8);
         const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
-        const vec8 va = __builtin_bit_cast(vec8, raw);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          oacc[dt][nt] = Mfma<T>::mma(va, pb[ps][nt], oacc[dt][nt]);
-          if constexpr (Mfma<T>::kSplitP) oacc[dt][nt] = Mfma<T>::mma(va, pl[ps][nt], oacc[dt][nt]);
-        }
+        oacc[db] = mma32_f16(__builtin_bit_cast(vec8, raw), pb[ps], oacc[db]);
       }
     }
   };
 
-  // ---- prologue: K_0, V_0, K_1 in LDS; S_0
   load_k(0);
   load_v(0);
   store_k(0, 0);
@@ -710,56 +663,39 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
   }
   __syncthreads();
 
-  float4_t sa[KT][NT], sb[KT][NT];
+  float16v_t sa[KB], sb[KB];
   scores(0, sa);
   if (dlo == 0) mask(0, sa);
 
-  // one tile: softmax(cur) overlapped with nxt = K_{j+1} Q^T, then P V_j
-  auto step = [&](int j, float4_t (&cur)[KT][NT], float4_t (&nxt)[KT][NT]) {
+  auto step = [&](int j, float16v_t (&cur)[KB], float16v_t (&nxt)[KB]) {
     if (j + 2 < n_tiles) load_k(j + 2);
     if (j + 1 < n_tiles) load_v(j + 1);
     __builtin_amdgcn_sched_barrier(0);
-    if (j <= dhi) {  // wave-uniform
-      vec8 pb[PS][NT];
-      vec8 pl[Mfma<T>::kSplitP ? PS : 1][NT];
-      float al[NT];
-      // Raised priority for the tile's math and back to normal for the
-      // staging stores: when both waves of a SIMD are ready, the one with
-      // matrix work issues first (about 2% faster on MI355X, T = 8192).
+    if (j <= dhi) {
+      vec8 pb[PS];
+      float al;
       __builtin_amdgcn_s_setprio(2);
       const bool any_resc = stats(cur, al);
-      // The next tile's scores are computed unconditionally (on the wave's
-      // last tile they go unused: the slot then holds finite stale data or
-      // is never read back), which keeps this block free of branches.
       scores((j + 1) & 1, nxt);
-      expo(cur, pb, pl, al);
+      expo(cur, pb, al);
       {
-        // Interleave: K-fragment reads run a few ahead; each score MFMA is
-        // followed by a share of the exponentials' vector instructions.
-        constexpr int NMF = KT * NT * KS;  // score MFMAs
-        constexpr int NRD = KT * KS;       // K-fragment reads
-        constexpr int VPM = (QW * BN / 64 * (Mfma<T>::kSplitP ? 5 : 3)) / NMF + 1;
+        constexpr int NMF = KB * KS;
+        constexpr int VPM = (QW * BN / 64 * 3) / NMF + 1;
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
         for (int i = 0; i < NMF; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
-          if (i % NT == NT - 1 && i / NT + 4 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (i + 4 < NMF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
       if (any_resc) {
-        // rare: keep it a real branch (the compiler would otherwise run the
-        // multiplies on every tile, since al is 1 when nothing moved)
         asm volatile("" ::);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] *= al[nt];
+        for (int db = 0; db < DB; ++db) oacc[db] *= al;
       }
-      pv(j & 1, pb, pl);
+      pv(j & 1, pb);
       if (j + 1 >= dlo && j + 1 <= dhi) {
-        // once or twice per wave; the opaque tile index keeps the compares
-        // from being hoisted out of the loop as invariants
         int t = j + 1;
         asm volatile("" : "+v"(t));
         mask(t, nxt);
@@ -775,16 +711,17 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QW == 32) ? 2 : 1) void prefil
     if (j + 1 < n_tiles) step(j + 1, sb, sa);
   }
 
-  // normalise and store: lane holds O^T[d = 16dt + 4lg + i][query = qw0 + 16nt + l16]
+  // lane holds O^T[d = 32 db + 8 g + 4 hh + i][query = qw0 + l32]
+  const float inv = 1.0f / across_h<false>(lrow);
+  const int qr = qw0 + l32;
+  if (qr < Tn) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const float inv = 1.0f / across_lg<false>(lrow[nt]);
-    const int qr = qw0 + nt * 16 + l16;
-    if (qr < Tn) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        store4(a.o, ((size_t)bh * Tn + qr) * D + dt * 16 + lg * 4, oacc[dt][nt], inv, a.o_dt);
-    }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4_t x = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+        store4(a.o, ((size_t)bh * Tn + qr) * D + db * 32 + 8 * g4 + 4 * hh, x, inv, a.o_dt);
+      }
   }
 }
 
@@ -888,7 +825,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 }
 
 // Tile configurations, chosen by measurement on MI355X: the pipelined kernel
-// (8 waves of 32 query rows, 64-key tiles) wins for f16 at D = 128; bf16 there
+// (8 waves of 32 query rows, 64-key tiles, 32x32x16 MFMA) wins for f16 at
+// D = 128; bf16 there
 // (which carries P as two parts and would spill) and the smaller head dims are
 // faster with the plain kernel (4 waves of 32 rows; 128-key tiles at D = 32).
 template <typename T, int D>
@@ -932,8 +870,8 @@ static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
     // the plain kernel takes the window mask, and prompts whose K/V slab does
     // not fit the 32-bit range of the pipelined kernel's buffer loads
     if (a.window > 0 || (size_t)a.T * D * sizeof(T) >= ((size_t)1 << 31)) return launch_extend_mfma<T, D>(a, s);
-    return launch_with_lds(prefill_pipe_kernel<T, D, C::QW, C::BN, C::NW>, grid, C::NW * 64,
-                           PipeLds<D, C::BN>::BYTES, s, attr_done, a);
+    return launch_with_lds(prefill_pipe_kernel<D, C::BN>, grid, C::NW * 64, PipeLds<D, C::BN>::BYTES, s,
+                           attr_done, a);
   } else {
     return launch_with_lds(prefill_mfma_kernel<T, D, C::QW, C::BN, C::NW>, grid, C::NW * 64,
                            PrefillLds<D, C::BN>::BYTES, s, attr_done, a);
@@ -961,8 +899,8 @@ static hipError_t launch_extend_mfma(const PrefillArgs &a, hipStream_t s) {
       constexpr int PBM = C::NW * C::QW;
       const dim3 pgrid((unsigned)((a.T + PBM - 1) / PBM) * a.batch * a.q_heads);
       static std::atomic<uint64_t> attr_pipe{0};
-      return launch_with_lds(prefill_pipe_kernel<T, D, C::QW, C::BN, C::NW>, pgrid, C::NW * 64,
-                             PipeLds<D, C::BN>::BYTES, s, attr_pipe, a);
+      return launch_with_lds(prefill_pipe_kernel<D, C::BN>, pgrid, C::NW * 64, PipeLds<D, C::BN>::BYTES, s,
+                             attr_pipe, a);
     }
   }
   constexpr int NW = 4, QW = 32, BN = D == 32 ? 128 : 64, BM = NW * QW;
