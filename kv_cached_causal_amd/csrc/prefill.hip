@@ -462,7 +462,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
   constexpr int PS = BN / 16;    // P V k-steps over keys
   constexpr int KCH = BN * D / 8 / 256;
   constexpr int VPAIRS = (BN / 4) * (D / 8);
-  static_assert(KCH == 4 && VPAIRS == 256, "one 16-byte chunk set per staging thread");
+  static_assert(KCH >= 1 && KCH <= 4 && BN * D / 8 == KCH * 256, "K tile: 1-4 chunks per staging thread");
+  static_assert(VPAIRS <= 256 && VPAIRS % 64 == 0, "V tile must cover whole waves");
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T *const Kbuf = reinterpret_cast<T *>(smem_raw);
@@ -535,8 +536,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
       }
     }
   };
+  // waves 4-7 stage V, (4-key group, 8-column slice) pairs of the tile
+  const bool stage_v = !stage_k && stid < VPAIRS;
   auto load_v = [&](int t) {
-    if (!stage_k) {
+    if (stage_v) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         sreg[r] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + r * D * (int)sizeof(T), t * BN * D * (int)sizeof(T), 0);
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
     }
   };
   auto store_v = [&](int t, int slot) {
-    if (!stage_k) {
+    if (stage_v) {
       T *Vt = Vbuf + slot * LDS::V_ELEMS;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -826,12 +829,13 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 
 // Tile configurations, chosen by measurement on MI355X: the pipelined kernel
 // (8 waves of 32 query rows, 64-key tiles, 32x32x16 MFMA) wins for f16 at
-// D = 128; bf16 there
-// (which carries P as two parts and would spill) and the smaller head dims are
-// faster with the plain kernel (4 waves of 32 rows; 128-key tiles at D = 32).
+// D = 128 and D = 64 (B = 4, 12 heads, T = 2048: 65 against 76 us); bf16
+// (which carries P as two parts and would spill) and f16 at D = 32 (173
+// against 163 us at T = 8192, 16 heads) are faster with the plain kernel
+// (4 waves of 32 rows; 128-key tiles at D = 32).
 template <typename T, int D>
 struct PrefillConfig {
-  static constexpr bool kPipe = std::is_same<T, half_t>::value && D == 128;
+  static constexpr bool kPipe = std::is_same<T, half_t>::value && (D == 64 || D == 128);
   static constexpr int NW = kPipe ? 8 : 4;
   static constexpr int QW = 32;
   static constexpr int BN = (!kPipe && D == 32) ? 128 : 64;
@@ -886,7 +890,7 @@ static hipError_t launch_f32(const PrefillArgs &a, hipStream_t s) {
 }
 
 // Extend (queries after a cached prefix, K/V read from the cache): the
-// pipelined kernel where the prompt uses it (f16, D = 128; no window, no block
+// pipelined kernel where the prompt uses it (f16, D = 64 or 128; no window, no block
 // table), else the plain kernel for every 16-bit type and head dim, the vector
 // kernel for fp32.
 template <typename T, int D>
