@@ -828,17 +828,18 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 }
 
 // Tile configurations, chosen by measurement on MI355X: the pipelined kernel
-// (8 waves of 32 query rows, 64-key tiles, 32x32x16 MFMA) wins for f16 at
-// D = 128 and D = 64 (B = 4, 12 heads, T = 2048: 65 against 76 us); bf16
-// (which carries P as two parts and would spill) and f16 at D = 32 (173
-// against 163 us at T = 8192, 16 heads) are faster with the plain kernel
-// (4 waves of 32 rows; 128-key tiles at D = 32).
+// (8 waves of 32 query rows, 32x32x16 MFMA) for f16 at every head dim, with
+// 64-key tiles at D = 64 and 128 and 128-key tiles at D = 32 (against the
+// plain kernel: B = 4, 12 heads, T = 2048, D = 64: 65 against 76 us;
+// T = 8192, 16 heads, D = 32: 155 against 165 us); bf16, which carries P as
+// two parts and would spill there, takes the plain kernel (4 waves of 32
+// rows; 128-key tiles at D = 32).
 template <typename T, int D>
 struct PrefillConfig {
-  static constexpr bool kPipe = std::is_same<T, half_t>::value && (D == 64 || D == 128);
+  static constexpr bool kPipe = std::is_same<T, half_t>::value;
   static constexpr int NW = kPipe ? 8 : 4;
   static constexpr int QW = 32;
-  static constexpr int BN = (!kPipe && D == 32) ? 128 : 64;
+  static constexpr int BN = D == 32 ? 128 : 64;
 };
 
 // Launch with `lds` bytes of dynamic LDS.  The kernel's maximum dynamic LDS
@@ -890,7 +891,7 @@ static hipError_t launch_f32(const PrefillArgs &a, hipStream_t s) {
 }
 
 // Extend (queries after a cached prefix, K/V read from the cache): the
-// pipelined kernel where the prompt uses it (f16, D = 64 or 128; no window, no block
+// pipelined kernel where the prompt uses it (f16; no window, no block
 // table), else the plain kernel for every 16-bit type and head dim, the vector
 // kernel for fp32.
 template <typename T, int D>
