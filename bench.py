@@ -90,7 +90,7 @@ TRAFFIC_KERNELS = {
                                            "decode_merge_kernel<128, 1>"]),
     "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4, 4, 1, 4, false, false>",
                                         "decode_merge_kernel<128, 4>"]),
-    "prefill_t8192": (PREFILL_SOURCES, ["prefill_pipe_kernel<128, 64>"]),
+    "prefill_t8192": (PREFILL_SOURCES, ["prefill_pipe_kernelIDF16_Li128"]),
 }
 
 
@@ -743,7 +743,7 @@ def main():
                           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                                        "traffic": traffic_from_profiles("prefill_t8192", pre_hash),
-                                       "kernel": "prefill_pipe_kernel<D=128> (f16, 8 waves x 32 query rows, 64-key tiles, 32x32x16 MFMA)",
+                                       "kernel": "prefill_pipe_kernel<f16, D=128> (8 waves x 32 query rows, 64-key tiles, 32x32x16 MFMA)",
                                        "algorithmic_flops_per_launch": pre["flops_layer"],
                                        "mean_launch_ms": round(k_ms, 5)}}
         if "value" not in out:

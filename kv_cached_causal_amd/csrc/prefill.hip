@@ -411,7 +411,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
 }
 
 // ---------------------------------------------------------------- pipelined kernel
-// Software-pipelined variant (f16): while the vector ALUs turn the scores of
+// Software-pipelined variant: while the vector ALUs turn the scores of
 // tile j into P (max, exp2, rounding, row sums), the matrix cores already
 // compute the scores of tile j+1; then P_j V_j runs.  K and V live in separate
 // two-deep LDS rings: iteration j reads K_{j+1} and V_j and stages K_{j+2} and
@@ -419,7 +419,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
 // rescale of O, the causal mask of a wave's diagonal tiles) sit between the
 // overlapped blocks.
 //
-// Both products run on v_mfma_f32_32x32x16_f16, whose 32 output columns are a
+// Both products run on v_mfma_f32_32x32x16_{f16,bf16} (bf16 carries P as hi +
+// lo parts, two P V MFMAs), whose 32 output columns are a
 // wave's 32 query rows: S^T = K Q^T (two 32-key blocks per 64-key tile, eight
 // k-steps over D = 128) and O^T += V^T P^T (four 32-wide d-blocks, four
 // 16-key k-steps).  A lane then holds one query column (lanes l and l ^ 32 the
@@ -439,8 +440,11 @@ struct PipeLds {
 };
 
 typedef float float16v_t __attribute__((ext_vector_type(16)));
-__device__ __forceinline__ float16v_t mma32_f16(const half8_t &a, const half8_t &b, const float16v_t &c) {
+__device__ __forceinline__ float16v_t mma32(const half8_t &a, const half8_t &b, const float16v_t &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float16v_t mma32(const bf168_t &a, const bf168_t &b, const float16v_t &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 // x combined over lanes l and l ^ 32 (the two lanes holding one query column)
 template <bool MAX>
@@ -449,10 +453,10 @@ __device__ __forceinline__ float across_h(float x) {
   return MAX ? fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])) : __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int BN>
+template <typename T, int D, int BN>
 __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
-  typedef half_t T;
-  typedef half8_t vec8;
+  typedef typename Mfma<T>::vec vec8;
+  constexpr bool SPL = Mfma<T>::kSplitP;
   typedef PipeLds<D, BN> LDS;
   constexpr int NW = 8, QW = 32;
   constexpr int BM = NW * QW;
@@ -603,7 +607,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
 #pragma unroll
       for (int k2 = 0; k2 < KB; ++k2) {
         const vec8 ka = *(const vec8 *)(Ks + (k2 * 32 + l32) * LDS::KSTR + ks * 16 + hh * 8);
-        s[k2] = mma32_f16(ka, qf[ks], s[k2]);
+        s[k2] = mma32(ka, qf[ks], s[k2]);
       }
     }
   };
@@ -630,18 +634,30 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
   };
   // P for k-step ps: S elements 8 (ps % 2) .. + 7 of block ps / 2 -- the lane's
   // keys 16 ps + 8 (i / 4) + 4 hh + i % 4, matched by the V^T fragment below
-  auto expo = [&](float16v_t (&s)[KB], vec8 (&pb)[PS], float al) {
+  auto expo = [&](float16v_t (&s)[KB], vec8 (&pb)[PS], vec8 (&pl)[SPL ? PS : 1], float al) {
     float ls = 0.f;
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps) {
+      if constexpr (SPL) {
+        // bf16 keeps 8 significand bits: P as hi + lo parts, the sum in fp32
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[ps][i] = (T)fast_exp2(fmaf(s[ps / 2][8 * (ps % 2) + i], c, -mrow));
-      ls = Mfma<T>::sum8(pb[ps], ls);
+        for (int i = 0; i < 8; ++i) {
+          const float p = fast_exp2(fmaf(s[ps / 2][8 * (ps % 2) + i], c, -mrow));
+          const T hi = (T)p;
+          ls += p;
+          pb[ps][i] = hi;
+          pl[ps][i] = (T)(p - (float)hi);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[ps][i] = (T)fast_exp2(fmaf(s[ps / 2][8 * (ps % 2) + i], c, -mrow));
+        ls = Mfma<T>::sum8(pb[ps], ls);
+      }
     }
     lrow = fmaf(lrow, al, ls);
   };
   // O^T += V_t^T P^T: A operand V^T[d = 32 db + l32][keys 16 ps + 4 hh + 0..3, 16 ps + 8 + 4 hh + 0..3]
-  auto pv = [&](int slot, const vec8 (&pb)[PS]) {
+  auto pv = [&](int slot, const vec8 (&pb)[PS], const vec8 (&pl)[SPL ? PS : 1]) {
     const T *Vt = Vbuf + slot * LDS::V_ELEMS;
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps) {
@@ -651,7 +667,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
         const u32x2 lo = *(const u32x2 *)vrow;
         const u32x2 hi = *(const u32x2 *)(vrow + 8);
         const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = mma32_f16(__builtin_bit_cast(vec8, raw), pb[ps], oacc[db]);
+        const vec8 va = __builtin_bit_cast(vec8, raw);
+        oacc[db] = mma32(va, pb[ps], oacc[db]);
+        if constexpr (SPL) oacc[db] = mma32(va, pl[ps], oacc[db]);
       }
     }
   };
@@ -676,14 +694,15 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     if (j <= dhi) {
       vec8 pb[PS];
+      vec8 pl[SPL ? PS : 1];
       float al;
       __builtin_amdgcn_s_setprio(2);
       const bool any_resc = stats(cur, al);
       scores((j + 1) & 1, nxt);
-      expo(cur, pb, al);
+      expo(cur, pb, pl, al);
       {
         constexpr int NMF = KB * KS;
-        constexpr int VPM = (QW * BN / 64 * 3) / NMF + 1;
+        constexpr int VPM = (QW * BN / 64 * (SPL ? 5 : 3)) / NMF + 1;
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
         for (int i = 0; i < NMF; ++i) {
@@ -697,7 +716,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] *= al;
       }
-      pv(j & 1, pb);
+      pv(j & 1, pb, pl);
       if (j + 1 >= dlo && j + 1 <= dhi) {
         int t = j + 1;
         asm volatile("" : "+v"(t));
@@ -828,15 +847,16 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 }
 
 // Tile configurations, chosen by measurement on MI355X: the pipelined kernel
-// (8 waves of 32 query rows, 32x32x16 MFMA) for f16 at every head dim, with
-// 64-key tiles at D = 64 and 128 and 128-key tiles at D = 32 (against the
-// plain kernel: B = 4, 12 heads, T = 2048, D = 64: 65 against 76 us;
-// T = 8192, 16 heads, D = 32: 155 against 165 us); bf16, which carries P as
-// two parts and would spill there, takes the plain kernel (4 waves of 32
-// rows; 128-key tiles at D = 32).
+// (8 waves of 32 query rows, 32x32x16 MFMA) for f16 at every head dim and for
+// bf16 at D = 64 and 128, with 64-key tiles at D = 64 and 128 and 128-key
+// tiles at D = 32 (against the plain kernel: B = 4, 12 heads, T = 2048,
+// D = 64: 65 against 76 us in f16, 78 against 90 us in bf16; T = 8192,
+// 16 heads, D = 32: 155 against 165 us; T = 8192, 32 heads, D = 128 in
+// bf16: 815 against 878 us).  bf16 at D = 32, whose two-part P would spill
+// heavily with 128-key tiles, takes the plain kernel (4 waves of 32 rows).
 template <typename T, int D>
 struct PrefillConfig {
-  static constexpr bool kPipe = std::is_same<T, half_t>::value;
+  static constexpr bool kPipe = std::is_same<T, half_t>::value || D != 32;
   static constexpr int NW = kPipe ? 8 : 4;
   static constexpr int QW = 32;
   static constexpr int BN = D == 32 ? 128 : 64;
@@ -875,7 +895,7 @@ static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
     // the plain kernel takes the window mask, and prompts whose K/V slab does
     // not fit the 32-bit range of the pipelined kernel's buffer loads
     if (a.window > 0 || (size_t)a.T * D * sizeof(T) >= ((size_t)1 << 31)) return launch_extend_mfma<T, D>(a, s);
-    return launch_with_lds(prefill_pipe_kernel<D, C::BN>, grid, C::NW * 64, PipeLds<D, C::BN>::BYTES, s,
+    return launch_with_lds(prefill_pipe_kernel<T, D, C::BN>, grid, C::NW * 64, PipeLds<D, C::BN>::BYTES, s,
                            attr_done, a);
   } else {
     return launch_with_lds(prefill_mfma_kernel<T, D, C::QW, C::BN, C::NW>, grid, C::NW * 64,
@@ -891,7 +911,7 @@ static hipError_t launch_f32(const PrefillArgs &a, hipStream_t s) {
 }
 
 // Extend (queries after a cached prefix, K/V read from the cache): the
-// pipelined kernel where the prompt uses it (f16; no window, no block
+// pipelined kernel where the prompt uses it (16-bit types; no window, no block
 // table), else the plain kernel for every 16-bit type and head dim, the vector
 // kernel for fp32.
 template <typename T, int D>
@@ -904,7 +924,7 @@ static hipError_t launch_extend_mfma(const PrefillArgs &a, hipStream_t s) {
       constexpr int PBM = C::NW * C::QW;
       const dim3 pgrid((unsigned)((a.T + PBM - 1) / PBM) * a.batch * a.q_heads);
       static std::atomic<uint64_t> attr_pipe{0};
-      return launch_with_lds(prefill_pipe_kernel<D, C::BN>, pgrid, C::NW * 64, PipeLds<D, C::BN>::BYTES, s,
+      return launch_with_lds(prefill_pipe_kernel<T, D, C::BN>, pgrid, C::NW * 64, PipeLds<D, C::BN>::BYTES, s,
                              attr_pipe, a);
     }
   }

@@ -250,12 +250,11 @@ def test_paged_extend_matches_oracle(dtype, bs):
 def test_paged_extend_equals_contiguous_bitwise(dtype, heads):
     """A 4-token verification after ragged prefixes, through shuffled 32-position
     blocks and through a contiguous cache.  Where both run the same kernel the
-    outputs are bit-identical: the decode kernels' short-extend form (G = 1)
-    and the plain prefill kernel (bf16, G = 4).  An f16 extend at D = 128 with
-    G = 4 runs the pipelined kernel (32x32 MFMA) on the contiguous cache and the
-    plain kernel through the block tables: the two sum in different orders, so
-    they agree to rounding (each is checked against the oracle in its own
-    test)."""
+    outputs are bit-identical: the decode kernels' short-extend form (G = 1).
+    An extend at D = 128 with G = 4 runs the pipelined kernel (32x32 MFMA) on
+    the contiguous cache and the plain kernel through the block tables: the
+    two sum in different orders, so they agree to rounding (each is checked
+    against the oracle in its own test)."""
     kv = _kv()
     (H, Hkv), D, bs, T = heads, 128, 32, 4
     lens = [5, 385, 999]
@@ -283,7 +282,7 @@ def test_paged_extend_equals_contiguous_bitwise(dtype, heads):
     a = flat.extend(0, to_dev(q, dtype), to_dev(kn, dtype), to_dev(vn, dtype), out_dtype=torch.float32)
     b = paged.extend(0, to_dev(q, dtype), to_dev(kn, dtype), to_dev(vn, dtype), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    if dtype == "f16" and H // Hkv == 4:
+    if H // Hkv == 4:
         err = (a - b).abs().max().item()
         assert err <= 1e-3, err
     else:
