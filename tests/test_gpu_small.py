@@ -270,3 +270,24 @@ def test_bound_calls_match_regular_calls(dtype):
         c.close()
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+def test_measurement_aids_run():
+    """The plain kernels bench.py reads the device's ceilings with (a streaming
+    read, an fp16 MFMA loop, an exp2 loop) launch and finish on small grids;
+    their sinks stay untouched (they only write on an unlikely value)."""
+    import ctypes
+    kv = _kv()
+    lib = kv.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    buf = torch.arange(1 << 18, dtype=torch.int32, device="cuda")
+    sink_u = torch.zeros(64, dtype=torch.int32, device="cuda")
+    sink_f = torch.zeros(64, dtype=torch.float32, device="cuda")
+    say("measurement aids: stream read, MFMA loop, exp2 loop")
+    assert lib.kvattn_measure_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * 4, 64,
+                                          ctypes.c_void_p(sink_u.data_ptr()), stream) == 0
+    assert lib.kvattn_measure_mfma_f16(64, 50, ctypes.c_void_p(sink_f.data_ptr()), stream) == 0
+    assert lib.kvattn_measure_exp2(64, 50, ctypes.c_void_p(sink_f.data_ptr()), stream) == 0
+    torch.cuda.synchronize()
+    assert int(sink_u.abs().sum()) == 0 and float(sink_f.abs().sum()) == 0.0
+    assert lib.kvattn_measure_exp2_count(64, 50) == 64 * 256 * 50 * 8
