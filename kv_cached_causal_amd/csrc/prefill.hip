@@ -7,14 +7,18 @@
 // T x T score matrix to device memory.  The README's chunked attention with
 // the online-softmax recurrence is the algebra used here, tile by tile.
 //
-// gfx950 design (F16/BF16): a workgroup is 4 wave64s and owns BM = 4*QW query
-// rows of one (b, h).  Each wave keeps its QW query rows in registers as MFMA
-// operands and computes, per K/V tile of BN keys staged through LDS,
-//     S^T = K Q^T   (v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulate)
+// gfx950 design (F16/BF16): a workgroup owns a block of query rows of one
+// (b, h); each wave keeps its 32 query rows in registers as MFMA operands and
+// computes, per K/V tile of BN keys staged through LDS,
+//     S^T = K Q^T   (fp32 accumulate)
 //     O^T += V^T P^T
+// The plain kernel below (4 waves, v_mfma_f32_16x16x32) serves windows, block
+// tables and bf16 at D = 32; the pipelined kernel further down (8 waves,
+// v_mfma_f32_32x32x16, the next tile's scores overlapped with this tile's
+// softmax) serves the other prompts and extends.
 // The transposed orientation puts one query in one lane column for both
 // products, so the running max / sum and the rescale of O stay per-lane; row
-// statistics need only two cross-lane steps per tile.  V is transposed while
+// statistics need two cross-lane steps per tile (one with the 32x32 shape).  V is transposed while
 // it is staged to LDS so that its reduction axis (keys) is contiguous for the
 // MFMA operand.  Tiles past the diagonal are never visited.  The workgroups
 // that own the diagonal tile of the first query head of a KV group also
