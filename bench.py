@@ -182,7 +182,7 @@ def measure_mfma_ceiling(kv, dev, workgroups=1024, iters=20000, reps=5):
     return flops / (a.elapsed_time(b) / reps * 1e-3) / 1e12
 
 
-def measure_exp_ceiling(kv, dev, workgroups=1024, iters=20000, reps=5):
+def measure_exp_ceiling(kv, dev, workgroups=4096, iters=5000, reps=5):
     """exp2 rate of this device (plain v_exp_f32 loop of the library), exponentials per second."""
     import ctypes
     sink = torch.zeros(workgroups, dtype=torch.float32, device=dev)

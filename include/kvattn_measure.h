@@ -47,7 +47,7 @@ int kvattn_measure_mfma_f16(int workgroups, int iters, float *sink, void *stream
 double kvattn_measure_mfma_f16_flops(int workgroups, int iters);
 
 /* Enqueue on `stream` a plain exponential loop: `workgroups` workgroups of 256
- * threads, each thread running `iters` rounds of eight independent chains
+ * threads, each thread running `iters` rounds of 32 independent chains
  * x <- exp2(-x) (one v_exp_f32 per exponential, fp32), with no memory
  * traffic in the loop.  The sums are written to sink[blockIdx] (a device
  * array of at least `workgroups` floats) only if they equal an unlikely

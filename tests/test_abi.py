@@ -134,8 +134,8 @@ def test_measure_exp2_validates_on_host_and_counts():
     assert lib.kvattn_measure_exp2(0, 10, fake, None) == -1
     assert lib.kvattn_measure_exp2(8, 0, fake, None) == -1
     assert lib.kvattn_measure_exp2(8, 10, None, None) == -1
-    # 256 threads x 8 chains per round
-    assert lib.kvattn_measure_exp2_count(3, 5) == 3 * 256 * 5 * 8
+    # 256 threads x 32 chains per round
+    assert lib.kvattn_measure_exp2_count(3, 5) == 3 * 256 * 5 * 32
     assert lib.kvattn_measure_exp2_count(0, 5) == 0.0
 
 

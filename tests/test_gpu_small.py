@@ -290,4 +290,4 @@ def test_measurement_aids_run():
     assert lib.kvattn_measure_exp2(64, 50, ctypes.c_void_p(sink_f.data_ptr()), stream) == 0
     torch.cuda.synchronize()
     assert int(sink_u.abs().sum()) == 0 and float(sink_f.abs().sum()) == 0.0
-    assert lib.kvattn_measure_exp2_count(64, 50) == 64 * 256 * 50 * 8
+    assert lib.kvattn_measure_exp2_count(64, 50) == 64 * 256 * 50 * 32
