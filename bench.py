@@ -240,6 +240,64 @@ def small_head_prefill(kv, dev, mceil, eceil, reps=20):
             "frac_of_exp_ceiling": round(exps / eceil / med, 4)}
 
 
+def small_config_measurements(kv, dev):
+    """The three small workloads, whole: prompt prefill of every layer, then every decode step
+    (append + decode per layer), timed with HIP events per launch.  Their caches (0.3-69 MB) stay in
+    the 256 MB last-level cache and their launches take a few microseconds, so they are reported in
+    microseconds per step (launch-bound), not as bandwidth."""
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    out = {}
+    for cfg in (1, 2, 3):
+        w = si.WORKLOADS[cfg]
+        dt = tdt[w.dtype]
+        B, H, Hkv, D, T, L = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.prompt, w.layers
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(100 + cfg)
+        rnd = lambda shape: torch.randn(shape, generator=gen, device=dev).to(dt)
+        c = kv.KVCache(L, B, H, Hkv, D, w.max_T, dt, device=dev)
+        pre = [c.bind_prefill(l, rnd((B, H, T, D)), rnd((B, Hkv, T, D)), rnd((B, Hkv, T, D)),
+                              torch.empty((B, H, T, D), dtype=dt, device=dev), scale=w.scale) for l in range(L)]
+        kn, vn, qd = rnd((B, Hkv, 1, D)), rnd((B, Hkv, 1, D)), rnd((B, H, 1, D))
+        od = torch.empty((B, H, 1, D), dtype=dt, device=dev)
+        app = [c.bind_append(l, kn, vn) for l in range(L)]
+        dec = [c.bind_decode(l, qd, od, scale=w.scale) for l in range(L)]
+
+        def run(record):
+            c.set_lengths([0] * B)
+            t_pre, t_step = [], []
+            for l in range(L):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                pre[l]()
+                b.record()
+                t_pre.append((a, b))
+            for _ in range(w.steps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for l in range(L):
+                    app[l]()
+                    dec[l]()
+                b.record()
+                t_step.append((a, b))
+            torch.cuda.synchronize()
+            if record:
+                return ([x.elapsed_time(y) for x, y in t_pre], [x.elapsed_time(y) for x, y in t_step])
+        run(False)
+        tp, ts = run(True)
+        c.close()
+        pre_ms, step_ms = statistics.median(tp), statistics.median(ts)
+        flops = 4.0 * B * H * D * T * (T + 1) / 2
+        out[w.name] = {"prefill_us_per_layer": round(pre_ms * 1e3, 1),
+                       "prefill_tflops": round(flops / (pre_ms * 1e-3) / 1e12, 2),
+                       "decode_step_us": round(step_ms * 1e3, 1),
+                       "decode_us_per_layer": round(step_ms * 1e3 / L, 2),
+                       "decode_tok_s": round(B / (step_ms * 1e-3), 1),
+                       "whole_run_ms": round(sum(tp) + sum(ts), 3),
+                       "note": f"{L} layer(s), B={B}, {H}/{Hkv} heads, D={D}, {w.dtype}: prompt {T} then "
+                               f"{w.steps} steps; launch-bound, cache-resident"}
+    return out
+
+
 def calibration_kernels(kv, dev):
     """A plain read and a fill of CALIB_BYTES each (run under --pmc to calibrate the HBM counters)."""
     import ctypes
@@ -803,6 +861,9 @@ def main():
         if not args.no_extras:
             log("small-head prefill (T=8192, 16 heads of D=32)")
             out["prefill_d32"] = small_head_prefill(kv, dev, mceil, eceil)
+    if args.only is None and not args.no_extras:
+        log("small workloads (configs 1-3), whole")
+        out["small_configs"] = small_config_measurements(kv, dev)
     if args.calibrate:
         calibration_kernels(kv, dev)
     if not args.no_cpu_baseline:

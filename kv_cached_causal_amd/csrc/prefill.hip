@@ -24,7 +24,7 @@
 // that own the diagonal tile of the first query head of a KV group also
 // store that K/V tile into the cache from the registers it was loaded into.
 //
-// F32 takes a plain vector-ALU kernel (one lane per query row).
+// F32 takes a plain vector-ALU kernel (four lanes per query row).
 #include <atomic>
 #include <type_traits>
 
@@ -752,17 +752,25 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------- fp32 path
-// One wave per (64-query tile, b, h); lane = query row; keys staged in LDS in
-// tiles of 32, each tile folded into the row's (m, l, o) state.
+// Vector-ALU kernel: one wave per (16-query tile, b, h); four lanes per query
+// row, each holding a contiguous quarter of the head dim, so a score is a
+// quarter dot product per lane plus two in-quad DPP additions, and each lane
+// accumulates its quarter of O.  Keys are staged in LDS in tiles of 32, each
+// tile folded into the row's (m, l, o) state.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+  return x;
+}
 template <int D>
 __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
-  constexpr int BMF = 64, BNF = 32;
+  constexpr int RPW = 16, LPQ = 4, DL = D / LPQ, BNF = 32;
   __shared__ float Ks[BNF][D];
   __shared__ float Vs[BNF][D];
   const int Tn = a.T;
   const int H = a.q_heads;
   const int G = H / a.kv_heads;
-  const int n_qt = (Tn + BMF - 1) / BMF;
+  const int n_qt = (Tn + RPW - 1) / RPW;
   const int BH = a.batch * H;
   const int qt = n_qt - 1 - (int)(blockIdx.x / BH);
   const int bh = blockIdx.x % BH;
@@ -770,8 +778,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   const int h = bh - b * H;
   const int g = h / G;
   const bool writer = (h - g * G) == 0;
-  const int q0 = qt * BMF;
-  const int row = q0 + threadIdx.x;
+  const int q0 = qt * RPW;
+  const int row = q0 + (int)threadIdx.x / LPQ;
+  const int d0 = ((int)threadIdx.x % LPQ) * DL;  // this lane's slice of the head dim
 
   const float *qb = (const float *)a.q + (size_t)bh * Tn * D;
   const int off = a.offsets ? a.offsets[b] : 0;  // absolute position of query row 0
@@ -782,16 +791,17 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   float *cvb = (float *)a.cache_v + (size_t)(b * a.kv_heads + g) * a.max_T * D;
   if (a.write_cache && qt == 0 && h == 0 && threadIdx.x == 0) a.len[b] = Tn;
 
-  float qr[D], o[D];
+  float qr[DL], o[DL];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    qr[d] = row < Tn ? qb[(size_t)row * D + d] : 0.f;
-    o[d] = 0.f;
+  for (int i = 0; i < DL; ++i) {
+    qr[i] = row < Tn ? qb[(size_t)row * D + d0 + i] : 0.f;
+    o[i] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
   const float c = a.scale_log2;
-  const int kv_end = off + min(q0 + BMF, Tn);
+  const int kv_end = off + min(q0 + RPW, Tn);
   const int W = a.window, S = a.sink;
+  const int pos = off + row;
   for (int k0 = 0; k0 < kv_end; k0 += BNF) {
     // workgroup-uniform: a tile older than every row's window and past the sink is never read
     if (W > 0 && k0 >= S && k0 + BNF - 1 <= off + q0 - W) continue;
@@ -805,8 +815,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
                                   : (size_t)key;
         kx = kb[rk * D + d];
         vx = vb[rk * D + d];
-        if (a.write_cache && writer && key >= q0) {
-          // bit copy: reinterpret, never round
+        if (a.write_cache && writer && key >= q0 && key < q0 + RPW) {
+          // bit copy of this tile's own rows: reinterpret, never round
           ((uint32_t *)ckb)[(size_t)key * D + d] = __float_as_uint(kx);
           ((uint32_t *)cvb)[(size_t)key * D + d] = __float_as_uint(vx);
         }
@@ -821,8 +831,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     for (int j = 0; j < BNF; ++j) {
       float acc = 0.f;
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc = fmaf(qr[d], Ks[j][d], acc);
-      const int key = k0 + j, pos = off + row;
+      for (int i = 0; i < DL; ++i) acc = fmaf(qr[i], Ks[j][d0 + i], acc);
+      acc = quad_sum(acc);
+      const int key = k0 + j;
       const bool vis = key <= pos && (W == 0 || pos - key < W || key < S);
       s[j] = vis ? acc * c : -INFINITY;
       mx = fmaxf(mx, s[j]);
@@ -832,21 +843,21 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     const float al = fast_exp2(m - ms);
     l *= al;
 #pragma unroll
-    for (int d = 0; d < D; ++d) o[d] *= al;
+    for (int i = 0; i < DL; ++i) o[i] *= al;
 #pragma unroll
     for (int j = 0; j < BNF; ++j) {
       const float p = fast_exp2(s[j] - ms);
       l += p;
 #pragma unroll
-      for (int d = 0; d < D; ++d) o[d] = fmaf(p, Vs[j][d], o[d]);
+      for (int i = 0; i < DL; ++i) o[i] = fmaf(p, Vs[j][d0 + i], o[i]);
     }
     m = mn;
   }
   if (row < Tn) {
     const float inv = 1.0f / l;
-    float *ob = (float *)a.o + ((size_t)bh * Tn + row) * D;
+    float *ob = (float *)a.o + ((size_t)bh * Tn + row) * D + d0;
 #pragma unroll
-    for (int d = 0; d < D; ++d) ob[d] = o[d] * inv;
+    for (int i = 0; i < DL; ++i) ob[i] = o[i] * inv;
   }
 }
 
@@ -909,7 +920,7 @@ static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
 
 template <int D>
 static hipError_t launch_f32(const PrefillArgs &a, hipStream_t s) {
-  const int n_qt = (a.T + 63) / 64;
+  const int n_qt = (a.T + 15) / 16;  // 16 query rows per workgroup
   prefill_f32_kernel<D><<<dim3((unsigned)n_qt * a.batch * a.q_heads), 64, 0, s>>>(a);
   return hipGetLastError();
 }
