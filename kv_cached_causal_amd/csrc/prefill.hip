@@ -752,21 +752,35 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------- fp32 path
-// Vector-ALU kernel: one wave per (16-query tile, b, h); four lanes per query
-// row, each holding a contiguous quarter of the head dim, so a score is a
-// quarter dot product per lane plus two in-quad DPP additions, and each lane
-// accumulates its quarter of O.  Keys are staged in LDS in tiles of 32, each
-// tile folded into the row's (m, l, o) state.
+// Vector-ALU kernel: one workgroup of four waves per (16-query tile, b, h).
+// Four lanes per query row, each holding a contiguous quarter of the head
+// dim, so a score is a quarter dot product per lane plus two in-quad DPP
+// additions, and each lane accumulates its quarter of O.  Keys are staged in
+// LDS in tiles of 4096 / D rows, every lane issuing its four 16-byte K and
+// four V loads of a tile at once, with the next tile's loads in flight while
+// the current one is folded in; each wave folds a quarter of every tile into
+// its own (m, l, o) state, and the four states are merged at the end by the
+// chunked-softmax rule (the prompts this kernel serves are short, so the work
+// of one query tile is spread over four waves to cut its latency).
 __device__ __forceinline__ float quad_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
   return x;
 }
+constexpr int kF32Waves = 4;
 template <int D>
-__global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
-  constexpr int RPW = 16, LPQ = 4, DL = D / LPQ, BNF = 32;
-  __shared__ float Ks[BNF][D];
-  __shared__ float Vs[BNF][D];
+__global__ __launch_bounds__(64 * kF32Waves) void prefill_f32_kernel(PrefillArgs a) {
+  constexpr int NWF = kF32Waves, RPW = 16, LPQ = 4, DL = D / LPQ;
+  constexpr int BNF = 4096 / D;       // keys per tile
+  constexpr int KPW = BNF / NWF;      // keys of a tile per wave
+  constexpr int C4 = D / 4;           // 16-byte chunks per row
+  constexpr int NV = BNF * C4 / (64 * NWF);  // 16-byte loads per thread per tile, of K and of V
+  static_assert(NV * 64 * NWF == BNF * C4, "tile chunks must cover the workgroup");
+  // K/V tiles while streaming; the waves' (m, l, o) states for the final merge
+  constexpr int STAGE_F = 2 * BNF * D, MERGE_F = NWF * 64 * (DL + 2);
+  __shared__ float4_t lds4[(STAGE_F > MERGE_F ? STAGE_F : MERGE_F) / 4];
+  float4_t(*Ks)[C4] = (float4_t(*)[C4])lds4;
+  float4_t(*Vs)[C4] = (float4_t(*)[C4])(lds4 + BNF * C4);
   const int Tn = a.T;
   const int H = a.q_heads;
   const int G = H / a.kv_heads;
@@ -777,87 +791,155 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   const int b = bh / H;
   const int h = bh - b * H;
   const int g = h / G;
-  const bool writer = (h - g * G) == 0;
+  const bool writer = a.write_cache && (h - g * G) == 0;
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int q0 = qt * RPW;
-  const int row = q0 + (int)threadIdx.x / LPQ;
-  const int d0 = ((int)threadIdx.x % LPQ) * DL;  // this lane's slice of the head dim
+  const int row = q0 + lane / LPQ;
+  const int c0 = (lane % LPQ) * (DL / 4);  // this lane's first 16-byte chunk of the head dim
 
   const float *qb = (const float *)a.q + (size_t)bh * Tn * D;
   const int off = a.offsets ? a.offsets[b] : 0;  // absolute position of query row 0
   // with a block table, k/v are the paged pools and rows are looked up per key
-  const float *kb = (const float *)a.k + (a.table ? 0 : (size_t)(b * a.kv_heads + g) * a.kv_rows * D);
-  const float *vb = (const float *)a.v + (a.table ? 0 : (size_t)(b * a.kv_heads + g) * a.kv_rows * D);
-  float *ckb = (float *)a.cache_k + (size_t)(b * a.kv_heads + g) * a.max_T * D;
-  float *cvb = (float *)a.cache_v + (size_t)(b * a.kv_heads + g) * a.max_T * D;
-  if (a.write_cache && qt == 0 && h == 0 && threadIdx.x == 0) a.len[b] = Tn;
+  const float4_t *kb = (const float4_t *)a.k + (a.table ? 0 : (size_t)(b * a.kv_heads + g) * a.kv_rows * C4);
+  const float4_t *vb = (const float4_t *)a.v + (a.table ? 0 : (size_t)(b * a.kv_heads + g) * a.kv_rows * C4);
+  float4_t *ckb = (float4_t *)a.cache_k + (size_t)(b * a.kv_heads + g) * a.max_T * C4;
+  float4_t *cvb = (float4_t *)a.cache_v + (size_t)(b * a.kv_heads + g) * a.max_T * C4;
+  if (a.write_cache && qt == 0 && h == 0 && tid == 0) a.len[b] = Tn;
 
   float qr[DL], o[DL];
 #pragma unroll
   for (int i = 0; i < DL; ++i) {
-    qr[i] = row < Tn ? qb[(size_t)row * D + d0 + i] : 0.f;
+    qr[i] = row < Tn ? qb[(size_t)row * D + 4 * c0 + i] : 0.f;
     o[i] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
   const float c = a.scale_log2;
+  const int n_keys = off + Tn;
   const int kv_end = off + min(q0 + RPW, Tn);
   const int W = a.window, S = a.sink;
   const int pos = off + row;
-  for (int k0 = 0; k0 < kv_end; k0 += BNF) {
-    // workgroup-uniform: a tile older than every row's window and past the sink is never read
-    if (W > 0 && k0 >= S && k0 + BNF - 1 <= off + q0 - W) continue;
+  // the first tile at or after k that some row of the workgroup sees: tiles
+  // older than every row's window and past the sink are never read
+  const int lim = off + q0 - W;
+  auto live = [&](int k) {
+    return (W > 0 && k >= S && k + BNF - 1 <= lim) ? ((lim + 1) / BNF) * BNF : k;
+  };
+  // chunk ch = tid + 64 NWF n of a tile: key row ch / C4, 16-byte column ch % C4
+  float4_t kr[NV], vr[NV];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const int ch = tid + 64 * NWF * n;
+      const int key = min(k0 + ch / C4, n_keys - 1);  // in range; rows past the end are zeroed below
+      const size_t rk = a.table ? paged_row(a.table, b, a.max_blocks, a.block_log2, a.kv_heads, g, key)
+                                : (size_t)key;
+      kr[n] = kb[rk * C4 + ch % C4];
+      vr[n] = vb[rk * C4 + ch % C4];
+    }
+  };
+  int k0 = live(0);
+  if (k0 < kv_end) load(k0);
+  while (k0 < kv_end) {
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const int ch = tid + 64 * NWF * n;
+      const int key = k0 + ch / C4;
+      const bool in = key < n_keys;
+      const float4_t z = {0.f, 0.f, 0.f, 0.f};
+      Ks[ch / C4][ch % C4] = in ? kr[n] : z;
+      Vs[ch / C4][ch % C4] = in ? vr[n] : z;
+      // this workgroup's own prompt rows go to the cache: a bit copy of what was loaded
+      if (writer && in && key >= q0 && key < q0 + RPW) {
+        ckb[(size_t)key * C4 + ch % C4] = kr[n];
+        cvb[(size_t)key * C4 + ch % C4] = vr[n];
+      }
+    }
+    const int k1 = live(k0 + BNF);
+    if (k1 < kv_end) load(k1);  // in flight while this tile is folded in
     __syncthreads();
-    for (int i = threadIdx.x; i < BNF * D; i += 64) {
-      const int r = i / D, d = i - r * D;
-      const int key = k0 + r;
-      float kx = 0.f, vx = 0.f;
-      if (key < off + Tn) {
-        const size_t rk = a.table ? paged_row(a.table, b, a.max_blocks, a.block_log2, a.kv_heads, g, key)
-                                  : (size_t)key;
-        kx = kb[rk * D + d];
-        vx = vb[rk * D + d];
-        if (a.write_cache && writer && key >= q0 && key < q0 + RPW) {
-          // bit copy of this tile's own rows: reinterpret, never round
-          ((uint32_t *)ckb)[(size_t)key * D + d] = __float_as_uint(kx);
-          ((uint32_t *)cvb)[(size_t)key * D + d] = __float_as_uint(vx);
+    const int kw = k0 + wave * KPW;  // this wave's keys: [kw, kw + KPW)
+    if (kw <= off + q0 + RPW - 1) {  // wave-uniform: some row of the tile sees a key of the quarter
+      float s[KPW];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < KPW; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i4 = 0; i4 < DL / 4; ++i4) {
+          const float4_t kx = Ks[wave * KPW + j][c0 + i4];
+          acc = fmaf(qr[4 * i4], kx[0], acc);
+          acc = fmaf(qr[4 * i4 + 1], kx[1], acc);
+          acc = fmaf(qr[4 * i4 + 2], kx[2], acc);
+          acc = fmaf(qr[4 * i4 + 3], kx[3], acc);
+        }
+        acc = quad_sum(acc);
+        const int key = kw + j;
+        const bool vis = key <= pos && (W == 0 || pos - key < W || key < S);
+        s[j] = vis ? acc * c : -INFINITY;
+        mx = fmaxf(mx, s[j]);
+      }
+      const float mn = fmaxf(m, mx);
+      const float ms = mn == -INFINITY ? 0.f : mn;  // no visible key yet: p = 0, not NaN
+      const float al = fast_exp2(m - ms);
+      l *= al;
+#pragma unroll
+      for (int i = 0; i < DL; ++i) o[i] *= al;
+#pragma unroll
+      for (int j = 0; j < KPW; ++j) {
+        const float p = fast_exp2(s[j] - ms);
+        l += p;
+#pragma unroll
+        for (int i4 = 0; i4 < DL / 4; ++i4) {
+          const float4_t vx = Vs[wave * KPW + j][c0 + i4];
+          o[4 * i4] = fmaf(p, vx[0], o[4 * i4]);
+          o[4 * i4 + 1] = fmaf(p, vx[1], o[4 * i4 + 1]);
+          o[4 * i4 + 2] = fmaf(p, vx[2], o[4 * i4 + 2]);
+          o[4 * i4 + 3] = fmaf(p, vx[3], o[4 * i4 + 3]);
         }
       }
-      Ks[r][d] = kx;
-      Vs[r][d] = vx;
+      m = mn;
     }
-    __syncthreads();
-    float s[BNF];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < BNF; ++j) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < DL; ++i) acc = fmaf(qr[i], Ks[j][d0 + i], acc);
-      acc = quad_sum(acc);
-      const int key = k0 + j;
-      const bool vis = key <= pos && (W == 0 || pos - key < W || key < S);
-      s[j] = vis ? acc * c : -INFINITY;
-      mx = fmaxf(mx, s[j]);
-    }
-    const float mn = fmaxf(m, mx);
-    const float ms = mn == -INFINITY ? 0.f : mn;  // no visible key yet (window): p = 0, not NaN
-    const float al = fast_exp2(m - ms);
-    l *= al;
-#pragma unroll
-    for (int i = 0; i < DL; ++i) o[i] *= al;
-#pragma unroll
-    for (int j = 0; j < BNF; ++j) {
-      const float p = fast_exp2(s[j] - ms);
-      l += p;
-#pragma unroll
-      for (int i = 0; i < DL; ++i) o[i] = fmaf(p, Vs[j][d0 + i], o[i]);
-    }
-    m = mn;
+    k0 = k1;
   }
-  if (row < Tn) {
-    const float inv = 1.0f / l;
-    float *ob = (float *)a.o + ((size_t)bh * Tn + row) * D + d0;
+  // merge the waves' states: m = max_w m_w, l = sum_w l_w 2^(m_w - m), o likewise
+  __syncthreads();  // the last tile's LDS reads are done
+  float *mf = (float *)lds4;  // [NWF][64] m, then [NWF][64] l, then [NWF][DL][64] o
+  float *lf = mf + NWF * 64;
+  float *of = lf + NWF * 64;
+  if (wave > 0) {
+    mf[wave * 64 + lane] = m;
+    lf[wave * 64 + lane] = l;
 #pragma unroll
-    for (int i = 0; i < DL; ++i) ob[i] = o[i] * inv;
+    for (int i = 0; i < DL; ++i) of[(wave * DL + i) * 64 + lane] = o[i];
+  }
+  __syncthreads();
+  if (wave == 0 && row < Tn) {
+    float mw[NWF];
+    mw[0] = m;
+    float mt = m;
+#pragma unroll
+    for (int w = 1; w < NWF; ++w) {
+      mw[w] = mf[w * 64 + lane];
+      mt = fmaxf(mt, mw[w]);
+    }
+    // every row sees at least its own key, so mt is finite
+    float sc[NWF];
+#pragma unroll
+    for (int w = 0; w < NWF; ++w) sc[w] = fast_exp2(mw[w] - mt);
+    float lt = l * sc[0];
+#pragma unroll
+    for (int w = 1; w < NWF; ++w) lt = fmaf(lf[w * 64 + lane], sc[w], lt);
+    const float inv = 1.0f / lt;
+    float *ob = (float *)a.o + ((size_t)bh * Tn + row) * D + 4 * c0;
+#pragma unroll
+    for (int i = 0; i < DL; ++i) {
+      float acc = o[i] * sc[0];
+#pragma unroll
+      for (int w = 1; w < NWF; ++w) acc = fmaf(of[(w * DL + i) * 64 + lane], sc[w], acc);
+      ob[i] = acc * inv;
+    }
   }
 }
 
@@ -921,7 +1003,7 @@ static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
 template <int D>
 static hipError_t launch_f32(const PrefillArgs &a, hipStream_t s) {
   const int n_qt = (a.T + 15) / 16;  // 16 query rows per workgroup
-  prefill_f32_kernel<D><<<dim3((unsigned)n_qt * a.batch * a.q_heads), 64, 0, s>>>(a);
+  prefill_f32_kernel<D><<<dim3((unsigned)n_qt * a.batch * a.q_heads), 64 * kF32Waves, 0, s>>>(a);
   return hipGetLastError();
 }
 
