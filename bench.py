@@ -242,7 +242,8 @@ def small_head_prefill(kv, dev, mceil, eceil, reps=20):
 
 def small_config_measurements(kv, dev):
     """The three small workloads, whole: prompt prefill of every layer, then every decode step
-    (append + decode per layer), timed with HIP events per launch.  Their caches (0.3-69 MB) stay in
+    (append + decode per layer), timed with HIP events around the prefills and around the steps
+    (median of five runs).  Their caches (0.3-69 MB) stay in
     the 256 MB last-level cache and their launches take a few microseconds, so they are reported in
     microseconds per step (launch-bound), not as bandwidth."""
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -255,44 +256,43 @@ def small_config_measurements(kv, dev):
         gen.manual_seed(100 + cfg)
         rnd = lambda shape: torch.randn(shape, generator=gen, device=dev).to(dt)
         c = kv.KVCache(L, B, H, Hkv, D, w.max_T, dt, device=dev)
-        pre = [c.bind_prefill(l, rnd((B, H, T, D)), rnd((B, Hkv, T, D)), rnd((B, Hkv, T, D)),
-                              torch.empty((B, H, T, D), dtype=dt, device=dev), scale=w.scale) for l in range(L)]
+        # the bound calls hold raw pointers: keep the tensors alive alongside them
+        ins = [(rnd((B, H, T, D)), rnd((B, Hkv, T, D)), rnd((B, Hkv, T, D)),
+                torch.empty((B, H, T, D), dtype=dt, device=dev)) for _ in range(L)]
+        pre = [c.bind_prefill(l, *ins[l], scale=w.scale) for l in range(L)]
         kn, vn, qd = rnd((B, Hkv, 1, D)), rnd((B, Hkv, 1, D)), rnd((B, H, 1, D))
         od = torch.empty((B, H, 1, D), dtype=dt, device=dev)
         app = [c.bind_append(l, kn, vn) for l in range(L)]
         dec = [c.bind_decode(l, qd, od, scale=w.scale) for l in range(L)]
 
-        def run(record):
+        def run():
+            # one event pair around all layers' prefills and one around all steps: an event
+            # pair per launch adds its own gap to launches this short
             c.set_lengths([0] * B)
-            t_pre, t_step = [], []
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
             for l in range(L):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
                 pre[l]()
-                b.record()
-                t_pre.append((a, b))
+            e[1].record()
             for _ in range(w.steps):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
                 for l in range(L):
                     app[l]()
                     dec[l]()
-                b.record()
-                t_step.append((a, b))
+            e[2].record()
             torch.cuda.synchronize()
-            if record:
-                return ([x.elapsed_time(y) for x, y in t_pre], [x.elapsed_time(y) for x, y in t_step])
-        run(False)
-        tp, ts = run(True)
+            return e[0].elapsed_time(e[1]) / L, e[1].elapsed_time(e[2]) / w.steps
+        run()
+        reps = [run() for _ in range(5)]
         c.close()
-        pre_ms, step_ms = statistics.median(tp), statistics.median(ts)
+        pre_ms = statistics.median(r[0] for r in reps)
+        step_ms = statistics.median(r[1] for r in reps)
         flops = 4.0 * B * H * D * T * (T + 1) / 2
         out[w.name] = {"prefill_us_per_layer": round(pre_ms * 1e3, 1),
                        "prefill_tflops": round(flops / (pre_ms * 1e-3) / 1e12, 2),
                        "decode_step_us": round(step_ms * 1e3, 1),
                        "decode_us_per_layer": round(step_ms * 1e3 / L, 2),
                        "decode_tok_s": round(B / (step_ms * 1e-3), 1),
-                       "whole_run_ms": round(sum(tp) + sum(ts), 3),
+                       "whole_run_ms": round(pre_ms * L + step_ms * w.steps, 3),
                        "note": f"{L} layer(s), B={B}, {H}/{Hkv} heads, D={D}, {w.dtype}: prompt {T} then "
                                f"{w.steps} steps; launch-bound, cache-resident"}
     return out

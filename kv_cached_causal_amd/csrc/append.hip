@@ -11,9 +11,15 @@ namespace kvattn {
 
 // One workgroup per sequence b: copies the Hkv rows of k_new/v_new to row
 // len[b] of the cache, then (after every thread has read len[b]) bumps it.
+// The entry points check capacity against their host copy of the lengths at
+// enqueue time; a replayed graph of appends advances only the device lengths,
+// so the kernel also keeps every write inside the cache: a sequence at
+// max_T positions (paged: at the end of its block-table row) is left as it
+// is, its length unchanged.
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int b = blockIdx.x;
   const int pos = a.len[b];
+  if (a.table ? (pos >> a.block_log2) >= a.max_blocks : pos >= a.max_T) return;  // workgroup-uniform
   const int vec_per_row = a.row_bytes >> 4;
   const int n_vec = a.kv_heads * vec_per_row;
   for (int i = threadIdx.x; i < n_vec; i += blockDim.x) {

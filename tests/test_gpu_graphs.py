@@ -1,0 +1,164 @@
+"""Decode steps captured in a HIP graph (torch.cuda.CUDAGraph over the C ABI).
+
+A decode step (append, then decode, for every layer) takes the lengths from
+device memory, so one captured step replayed n times is n steps of
+generation (inference chapter, section 9.3: each step appends one K/V row
+and attends over the cache).  Checked here:
+
+* every replay's output equals, bit for bit, the eager call sequence's output
+  at the same step, with the program's own eager work and synchronisations
+  between replays;
+* replays past the cache's capacity, which the host-side capacity check
+  cannot see (it runs once, at capture), leave the cache and the bytes around
+  it as they were: the append kernel drops a position past max_T and leaves
+  the length at max_T, and a decode then attends over all max_T rows.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+from gpu_util import TORCH_DT, check_output, host_bits, say, to_dev
+from oracle import attention as oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _kv():
+    import kv_cached_causal_amd as kv
+    return kv
+
+
+def _rand(shape, dtype, seed):
+    return si.round_to(np.random.default_rng(seed).standard_normal(shape), dtype)
+
+
+@pytest.mark.parametrize("heads", [(8, 8), (8, 2)], ids=lambda x: f"H{x[0]}kv{x[1]}")
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_graph_replayed_steps_equal_eager(dtype, heads):
+    kv = _kv()
+    H, Hkv = heads
+    L, B, D, T, steps = 2, 3, 64, 700, 6
+    max_T = T + steps
+    scale = float(np.float32(1 / np.sqrt(D)))
+    say(f"graph replay dtype={dtype} H={H} Hkv={Hkv} L={L} B={B} T={T} steps={steps}")
+    dev = lambda a: to_dev(a, dtype)
+    qs = [dev(_rand((B, H, T, D), dtype, 40 + 3 * l)) for l in range(L)]
+    ks = [dev(_rand((B, Hkv, T, D), dtype, 41 + 3 * l)) for l in range(L)]
+    vs = [dev(_rand((B, Hkv, T, D), dtype, 42 + 3 * l)) for l in range(L)]
+    kn, vn = dev(_rand((B, Hkv, 1, D), dtype, 50)), dev(_rand((B, Hkv, 1, D), dtype, 51))
+    qd = dev(_rand((B, H, 1, D), dtype, 52))
+    od = torch.empty((B, H, 1, D), dtype=torch.float32, device="cuda")
+    c = kv.KVCache(L, B, H, Hkv, D, max_T, TORCH_DT[dtype])
+
+    def prompt():
+        c.set_lengths([0] * B)
+        for l in range(L):
+            c.prefill(l, qs[l], ks[l], vs[l], scale=scale)
+        torch.cuda.synchronize()
+
+    def step(app, dec):
+        for l in range(L):
+            app[l]()
+            dec[l]()
+
+    prompt()
+    app = [c.bind_append(l, kn, vn) for l in range(L)]
+    dec = [c.bind_decode(l, qd, od, scale=scale) for l in range(L)]
+    eager = []
+    for _ in range(steps):
+        step(app, dec)
+        torch.cuda.synchronize()
+        eager.append(host_bits(od))
+    # the first step's output is checked against the oracle too
+    prompt()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gapp = [c.bind_append(l, kn, vn) for l in range(L)]
+        gdec = [c.bind_decode(l, qd, od, scale=scale) for l in range(L)]
+        step(gapp, gdec)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        g.replay()
+        scratch = torch.randn(1 << 16, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        assert np.array_equal(host_bits(od), eager[i]), f"replay {i} differs from the eager step"
+    # last layer after the first step, against the oracle
+    l = L - 1
+    ck = np.concatenate([si.to_f64(host_bits_to_np(ks[l], dtype), dtype), si.to_f64(host_bits_to_np(kn, dtype), dtype)], axis=2)
+    cv = np.concatenate([si.to_f64(host_bits_to_np(vs[l], dtype), dtype), si.to_f64(host_bits_to_np(vn, dtype), dtype)], axis=2)
+    ref = oracle.decode_cached(si.to_f64(host_bits_to_np(qd, dtype)[:, :, 0], dtype), ck, cv, [T + 1] * B, scale)
+    first = torch.from_numpy(eager[0].view(np.float32))
+    check_output(first[:, :, 0], ref, dtype, "first step, last layer")
+    del g
+    c.close()
+
+
+def host_bits_to_np(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """A device tensor back as the storage array synth_inputs uses for `dtype`."""
+    b = host_bits(t)
+    return b.view(np.float32) if dtype == "f32" else (b.view(np.float16) if dtype == "f16" else b)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_graph_replays_past_capacity_stay_inside_the_cache(dtype):
+    kv = _kv()
+    L, B, H, Hkv, D, T, room = 2, 2, 4, 2, 64, 50, 3
+    max_T = T + room
+    scale = float(np.float32(1 / np.sqrt(D)))
+    guard = 1 << 16
+    tdt = TORCH_DT[dtype]
+    nbytes = kv.cache_bytes(L, B, Hkv, D, max_T, tdt)
+    big = torch.full((nbytes + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    c = kv.KVCache.__new__(kv.KVCache)
+    c.device = big.device
+    c.layers, c.batch, c.q_heads, c.kv_heads = L, B, H, Hkv
+    c.head_dim, c.max_T, c.dtype, c.nbytes = D, max_T, tdt, nbytes
+    c._handle = ctypes.c_void_p()
+    c._buf = big[guard:guard + nbytes]
+    torch.cuda.synchronize()
+    rc = kv.lib().kvattn_cache_alloc(ctypes.byref(c._handle), L, B, H, Hkv, D, max_T, kv._DT[tdt],
+                                     ctypes.c_void_p(c._buf.data_ptr()), nbytes)
+    assert rc == 0
+    q = [_rand((B, H, T, D), dtype, 60 + 3 * l) for l in range(L)]
+    k = [_rand((B, Hkv, T, D), dtype, 61 + 3 * l) for l in range(L)]
+    v = [_rand((B, Hkv, T, D), dtype, 62 + 3 * l) for l in range(L)]
+    kn, vn, qd = _rand((B, Hkv, 1, D), dtype, 70), _rand((B, Hkv, 1, D), dtype, 71), _rand((B, H, 1, D), dtype, 72)
+    kn_d, vn_d, qd_d = to_dev(kn, dtype), to_dev(vn, dtype), to_dev(qd, dtype)
+    od = torch.empty((B, H, 1, D), dtype=torch.float32, device="cuda")
+    for l in range(L):
+        c.prefill(l, to_dev(q[l], dtype), to_dev(k[l], dtype), to_dev(v[l], dtype), scale=scale)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gapp = [c.bind_append(l, kn_d, vn_d) for l in range(L)]
+        gdec = [c.bind_decode(l, qd_d, od, scale=scale) for l in range(L)]
+        for l in range(L):
+            gapp[l]()
+            gdec[l]()
+    torch.cuda.synchronize()
+    n = room + 4
+    say(f"graph: {n} replays of an append + decode step into {room} free positions ({dtype})")
+    for _ in range(n):
+        g.replay()
+    torch.cuda.synchronize()
+    gb = big.cpu().numpy()
+    assert (gb[:guard] == 0x5A).all() and (gb[guard + nbytes:] == 0x5A).all(), "bytes outside the cache written"
+    # every layer: the prompt rows, then `room` copies of the appended row, nothing else
+    for l in range(L):
+        kk = host_bits_to_np(c.k_view(l), dtype)
+        vv = host_bits_to_np(c.v_view(l), dtype)
+        assert np.array_equal(kk[:, :, :T], k[l]) and np.array_equal(vv[:, :, :T], v[l]), f"layer {l}: prompt rows changed"
+        for t in range(T, max_T):
+            assert np.array_equal(kk[:, :, t], kn[:, :, 0]) and np.array_equal(vv[:, :, t], vn[:, :, 0])
+    # the last replay's decode saw all max_T rows
+    l = L - 1
+    ck = si.to_f64(np.concatenate([k[l]] + [kn] * room, axis=2), dtype)
+    cv = si.to_f64(np.concatenate([v[l]] + [vn] * room, axis=2), dtype)
+    ref = oracle.decode_cached(si.to_f64(qd[:, :, 0], dtype), ck, cv, [max_T] * B, scale)
+    check_output(od[:, :, 0], ref, dtype, "decode at capacity")
+    del g
+    c.close()
