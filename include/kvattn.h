@@ -131,7 +131,11 @@ int kvattn_prefill(kvattn_cache *c, int layer, const void *q, const void *k, con
 /* Append one position per sequence (inference chapter 9.3: decode appends one
  * position to the cache): k_new/v_new (B,Hkv,1,D) are copied bit-exactly to
  * row len[b] of sequence b, then len[b] += 1.  CAPACITY if any len[b] ==
- * max_T. */
+ * max_T.  That check runs on the host, at enqueue time, against the
+ * library's host copy of the lengths; the kernel reads len[b] from device
+ * memory, so a call captured in a HIP graph appends at the current length on
+ * every replay, and a replay at len[b] == max_T leaves that sequence's cache
+ * and length unchanged (no error is reported from the device). */
 int kvattn_append(kvattn_cache *c, int layer, const void *k_new, const void *v_new, void *stream);
 
 /* Extend one layer by T positions per sequence after its cached prefix: the
@@ -228,7 +232,9 @@ int kvattn_paged_prefill(kvattn_paged *p, int layer, const void *q, const void *
 
 /* Append one position per slot (k_new/v_new (slots,Hkv,1,D)) at its length,
  * in the block that holds that position; len += 1.  CAPACITY if a slot's
- * blocks are full. */
+ * blocks are full (checked on the host at enqueue time; on the device a
+ * position past the slot's block-table row is dropped, as in kvattn_append,
+ * but one past its assigned blocks is not detected there). */
 int kvattn_paged_append(kvattn_paged *p, int layer, const void *k_new, const void *v_new, void *stream);
 
 /* Extend over the paged cache: as kvattn_extend (chunked prefill, multi-token
