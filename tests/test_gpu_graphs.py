@@ -162,3 +162,42 @@ def test_graph_replays_past_capacity_stay_inside_the_cache(dtype):
     check_output(od[:, :, 0], ref, dtype, "decode at capacity")
     del g
     c.close()
+
+
+def test_graph_paged_appends_stop_at_the_block_table_row():
+    """Paged cache: replayed appends fill a slot up to the end of its block-table
+    row (max_blocks blocks) and then leave the pool as it is; blocks of other
+    slots and the unassigned block keep their contents."""
+    kv = _kv()
+    slots, max_blocks, num_blocks, bs, H, Hkv, D, dtype = 2, 2, 5, 16, 4, 2, 64, "f16"
+    c = kv.PagedKVCache(1, slots, max_blocks, num_blocks, bs, H, Hkv, D, TORCH_DT[dtype])
+    pk, pv = c.k_view(0), c.v_view(0)  # (num_blocks, Hkv, bs, D)
+    pk.fill_(7.0)
+    pv.fill_(-7.0)
+    tables = [[3, 0], [1, 4]]  # block 2 belongs to no slot
+    for s in range(slots):
+        c.set_blocks(s, tables[s])
+    start = [29, 31]  # capacity max_blocks * bs = 32 positions per slot
+    c.set_lengths(start)
+    kn, vn = _rand((slots, Hkv, 1, D), dtype, 80), _rand((slots, Hkv, 1, D), dtype, 81)
+    kn_d, vn_d = to_dev(kn, dtype), to_dev(vn, dtype)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        c.append(0, kn_d, vn_d)
+    torch.cuda.synchronize()
+    say("paged graph: 5 replays of an append into 3 and 1 free positions")
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    ek = np.full(tuple(pk.shape), 7.0, dtype=np.float16)
+    ev = np.full(tuple(pv.shape), -7.0, dtype=np.float16)
+    for s in range(slots):
+        for p in range(start[s], max_blocks * bs):
+            blk = tables[s][p // bs]
+            ek[blk, :, p % bs] = kn[s, :, 0]
+            ev[blk, :, p % bs] = vn[s, :, 0]
+    assert np.array_equal(host_bits(pk), ek.view(np.uint16)), "K pool differs from the expected appends"
+    assert np.array_equal(host_bits(pv), ev.view(np.uint16)), "V pool differs from the expected appends"
+    del g
+    c.close()
