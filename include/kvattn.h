@@ -164,6 +164,36 @@ int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, cons
 int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scale,
                   kvattn_dtype o_dtype, void *stream);
 
+/* Bytes of the fixed device array that holds kvattn_decode_noalloc's split-K
+ * partials (one copy per device, kept until the process ends). */
+#define KVATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* Decode that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It computes what kvattn_decode computes, with the same
+ * kernels, over a caller-owned contiguous cache: k_cache and v_cache are
+ * device arrays (batch, kv_heads, max_T, head_dim) in `dt`, lengths a device
+ * int32 array [batch] (query q[b,h] (B,H,1,D) sits at position lengths[b]-1
+ * and attends cache rows 0 .. lengths[b]-1), o (B,H,1,D) in o_dtype (dt or
+ * F32).  No window, no block table.  The split-K partials go to a fixed
+ * device array of KVATTN_NOALLOC_SCRATCH_BYTES inside the library instead of
+ * a cache object's workspace; a shape needs
+ * 4 * batch * q_heads * ceil(max_T / split) * (head_dim + 2) bytes of it
+ * (split = the decode split size, 384-1024 keys by head dim and group size,
+ * doubled while max_T / split > 64), and CAPACITY is returned, with the
+ * sizes in kvattn_last_error, when that exceeds the array.  The array is
+ * shared by every call on a device and keeps the last call's contents:
+ * calls that overlap on one device (concurrent streams) race on it.  Every
+ * partial is written before it is read within a call, so nothing needs
+ * clearing between calls.  Lengths are read on the device only: each must be
+ * in [1, max_T]; a larger one is read as max_T and a sequence with a length
+ * <= 0 gets no output written.  The first call on a device looks up the
+ * array's device address (no allocation).  INVALID_ARG / UNSUPPORTED as for
+ * kvattn_decode; nothing is enqueued on error. */
+int kvattn_decode_noalloc(const void *k_cache, const void *v_cache, const int32_t *lengths, int batch,
+                          int q_heads, int kv_heads, int head_dim, int max_T, kvattn_dtype dt, const void *q,
+                          void *o, float scale, kvattn_dtype o_dtype, void *stream);
+
 /* ---------------------------------------------------------------- paged cache
  * The cache managed in fixed-size blocks instead of one max-length region per
  * sequence (inference chapter, section 9.6, Continuous Batching and Paged KV;

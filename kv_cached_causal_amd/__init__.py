@@ -17,7 +17,8 @@ import os
 
 import torch
 
-__all__ = ["KVCache", "PagedKVCache", "Decoder", "KVAttnError", "cache_bytes", "paged_bytes", "lib", "LIB_PATH"]
+__all__ = ["KVCache", "PagedKVCache", "Decoder", "KVAttnError", "cache_bytes", "paged_bytes", "decode_noalloc",
+           "NOALLOC_SCRATCH_BYTES", "lib", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # KVATTN_LIB names another build of the library (for example a tuning variant)
@@ -52,6 +53,8 @@ _SIGS = {
                       + [ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "kvattn_decode_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 6
+                              + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_paged_bytes": (ctypes.c_size_t, [ctypes.c_int] * 6),
     "kvattn_paged_alloc": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p)] + [ctypes.c_int] * 9
                            + [ctypes.c_void_p, ctypes.c_size_t]),
@@ -352,6 +355,40 @@ class KVCache:
 
     def __exit__(self, *exc):
         self.close()
+
+
+# bytes of the library's fixed split-K array used by decode_noalloc (KVATTN_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_noalloc(k_cache: torch.Tensor, v_cache: torch.Tensor, lengths: torch.Tensor, q: torch.Tensor,
+                   out: torch.Tensor, scale: float | None = None) -> torch.Tensor:
+    """kvattn_decode_noalloc: decode over a caller-owned cache, allocating nothing.
+
+    k_cache, v_cache (B, Hkv, max_T, D) and q (B, H, 1, D) in one dtype; lengths a
+    device int32 tensor [B]; out (B, H, 1, D) in that dtype or float32.  The
+    split-K partials go to the library's fixed device array."""
+    tensors = {"k_cache": k_cache, "v_cache": v_cache, "lengths": lengths, "q": q, "out": out}
+    for name, t in tensors.items():
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must be (B, Hkv, max_T, D) of one dtype")
+    B, Hkv, max_T, D = k_cache.shape
+    if q.dim() != 4 or q.shape[0] != B or q.shape[2] != 1 or q.shape[3] != D or q.dtype != k_cache.dtype:
+        raise ValueError("q must be (B, H, 1, D) in the cache dtype")
+    if out.shape != q.shape or out.dtype not in (q.dtype, torch.float32):
+        raise ValueError("out must have q's shape, in q's dtype or float32")
+    if lengths.dtype != torch.int32 or tuple(lengths.shape) != (B,):
+        raise ValueError("lengths must be an int32 tensor of shape (B,)")
+    scale = float(1.0 / math.sqrt(D)) if scale is None else float(scale)
+    st = lib().kvattn_decode_noalloc(_ptr(k_cache), _ptr(v_cache), _ptr(lengths), B, q.shape[1], Hkv, D, max_T,
+                                     _DT[k_cache.dtype], _ptr(q), _ptr(out), scale, _DT[out.dtype],
+                                     _stream_ptr(q.device))
+    _check(st, "kvattn_decode_noalloc")
+    return out
 
 
 def paged_bytes(layers: int, num_blocks: int, block_size: int, kv_heads: int, head_dim: int, dtype) -> int:

@@ -131,8 +131,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int unit = blockIdx.y;  // (kv head, sub-group of GT query rows)
   const int kvh = unit / subs;
   const int h0 = kvh * RK + (unit - kvh * subs) * GT;  // first query row
-  // splits run over the visible keys (all L, or the sink and window ones)
-  const VisibleKeys vk = visible_keys(a.len[b], a.window, a.sink);
+  // splits run over the visible keys (all L, or the sink and window ones);
+  // a length past the capacity is read as the capacity, so no row outside
+  // the sequence's region is ever touched (a length <= 0 leaves every split
+  // empty and the sequence's output unwritten)
+  const VisibleKeys vk = visible_keys(min(a.len[b], a.max_T), a.window, a.sink);
   const int kb = split * a.chunk;  // first visible index of this split
   if (kb >= vk.count) return;  // empty split
   const int rows = min(a.chunk, vk.count - kb);
@@ -413,7 +416,7 @@ __global__ __launch_bounds__((merge_threads<D, GT>())) void decode_merge_kernel(
   const int unit = blockIdx.x;
   const int kvh = unit / subs;
   const int h0 = kvh * RK + (unit - kvh * subs) * GT;
-  const int ns = (visible_keys(a.len[b], a.window, a.sink).count + a.chunk - 1) / a.chunk;
+  const int ns = (visible_keys(min(a.len[b], a.max_T), a.window, a.sink).count + a.chunk - 1) / a.chunk;
   if (ns <= 1) return;
   const float *ws_unit = a.ws + (size_t)(b * RS + h0) * a.n_splits * (D + 2);
 

@@ -10,6 +10,7 @@
 
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -63,6 +64,42 @@ int check_device(const kvattn_cache *c) {
 char *layer_k(const kvattn_cache *c, int layer) { return c->base + (size_t)layer * c->layer_bytes; }
 char *layer_v(const kvattn_cache *c, int layer) {
   return layer_k(c, layer) + c->layer_bytes / 2;
+}
+
+}  // namespace
+
+// Split-K workspace of kvattn_decode_noalloc: a fixed device array, so that
+// call allocates nothing.  Each device that loads the library holds its own
+// copy until the process ends.  In host code `scratch` is only a stand-in
+// for the device array: its device address comes from hipGetSymbolAddress,
+// looked up once per device (with that device current) and kept below.
+static __device__ __align__(256) float scratch[KVATTN_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<float *> g_scratch_ptr;  // per device ordinal; null until looked up
+
+// device address of `scratch` on the current device, or null on error
+float *scratch_on_current_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    hip_fail(e, "hipGetDevice");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = (float *)p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -424,6 +461,54 @@ int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scal
   a.max_blocks = 0;
   hipError_t e = launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return KVATTN_OK;
+}
+
+int kvattn_decode_noalloc(const void *k_cache, const void *v_cache, const int32_t *lengths, int batch,
+                          int q_heads, int kv_heads, int head_dim, int max_T, kvattn_dtype dt, const void *q,
+                          void *o, float scale, kvattn_dtype o_dtype, void *stream) {
+  if (!k_cache || !v_cache || !lengths || !q || !o) return KVATTN_ERR_INVALID_ARG;
+  if (batch <= 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 || max_T <= 0) return KVATTN_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
+  if (elem_bytes(dt) == 0 || !supported_dim(head_dim) || q_heads % kv_heads != 0) return KVATTN_ERR_UNSUPPORTED;
+  if (o_dtype != dt && o_dtype != KVATTN_F32) return KVATTN_ERR_UNSUPPORTED;
+  // split-K partials (m, l, u[D]) of every (sequence, query head, split);
+  // the split count depends on the capacity only, not on the lengths
+  const int chunk = decode_chunk(head_dim, q_heads / kv_heads, max_T);
+  const int n_splits = (max_T + chunk - 1) / chunk;
+  const size_t need = sizeof(float) * (size_t)batch * q_heads * n_splits * (head_dim + 2);
+  if (need > (size_t)KVATTN_NOALLOC_SCRATCH_BYTES) {
+    std::snprintf(g_last_error, sizeof g_last_error,
+                  "kvattn_decode_noalloc: this shape needs %zu bytes of split-K scratch, the fixed array holds %zu",
+                  need, (size_t)KVATTN_NOALLOC_SCRATCH_BYTES);
+    return KVATTN_ERR_CAPACITY;
+  }
+  float *ws = scratch_on_current_device();
+  if (!ws) return KVATTN_ERR_HIP;
+  DecodeArgs a;
+  a.k_layer = k_cache;
+  a.v_layer = v_cache;
+  a.q = q;
+  a.o = o;
+  a.ws = ws;
+  a.len = lengths;
+  a.batch = batch;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.head_dim = head_dim;
+  a.max_T = max_T;
+  a.chunk = chunk;
+  a.n_splits = n_splits;
+  a.window = 0;
+  a.sink = 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dt = dt;
+  a.o_dt = o_dtype;
+  a.table = nullptr;
+  a.block_log2 = 0;
+  a.max_blocks = 0;
+  hipError_t e = launch_decode(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode (no-alloc) launch");
   return KVATTN_OK;
 }
 

@@ -247,3 +247,22 @@ def test_model_calls_reject_null_model_without_a_device():
     assert lib.kvattn_model_step(None, p, p, p, None) == -1
     assert lib.kvattn_model_generate(None, 4, p, p, None) == -1
     assert lib.kvattn_model_positions(None, (ctypes.c_int32 * 1)()) == -1
+
+
+def test_noalloc_decode_validates_on_the_host():
+    """kvattn_decode_noalloc checks its arguments, and the size of the split-K
+    partials against its fixed array, before any device call (so this runs
+    without a GPU): a shape that needs more than the array is CAPACITY, with
+    the sizes in the error text."""
+    lib = kv.lib()
+    p = 0x1000  # never dereferenced: every case is rejected on the host
+    # B = 1024, H = 32, D = 128, 4096 keys in 4 splits of 1024: 4*1024*32*4*130 B = 68 MB > 16 MiB
+    assert lib.kvattn_decode_noalloc(p, p, p, 1024, 32, 8, 128, 4096, 1, p, p, 0.125, 1, None) == -3
+    assert b"scratch" in lib.kvattn_last_error()
+    assert kv.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert lib.kvattn_decode_noalloc(None, p, p, 2, 4, 4, 64, 64, 1, p, p, 0.125, 1, None) == -1
+    assert lib.kvattn_decode_noalloc(p, p, p, 2, 4, 3, 64, 64, 1, p, p, 0.125, 1, None) == -2
+    assert lib.kvattn_decode_noalloc(p, p, p, 2, 4, 4, 48, 64, 1, p, p, 0.125, 1, None) == -2
+    assert lib.kvattn_decode_noalloc(p, p, p, 2, 4, 4, 64, 64, 1, p, p, 0.125, 2, None) == -2
+    assert lib.kvattn_decode_noalloc(p, p, p, 2, 4, 4, 64, 64, 1, p, p, -1.0, 1, None) == -1
+    assert lib.kvattn_decode_noalloc(p, p, p, 0, 4, 4, 64, 64, 1, p, p, 0.125, 1, None) == -1
