@@ -164,6 +164,26 @@ int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, cons
 int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scale,
                   kvattn_dtype o_dtype, void *stream);
 
+/* One decode step of one layer in one launch: kvattn_append followed by
+ * kvattn_decode (inference chapter, section 9.3: decode appends the new
+ * token's K and V to the cache and attends the whole cache).  k_new/v_new
+ * (B,Hkv,1,D) are copied bit-exactly to row len[b] of sequence b; query
+ * q[b,h] (B,H,1,D) at position len[b] attends cache rows 0 .. len[b] (the new
+ * row included, within the layer's window and sink if set); o (B,H,1,D) in
+ * o_dtype (cache dtype or F32); then len[b] += 1.  The result equals that of
+ * the two calls.  The new row is taken from k_new/v_new for the attention and
+ * stored into the cache by the same kernel; the splits of each sequence are
+ * merged by log-sum-exp inside the launch, and the last of a sequence's
+ * workgroups advances its length, so the call needs no host synchronisation
+ * and may be captured in a HIP graph.  CAPACITY if any len[b] == max_T
+ * (checked on the host against its copy of the lengths); on a replayed graph
+ * a sequence found full on the device is left unchanged, cache, length and
+ * output rows alike.  Lengths may be 0 (the query then sees only its own
+ * row).  Calls on one cache must be ordered on one stream (the split
+ * counters and workspace are shared by its layers). */
+int kvattn_append_decode(kvattn_cache *c, int layer, const void *k_new, const void *v_new, const void *q, void *o,
+                         float scale, kvattn_dtype o_dtype, void *stream);
+
 /* Bytes of the fixed device array that holds kvattn_decode_noalloc's split-K
  * partials (one copy per device, kept until the process ends). */
 #define KVATTN_NOALLOC_SCRATCH_BYTES (16u << 20)

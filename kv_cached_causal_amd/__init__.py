@@ -53,6 +53,8 @@ _SIGS = {
                       + [ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "kvattn_append_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 4
+                             + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_decode_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 6
                               + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_paged_bytes": (ctypes.c_size_t, [ctypes.c_int] * 6),
@@ -300,6 +302,25 @@ class KVCache:
                    "kvattn_decode")
         return out
 
+    def append_decode(self, layer: int, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                      out: torch.Tensor | None = None, scale: float | None = None, out_dtype=None) -> torch.Tensor:
+        """One decode step in one launch: append k_new/v_new at len[b], attend the
+        len[b] + 1 keys with q, then len[b] += 1 (same result as append + decode)."""
+        kv_shape = (self.batch, self.kv_heads, 1, self.head_dim)
+        shape = (self.batch, self.q_heads, 1, self.head_dim)
+        self._tensor(k_new, kv_shape, "k_new")
+        self._tensor(v_new, kv_shape, "v_new")
+        self._tensor(q, shape, "q")
+        od = out_dtype or self.dtype
+        if out is None:
+            out = torch.empty(shape, dtype=od, device=self.device)
+        self._tensor(out, shape, "out", od)
+        with torch.cuda.device(self.device):
+            _check(lib().kvattn_append_decode(self._handle, layer, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
+                                              self._scale(scale), _DT[od], _stream_ptr(self.device)),
+                   "kvattn_append_decode")
+        return out
+
     # ------------------------------------------------------------------ pre-bound calls
     # For launch-bound loops (many short kernels): the arguments are checked
     # and marshalled once, on the stream current at bind time, and the returned
@@ -336,6 +357,20 @@ class KVCache:
         args = (self._handle, layer, _ptr(q), _ptr(out), ctypes.c_float(self._scale(scale)), _DT[out.dtype],
                 _stream_ptr(self.device))
         return lambda: _check(fn(*args), "kvattn_decode")
+
+    def bind_append_decode(self, layer: int, k_new, v_new, q, out, scale: float | None = None):
+        kv_shape = (self.batch, self.kv_heads, 1, self.head_dim)
+        shape = (self.batch, self.q_heads, 1, self.head_dim)
+        self._tensor(k_new, kv_shape, "k_new")
+        self._tensor(v_new, kv_shape, "v_new")
+        self._tensor(q, shape, "q")
+        self._tensor(out, shape, "out", out.dtype)
+        if out.dtype not in (self.dtype, torch.float32):
+            raise TypeError(f"out has dtype {out.dtype}")
+        fn = lib().kvattn_append_decode
+        args = (self._handle, layer, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), ctypes.c_float(self._scale(scale)),
+                _DT[out.dtype], _stream_ptr(self.device))
+        return lambda: _check(fn(*args), "kvattn_append_decode")
 
     # ------------------------------------------------------------------ lifetime
     def close(self) -> None:

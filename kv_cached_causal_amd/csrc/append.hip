@@ -14,12 +14,12 @@ namespace kvattn {
 // The entry points check capacity against their host copy of the lengths at
 // enqueue time; a replayed graph of appends advances only the device lengths,
 // so the kernel also keeps every write inside the cache: a sequence at
-// max_T positions (paged: at the end of its block-table row) is left as it
-// is, its length unchanged.
+// max_T positions (paged: at the end of the blocks assigned to it) is left
+// as it is, its length unchanged.
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int b = blockIdx.x;
   const int pos = a.len[b];
-  if (a.table ? (pos >> a.block_log2) >= a.max_blocks : pos >= a.max_T) return;  // workgroup-uniform
+  if (pos >= seq_capacity(a.slot_blocks, b, a.block_log2, a.max_T)) return;  // workgroup-uniform
   const int vec_per_row = a.row_bytes >> 4;
   const int n_vec = a.kv_heads * vec_per_row;
   for (int i = threadIdx.x; i < n_vec; i += blockDim.x) {
@@ -50,16 +50,21 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
 
 // Extend: T rows per (sequence, KV head) copied to cache rows [len[b], len[b] + T)
 // (bit copies; through the block table for a paged cache); grid (row chunks, Hkv, B).  The lengths are only read here and
-// advanced by add_lengths_kernel once the attention over them has run.
+// advanced by add_lengths_kernel once the attention over them has run.  A
+// sequence whose T new rows would pass its capacity (only on a replayed
+// graph: the entry point checks its host copy of the lengths) is left as it
+// is by all three kernels of the extend: copy, attention and length update.
 __global__ __launch_bounds__(256) void extend_copy_kernel(ExtendCopyArgs a) {
   const int b = blockIdx.z;
   const int h = blockIdx.y;
   const int vec_per_row = a.row_bytes >> 4;
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= a.T * vec_per_row) return;
+  const int len0 = a.len[b];
+  if (len0 + a.T > seq_capacity(a.slot_blocks, b, a.block_log2, a.max_T)) return;
   const int t = idx / vec_per_row;
   const int w = idx - t * vec_per_row;
-  const int pos = a.len[b] + t;
+  const int pos = len0 + t;
   const size_t src = ((size_t)(b * a.kv_heads + h) * a.T + t) * a.row_bytes + (size_t)w * 16;
   const size_t row = a.table ? paged_row(a.table, b, a.max_blocks, a.block_log2, a.kv_heads, h, pos)
                              : (size_t)(b * a.kv_heads + h) * a.max_T + pos;
@@ -80,6 +85,9 @@ hipError_t launch_extend_copy(const ExtendCopyArgs &a, hipStream_t s) {
 __global__ __launch_bounds__(256) void paged_write_kernel(PagedWriteArgs a) {
   const int b = blockIdx.z;
   const int h = blockIdx.y;
+  // a prompt longer than the sequence's blocks (blocks reassigned after a
+  // graph was captured) is not written
+  if (a.T > (a.slot_blocks[b] << a.block_log2)) return;
   if (blockIdx.x == 0 && h == 0 && threadIdx.x == 0) a.len[b] = a.T;
   const int vec_per_row = a.row_bytes >> 4;
   const int idx = blockIdx.x * 256 + threadIdx.x;
@@ -101,13 +109,16 @@ hipError_t launch_paged_write(const PagedWriteArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ void add_lengths_kernel(int32_t *len, int batch, int T) {
+__global__ void add_lengths_kernel(int32_t *len, int batch, int T, int max_T, const int32_t *slot_blocks,
+                                   int block_log2) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < batch) len[b] += T;
+  if (b < batch && len[b] + T <= seq_capacity(slot_blocks, b, block_log2, max_T)) len[b] += T;
 }
 
-hipError_t launch_add_lengths(int32_t *len, int batch, int T, hipStream_t s) {
-  add_lengths_kernel<<<dim3((batch + 255) / 256), dim3(256), 0, s>>>(len, batch, T);
+hipError_t launch_add_lengths(int32_t *len, int batch, int T, int max_T, const int32_t *slot_blocks,
+                              int block_log2, hipStream_t s) {
+  add_lengths_kernel<<<dim3((batch + 255) / 256), dim3(256), 0, s>>>(len, batch, T, max_T, slot_blocks,
+                                                                     block_log2);
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ struct kvattn_cache {
   std::vector<int32_t> h_len;  // host mirror
   std::vector<int> window, sink;  // per layer: sliding window (0: none), sink positions
   float *d_ws;            // decode split-K workspace (device)
+  int32_t *d_cnt;         // fused decode step: [B][kStepSlots] (counter, attended count)
   int chunk, n_splits;
   int device;
 };

@@ -33,6 +33,7 @@ struct AppendArgs {
   // max_blocks + (p >> block_log2)]; null for the contiguous cache
   const int32_t *table;
   int block_log2, max_blocks;
+  const int32_t *slot_blocks = nullptr;  // paged: blocks assigned to each sequence [B] (device)
 };
 
 struct DecodeArgs {
@@ -53,7 +54,23 @@ struct DecodeArgs {
   // (multi-token verification), whose token t sits at position len - T + t
   // and sees the keys up to it (no window)
   int tokens = 1;
+  // extends on the decode kernels: the lengths do not include the `tokens`
+  // new rows yet (they are advanced afterwards), so L = len[b] + tokens, and
+  // a sequence for which that passes its capacity is skipped
+  int len_pending = 0;
+  const int32_t *slot_blocks = nullptr;  // paged: blocks assigned to each sequence [B] (device)
+  // the fused decode step (append + decode, contiguous cache): the new rows
+  // (B, Hkv, 1, D), writable views of the layer's K/V blocks and lengths, and
+  // per sequence kStepSlots ints: a counter that is zero between calls, and
+  // the attended count recorded for the merge kernel
+  const void *k_new = nullptr, *v_new = nullptr;
+  void *k_cache_rw = nullptr, *v_cache_rw = nullptr;
+  int32_t *len_rw = nullptr;
+  int32_t *counters = nullptr;
 };
+
+// ints per sequence of the fused decode step's device record (counter, count)
+constexpr int kStepSlots = 2;
 
 // the longest extend served by the decode kernels (its workspace is sized
 // for this many query positions per head)
@@ -64,6 +81,15 @@ constexpr int kMaxVerifyTokens = 8;
 inline bool verify_on_decode(int G, int T, int window) {
   const int r = G * T;
   return T >= 2 && T <= kMaxVerifyTokens && window == 0 && (r == 2 || r == 3 || r == 4 || r == 8);
+}
+
+// Positions sequence b may hold: the capacity of the contiguous cache, or
+// for a paged cache the blocks assigned to the sequence.  The entry points
+// check every write against their host copy of the lengths; the kernels that
+// write at device-held positions (append, extend) check again against this,
+// because a replayed HIP graph advances only the device lengths.
+__device__ inline int seq_capacity(const int32_t *slot_blocks, int b, int block_log2, int max_T) {
+  return slot_blocks ? (slot_blocks[b] << block_log2) : max_T;
 }
 
 // Row index (in rows of D elements) of position `pos` of KV head g of
@@ -116,6 +142,7 @@ struct PrefillArgs {
   // table[b * max_blocks + (j >> block_log2)]; null for the layouts above
   const int32_t *table = nullptr;
   int block_log2 = 0, max_blocks = 0;
+  const int32_t *slot_blocks = nullptr;  // paged: blocks assigned to each sequence [B] (device)
 };
 
 struct ExtendCopyArgs {
@@ -127,6 +154,7 @@ struct ExtendCopyArgs {
   int batch, kv_heads, max_T, row_bytes, T;
   const int32_t *table = nullptr;  // paged: [B][max_blocks] block ids
   int block_log2 = 0, max_blocks = 0;
+  const int32_t *slot_blocks = nullptr;  // paged: blocks assigned to each sequence [B] (device)
 };
 
 // Prefill rows [0, T) of each (sequence, KV head) copied into a paged
@@ -139,6 +167,7 @@ struct PagedWriteArgs {
   int32_t *len;         // layer's lengths [B]
   const int32_t *table; // [B][max_blocks]
   int batch, kv_heads, T, row_bytes, block_log2, max_blocks;
+  const int32_t *slot_blocks;  // blocks assigned to each sequence [B] (device)
 };
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
@@ -146,10 +175,12 @@ hipError_t launch_paged_write(const PagedWriteArgs &a, hipStream_t s);
 hipError_t launch_set_lengths(int32_t *dst, int layers, int batch, const int32_t *host_lens,
                               hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_extend_attention(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_extend_copy(const ExtendCopyArgs &a, hipStream_t s);
-hipError_t launch_add_lengths(int32_t *len, int batch, int T, hipStream_t s);
+hipError_t launch_add_lengths(int32_t *len, int batch, int T, int max_T, const int32_t *slot_blocks,
+                              int block_log2, hipStream_t s);
 
 // decode splits per (sequence, KV head) are capped, which bounds the
 // workspace and the merge's rounds of loads

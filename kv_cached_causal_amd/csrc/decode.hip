@@ -102,6 +102,19 @@ __device__ __forceinline__ void store_out(void *o, size_t idx, float x, kvattn_d
     ((bf16_t *)o)[idx] = (bf16_t)x;
 }
 
+// Keys attended by sequence b's last query position (decode and the extends
+// run on the decode kernels), from its device length len_in: a length past
+// the capacity is read as the capacity, so no row outside the sequence's
+// region is ever touched (a length <= 0 leaves every split empty and the
+// sequence's output unwritten).  With len_pending the lengths do not include
+// the extend's `tokens` new rows yet; an extend that would pass the
+// sequence's capacity (only on a replayed graph) gives -1: skipped.
+__device__ inline int attended_keys(const DecodeArgs &a, int b, int len_in) {
+  const int cap = seq_capacity(a.slot_blocks, b, a.block_log2, a.max_T);
+  if (a.len_pending) return len_in + a.tokens <= cap ? len_in + a.tokens : -1;
+  return min(len_in, cap);
+}
+
 // grid (n_splits, Hkv * G/GT, B), 256 threads.  A workgroup owns one split of
 // `chunk` keys of one KV head, for GT query heads of its group.  LPR lanes
 // share one key row, each holding NV 16-byte slices of it (columns cl + v *
@@ -112,7 +125,16 @@ __device__ __forceinline__ void store_out(void *o, size_t idx, float x, kvattn_d
 // workgroup (grid (n_splits, Hkv, B)); token t sits at position L - T + t and
 // its scores past that position are masked, so each K/V byte is still read
 // once for all G * T rows.
-template <class Tag, int D, int GT, int U, int NV, int NW, bool PAGED, bool VER = false>
+//
+// FUSED (the decode step, kvattn_append_decode): the sequence's new K/V row,
+// at position len[b], is read from k_new/v_new instead of the cache and
+// folded in by the workgroup whose split holds it, which also stores it into
+// the cache.  This kernel only reads len[b]; the advanced length is written
+// after every workgroup of the sequence has read it: by the merge kernel
+// (from the attended count this kernel records) when the cache has several
+// splits, else by the last of the sequence's workgroups to count itself in
+// on an atomic counter.
+template <class Tag, int D, int GT, int U, int NV, int NW, bool PAGED, bool VER = false, bool FUSED = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   constexpr int EPL = Tag::EPL;
   constexpr int LPR = D / (EPL * NV);  // lanes that share one key row
@@ -131,17 +153,40 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int unit = blockIdx.y;  // (kv head, sub-group of GT query rows)
   const int kvh = unit / subs;
   const int h0 = kvh * RK + (unit - kvh * subs) * GT;  // first query row
-  // splits run over the visible keys (all L, or the sink and window ones);
-  // a length past the capacity is read as the capacity, so no row outside
-  // the sequence's region is ever touched (a length <= 0 leaves every split
-  // empty and the sequence's output unwritten)
-  const VisibleKeys vk = visible_keys(min(a.len[b], a.max_T), a.window, a.sink);
+  const int tid = threadIdx.x;
+  // splits run over the visible keys (all L, or the sink and window ones)
+  const int len_in = a.len[b];
+  // FUSED: a full sequence is left as it is (cache, length, output); every
+  // workgroup of the sequence reads the same len_in, so they all skip it
+  const bool full = FUSED && len_in >= a.max_T;
+  int32_t *const step_b = FUSED ? a.counters + (size_t)b * kStepSlots : nullptr;
+  // several splits: the attended count (or -1: skipped) for the merge kernel,
+  // which commits it as the new length
+  if (FUSED && a.n_splits > 1 && split == 0 && blockIdx.y == 0 && tid == 0) step_b[1] = full ? -1 : len_in + 1;
+  if (full) return;
+  const int L = FUSED ? len_in + 1 : attended_keys(a, b, len_in);
+  if (L < 0) return;  // an extend past the sequence's capacity: skipped
+  const VisibleKeys vk = visible_keys(L, a.window, a.sink);
   const int kb = split * a.chunk;  // first visible index of this split
-  if (kb >= vk.count) return;  // empty split
+  if (kb >= vk.count) return;  // empty split (never with FUSED and a single split)
+  // one split: every workgroup of the sequence counts itself in (after its
+  // read of len[b]); the last one advances len[b] and clears the counter
+  int len_ticket = 0;
+  if (FUSED && a.n_splits == 1 && tid == 0)
+    len_ticket = __hip_atomic_fetch_add(step_b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto finish_len = [&]() {
+    if (FUSED && a.n_splits == 1 && tid == 0 && len_ticket == (int)gridDim.y - 1) {
+      __hip_atomic_store(step_b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a.len_rw[b] = len_in + 1;
+    }
+  };
   const int rows = min(a.chunk, vk.count - kb);
   const int n_valid = (vk.count + a.chunk - 1) / a.chunk;
+  // FUSED: the split holding the last visible key holds the new row, which
+  // is not streamed from the cache
+  const bool holds_new = FUSED && kb + rows == vk.count;
+  const int srows = rows - (holds_new ? 1 : 0);  // rows streamed from the cache
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int rg = lane / LPR;
@@ -201,19 +246,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     for (int e = 0; e < NV * EPL; ++e) acc[g][e] = 0.f;
   }
 
-  const int steps = (rows + ROWS_PER_STEP - 1) / ROWS_PER_STEP;
+  const int steps = (srows + ROWS_PER_STEP - 1) / ROWS_PER_STEP;
   const int nb = (steps + U - 1) / U;
   const float c = a.scale_log2;
 
   uint4 k0[U][NV], v0[U][NV], k1[U][NV], v1[U][NV];
   // Rows past the split's end are clamped to its last row (always valid: the
-  // split is non-empty) and their scores masked to -inf.  Keeping the loads
-  // free of branches lets the compiler wait for one batch while the next is
-  // still in flight.
+  // split is non-empty; with FUSED a split holding only the new row clamps
+  // to that row's cache slot, inside the sequence's region and never used)
+  // and their scores masked to -inf.  Keeping the loads free of branches
+  // lets the compiler wait for one batch while the next is still in flight.
+  const int last_row = max(srows, 1) - 1;
   auto load = [&](int ib, uint4 (&kr)[U][NV], uint4 (&vr)[U][NV]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      int r = min(((ib * U + u) * NW + wave) * RPW + rg, rows - 1);
+      int r = min(((ib * U + u) * NW + wave) * RPW + rg, last_row);
       size_t row;
       if constexpr (PAGED) {
         const bool in_b = r >= jump;
@@ -239,7 +286,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = ((ib * U + u) * NW + wave) * RPW + rg;
-      const bool ok = r < rows;
+      const bool ok = r < srows;
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
         float d = dot16(Tag{}, qv[g][0], kr[u][0]);
@@ -305,6 +352,46 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     if (ib + 1 < nb) compute(ib + 1, k1, v1);
   }
 
+  if constexpr (FUSED) {
+    // the new row: its score and value folded into the state of wave 0's
+    // first row group (exact maximum, no lazy threshold), and written into
+    // the cache by the first query sub-group of the KV head
+    if (holds_new && wave == 0 && rg == 0) {
+      const size_t nr = ((size_t)(b * a.kv_heads + kvh) * D + cl) * ESZ;
+      uint4 kn[NV], vn[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        kn[v] = *(const uint4 *)((const char *)a.k_new + nr + (size_t)v * VSTRIDE * ESZ);
+        vn[v] = *(const uint4 *)((const char *)a.v_new + nr + (size_t)v * VSTRIDE * ESZ);
+      }
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float d = dot16(Tag{}, qv[g][0], kn[0]);
+#pragma unroll
+        for (int v = 1; v < NV; ++v) d += dot16(Tag{}, qv[g][v], kn[v]);
+        const float sn = row_sum<LPR>(d) * c;
+        const float mn = fmaxf(m[g], sn);
+        const float al = fast_exp2(m[g] - mn);
+        const float p = fast_exp2(sn - mn);
+        l[g] = fmaf(l[g], al, p);
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            acc[g][v * EPL + e] = fmaf(p, elem(Tag{}, vn[v], e), acc[g][v * EPL + e] * al);
+        m[g] = mn;
+      }
+      if (unit == kvh * subs) {
+        const size_t dst = ((size_t)(b * a.kv_heads + kvh) * a.max_T + len_in) * D + cl;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          *(uint4 *)((char *)a.k_cache_rw + (dst + (size_t)v * VSTRIDE) * ESZ) = kn[v];
+          *(uint4 *)((char *)a.v_cache_rw + (dst + (size_t)v * VSTRIDE) * ESZ) = vn[v];
+        }
+      }
+    }
+  }
+
   // merge the row groups of this wave (lanes that hold the same columns)
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1) {
@@ -361,6 +448,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       }
       store_out(a.o, (size_t)(b * RS + h0 + g) * D + d, num / den, a.o_dt);
     }
+    finish_len();
     return;
   }
 
@@ -390,6 +478,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   }
 }
 
+// query heads per decode workgroup for G query heads per KV head: the
+// largest of 8, 4, 3, 2 that divides G (1 otherwise)
+inline int group_tile(int G) {
+  return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 3 == 0) ? 3 : (G % 2 == 0) ? 2 : 1;
+}
+
 // threads of the merge kernel: one per output element up to 256, else a
 // block size that divides the GT * D outputs evenly
 template <int D, int GT>
@@ -403,7 +497,12 @@ constexpr int merge_threads() {
 // each thread owns whole output elements and issues the loads of eight
 // splits (their m, l and its u column) at once: one dependent round trip per
 // eight splits, no shared memory and no barrier.
-template <int D, int GT>
+//
+// STEP (the fused decode step over several splits): the attended count comes
+// from the decode kernel's record instead of len[b] (-1: the sequence was
+// full and is skipped), and unit 0 of each sequence commits it as the new
+// length; no workgroup of this kernel reads len[b].
+template <int D, int GT, bool STEP = false>
 __global__ __launch_bounds__((merge_threads<D, GT>())) void decode_merge_kernel(DecodeArgs a) {
   constexpr int THREADS = merge_threads<D, GT>();
   constexpr int E = GT * D / THREADS;  // outputs per thread
@@ -416,7 +515,10 @@ __global__ __launch_bounds__((merge_threads<D, GT>())) void decode_merge_kernel(
   const int unit = blockIdx.x;
   const int kvh = unit / subs;
   const int h0 = kvh * RK + (unit - kvh * subs) * GT;
-  const int ns = (visible_keys(min(a.len[b], a.max_T), a.window, a.sink).count + a.chunk - 1) / a.chunk;
+  const int L = STEP ? a.counters[(size_t)b * kStepSlots + 1] : attended_keys(a, b, a.len[b]);
+  if (L < 0) return;
+  if (STEP && unit == 0 && threadIdx.x == 0) a.len_rw[b] = L;
+  const int ns = (visible_keys(L, a.window, a.sink).count + a.chunk - 1) / a.chunk;
   if (ns <= 1) return;
   const float *ws_unit = a.ws + (size_t)(b * RS + h0) * a.n_splits * (D + 2);
 
@@ -490,6 +592,21 @@ static hipError_t launch_gt_layout(const DecodeArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// the fused decode step (contiguous cache, one query per head): one launch
+// for a single-split cache, else the decode kernel and the merge kernel that
+// commits the lengths
+template <class Tag, int D, int GT>
+static hipError_t launch_gt_step(const DecodeArgs &a, hipStream_t s) {
+  constexpr int NV = 1, NW = 4;
+  constexpr int U = GT >= 4 ? 4 : 6;
+  const int units = a.q_heads / GT;
+  decode_kernel<Tag, D, GT, U, NV, NW, false, false, true><<<dim3(a.n_splits, units, a.batch), NW * 64, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_splits == 1) return e;
+  decode_merge_kernel<D, GT, true><<<dim3(units, a.batch), merge_threads<D, GT>(), 0, s>>>(a);
+  return hipGetLastError();
+}
+
 template <class Tag, int D, int GT, bool VER = false>
 static hipError_t launch_gt(const DecodeArgs &a, hipStream_t s) {
   if (a.table) return launch_gt_layout<Tag, D, GT, true, VER>(a, s);
@@ -509,13 +626,33 @@ static hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
       default: return hipErrorInvalidValue;  // the host routes other shapes to the prefill kernels
     }
   }
-  const int GT = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 3 == 0) ? 3 : (G % 2 == 0) ? 2 : 1;
-  switch (GT) {
+  switch (group_tile(G)) {
     case 8: return launch_gt<Tag, D, 8>(a, s);
     case 4: return launch_gt<Tag, D, 4>(a, s);
     case 3: return launch_gt<Tag, D, 3>(a, s);
     case 2: return launch_gt<Tag, D, 2>(a, s);
     default: return launch_gt<Tag, D, 1>(a, s);
+  }
+}
+
+template <class Tag, int D>
+static hipError_t launch_step_typed(const DecodeArgs &a, hipStream_t s) {
+  switch (group_tile(a.q_heads / a.kv_heads)) {
+    case 8: return launch_gt_step<Tag, D, 8>(a, s);
+    case 4: return launch_gt_step<Tag, D, 4>(a, s);
+    case 3: return launch_gt_step<Tag, D, 3>(a, s);
+    case 2: return launch_gt_step<Tag, D, 2>(a, s);
+    default: return launch_gt_step<Tag, D, 1>(a, s);
+  }
+}
+
+template <class Tag>
+static hipError_t launch_step_dim(const DecodeArgs &a, hipStream_t s) {
+  switch (a.head_dim) {
+    case 32: return launch_step_typed<Tag, 32>(a, s);
+    case 64: return launch_step_typed<Tag, 64>(a, s);
+    case 128: return launch_step_typed<Tag, 128>(a, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -525,6 +662,16 @@ static hipError_t launch_dim(const DecodeArgs &a, hipStream_t s) {
     case 32: return launch_typed<Tag, 32>(a, s);
     case 64: return launch_typed<Tag, 64>(a, s);
     case 128: return launch_typed<Tag, 128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t s) {
+  if (a.table || a.tokens != 1 || !a.k_new || !a.v_new || !a.counters || !a.len_rw) return hipErrorInvalidValue;
+  switch (a.dt) {
+    case KVATTN_F32: return launch_step_dim<TagF32>(a, s);
+    case KVATTN_F16: return launch_step_dim<TagF16>(a, s);
+    case KVATTN_BF16: return launch_step_dim<TagBF16>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -169,15 +169,19 @@ int kvattn_cache_alloc(kvattn_cache **out, int layers, int batch, int q_heads, i
   // split-K workspace for decode and for the short extends run on the decode
   // kernels (up to kMaxVerifyTokens query positions per head)
   const size_t ws_bytes = sizeof(float) * (size_t)batch * q_heads * kMaxVerifyTokens * c->n_splits * (head_dim + 2);
+  const size_t cnt_bytes = sizeof(int32_t) * (size_t)batch * kStepSlots;
   e = hipMalloc((void **)&c->d_len, len_bytes);
   if (e == hipSuccess) e = hipMalloc((void **)&c->d_ws, ws_bytes);
+  if (e == hipSuccess) e = hipMalloc((void **)&c->d_cnt, cnt_bytes);
   if (e == hipSuccess) e = hipMemset(c->d_len, 0, len_bytes);
+  if (e == hipSuccess) e = hipMemset(c->d_cnt, 0, cnt_bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     int rc = hip_fail(e, "cache side buffers");
     (void)hipGetLastError();
     if (c->d_len) (void)hipFree(c->d_len);
     if (c->d_ws) (void)hipFree(c->d_ws);
+    if (c->d_cnt) (void)hipFree(c->d_cnt);
     if (c->owns_base) (void)hipFree(c->base);
     delete c;
     return e == hipErrorOutOfMemory ? KVATTN_ERR_OOM : rc;
@@ -191,11 +195,13 @@ int kvattn_cache_free(kvattn_cache *c) {
   hipError_t e = hipDeviceSynchronize();
   hipError_t e1 = hipFree(c->d_len);
   hipError_t e2 = hipFree(c->d_ws);
+  hipError_t e4 = hipFree(c->d_cnt);
   hipError_t e3 = c->owns_base ? hipFree(c->base) : hipSuccess;
   delete c;
   if (e != hipSuccess) return hip_fail(e, "kvattn_cache_free sync");
   if (e1 != hipSuccess) return hip_fail(e1, "hipFree(lengths)");
   if (e2 != hipSuccess) return hip_fail(e2, "hipFree(workspace)");
+  if (e4 != hipSuccess) return hip_fail(e4, "hipFree(split counters)");
   if (e3 != hipSuccess) return hip_fail(e3, "hipFree(payload)");
   return KVATTN_OK;
 }
@@ -330,11 +336,10 @@ int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, cons
 
   const int G = c->q_heads / c->kv_heads;
   if (T == 1 || verify_on_decode(G, T, c->window[layer])) {
-    // short extend (one decode step, or a multi-token verification): commit
-    // the lengths first, then the decode kernels with T query positions per
-    // head, token t at position len[b] - T + t
-    e = launch_add_lengths(len, c->batch, T, st);
-    if (e != hipSuccess) return hip_fail(e, "extend length update launch");
+    // short extend (one decode step, or a multi-token verification): the
+    // decode kernels with T query positions per head, token t at position
+    // len[b] + t (the lengths do not include the new rows yet), then the
+    // lengths are committed
     DecodeArgs d;
     d.k_layer = layer_k(c, layer);
     d.v_layer = layer_v(c, layer);
@@ -358,8 +363,11 @@ int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, cons
     d.block_log2 = 0;
     d.max_blocks = 0;
     d.tokens = T;
+    d.len_pending = 1;
     e = launch_decode(d, st);
     if (e != hipSuccess) return hip_fail(e, "extend (decode form) launch");
+    e = launch_add_lengths(len, c->batch, T, c->max_T, nullptr, 0, st);
+    if (e != hipSuccess) return hip_fail(e, "extend length update launch");
     for (int b = 0; b < c->batch; ++b) hl[b] += T;
     return KVATTN_OK;
   }
@@ -391,7 +399,7 @@ int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, cons
   if (e != hipSuccess) return hip_fail(e, "extend attention launch");
 
   // 3. commit: len[b] += T
-  e = launch_add_lengths(len, c->batch, T, st);
+  e = launch_add_lengths(len, c->batch, T, c->max_T, nullptr, 0, st);
   if (e != hipSuccess) return hip_fail(e, "extend length update launch");
   for (int b = 0; b < c->batch; ++b) hl[b] += T;
   return KVATTN_OK;
@@ -425,18 +433,11 @@ int kvattn_append(kvattn_cache *c, int layer, const void *k_new, const void *v_n
   return KVATTN_OK;
 }
 
-int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scale,
-                  kvattn_dtype o_dtype, void *stream) {
-  int rc = check_layer(c, layer);
-  if (rc) return rc;
-  if (!q || !o) return KVATTN_ERR_INVALID_ARG;
-  if (!(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
-  if (!valid_out_dtype(c, o_dtype)) return KVATTN_ERR_UNSUPPORTED;
-  const int32_t *hl = &c->h_len[(size_t)layer * c->batch];
-  for (int b = 0; b < c->batch; ++b)
-    if (hl[b] <= 0) return KVATTN_ERR_STATE;
-  rc = check_device(c);
-  if (rc) return rc;
+}  // extern "C"
+
+namespace {
+
+DecodeArgs cache_decode_args(kvattn_cache *c, int layer, const void *q, void *o, float scale, kvattn_dtype o_dtype) {
   DecodeArgs a;
   a.k_layer = layer_k(c, layer);
   a.v_layer = layer_v(c, layer);
@@ -459,6 +460,51 @@ int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scal
   a.table = nullptr;
   a.block_log2 = 0;
   a.max_blocks = 0;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvattn_append_decode(kvattn_cache *c, int layer, const void *k_new, const void *v_new, const void *q, void *o,
+                         float scale, kvattn_dtype o_dtype, void *stream) {
+  int rc = check_layer(c, layer);
+  if (rc) return rc;
+  if (!k_new || !v_new || !q || !o) return KVATTN_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
+  if (!valid_out_dtype(c, o_dtype)) return KVATTN_ERR_UNSUPPORTED;
+  int32_t *hl = &c->h_len[(size_t)layer * c->batch];
+  for (int b = 0; b < c->batch; ++b)
+    if (hl[b] >= c->max_T) return KVATTN_ERR_CAPACITY;
+  rc = check_device(c);
+  if (rc) return rc;
+  DecodeArgs a = cache_decode_args(c, layer, q, o, scale, o_dtype);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache_rw = layer_k(c, layer);
+  a.v_cache_rw = layer_v(c, layer);
+  a.len_rw = c->d_len + (size_t)layer * c->batch;
+  a.counters = c->d_cnt;
+  hipError_t e = launch_decode_step(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode step launch");
+  for (int b = 0; b < c->batch; ++b) hl[b] += 1;
+  return KVATTN_OK;
+}
+
+int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scale,
+                  kvattn_dtype o_dtype, void *stream) {
+  int rc = check_layer(c, layer);
+  if (rc) return rc;
+  if (!q || !o) return KVATTN_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
+  if (!valid_out_dtype(c, o_dtype)) return KVATTN_ERR_UNSUPPORTED;
+  const int32_t *hl = &c->h_len[(size_t)layer * c->batch];
+  for (int b = 0; b < c->batch; ++b)
+    if (hl[b] <= 0) return KVATTN_ERR_STATE;
+  rc = check_device(c);
+  if (rc) return rc;
+  DecodeArgs a = cache_decode_args(c, layer, q, o, scale, o_dtype);
   hipError_t e = launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return KVATTN_OK;
@@ -533,6 +579,7 @@ struct kvattn_paged {
   int32_t *d_len;              // [layers][slots]
   std::vector<int32_t> h_len;  // host mirror
   int32_t *d_table;            // [slots][max_blocks]
+  int32_t *d_nblk;             // [slots] blocks assigned per slot (device copy of h_nblk)
   std::vector<int> h_nblk;     // table entries set per slot
   std::vector<int> window, sink;  // per layer; window 0 = none
   float *d_ws;
@@ -637,17 +684,21 @@ int kvattn_paged_alloc(kvattn_paged **out, int layers, int slots, int max_blocks
   const size_t len_bytes = sizeof(int32_t) * (size_t)layers * slots;
   const size_t tab_bytes = sizeof(int32_t) * (size_t)slots * max_blocks;
   const size_t ws_bytes = sizeof(float) * (size_t)slots * q_heads * kMaxVerifyTokens * p->n_splits * (head_dim + 2);
+  const size_t nblk_bytes = sizeof(int32_t) * (size_t)slots;
   e = hipMalloc((void **)&p->d_len, len_bytes);
   if (e == hipSuccess) e = hipMalloc((void **)&p->d_table, tab_bytes);
+  if (e == hipSuccess) e = hipMalloc((void **)&p->d_nblk, nblk_bytes);
   if (e == hipSuccess) e = hipMalloc((void **)&p->d_ws, ws_bytes);
   if (e == hipSuccess) e = hipMemset(p->d_len, 0, len_bytes);
   if (e == hipSuccess) e = hipMemset(p->d_table, 0, tab_bytes);
+  if (e == hipSuccess) e = hipMemset(p->d_nblk, 0, nblk_bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     int rc = hip_fail(e, "paged cache side buffers");
     (void)hipGetLastError();
     if (p->d_len) (void)hipFree(p->d_len);
     if (p->d_table) (void)hipFree(p->d_table);
+    if (p->d_nblk) (void)hipFree(p->d_nblk);
     if (p->d_ws) (void)hipFree(p->d_ws);
     if (p->owns_base) (void)hipFree(p->base);
     delete p;
@@ -662,12 +713,14 @@ int kvattn_paged_free(kvattn_paged *p) {
   hipError_t e = hipDeviceSynchronize();
   hipError_t e1 = hipFree(p->d_len);
   hipError_t e2 = hipFree(p->d_table);
+  hipError_t e5 = hipFree(p->d_nblk);
   hipError_t e3 = hipFree(p->d_ws);
   hipError_t e4 = p->owns_base ? hipFree(p->base) : hipSuccess;
   delete p;
   if (e != hipSuccess) return hip_fail(e, "kvattn_paged_free sync");
   if (e1 != hipSuccess) return hip_fail(e1, "hipFree(lengths)");
   if (e2 != hipSuccess) return hip_fail(e2, "hipFree(block tables)");
+  if (e5 != hipSuccess) return hip_fail(e5, "hipFree(block counts)");
   if (e3 != hipSuccess) return hip_fail(e3, "hipFree(workspace)");
   if (e4 != hipSuccess) return hip_fail(e4, "hipFree(pool)");
   return KVATTN_OK;
@@ -698,6 +751,11 @@ int kvattn_paged_set_blocks(kvattn_paged *p, int slot, const int32_t *host_block
                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "block table upload");
   }
+  // the device copy of the slot's block count bounds every write at a
+  // device-held position (appends and extends replayed from a graph)
+  const int32_t nb = n_blocks;
+  hipError_t e = launch_set_lengths(p->d_nblk + slot, 1, 1, &nb, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "block count upload");
   p->h_nblk[slot] = n_blocks;
   return KVATTN_OK;
 }
@@ -808,6 +866,7 @@ int kvattn_paged_prefill(kvattn_paged *p, int layer, const void *q, const void *
   w.row_bytes = p->head_dim * p->elem;
   w.block_log2 = p->block_log2;
   w.max_blocks = p->max_blocks;
+  w.slot_blocks = p->d_nblk;
   e = launch_paged_write(w, st);
   if (e != hipSuccess) return hip_fail(e, "paged prefill write launch");
   for (int s = 0; s < p->slots; ++s) p->h_len[(size_t)layer * p->slots + s] = T;
@@ -836,6 +895,7 @@ int kvattn_paged_append(kvattn_paged *p, int layer, const void *k_new, const voi
   a.table = p->d_table;
   a.block_log2 = p->block_log2;
   a.max_blocks = p->max_blocks;
+  a.slot_blocks = p->d_nblk;
   hipError_t e = launch_append(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "paged append launch");
   for (int s = 0; s < p->slots; ++s) hl[s] += 1;
@@ -872,14 +932,13 @@ int kvattn_paged_extend(kvattn_paged *p, int layer, const void *q, const void *k
   cp.table = p->d_table;
   cp.block_log2 = p->block_log2;
   cp.max_blocks = p->max_blocks;
+  cp.slot_blocks = p->d_nblk;
   hipError_t e = launch_extend_copy(cp, st);
   if (e != hipSuccess) return hip_fail(e, "paged extend copy launch");
 
   const int G = p->q_heads / p->kv_heads;
   if (T == 1 || verify_on_decode(G, T, p->window[layer])) {
     // short extend on the decode kernels, as for the contiguous cache
-    e = launch_add_lengths(len, p->slots, T, st);
-    if (e != hipSuccess) return hip_fail(e, "paged extend length update launch");
     DecodeArgs d;
     d.k_layer = paged_k(p, layer);
     d.v_layer = paged_v(p, layer);
@@ -903,8 +962,12 @@ int kvattn_paged_extend(kvattn_paged *p, int layer, const void *q, const void *k
     d.block_log2 = p->block_log2;
     d.max_blocks = p->max_blocks;
     d.tokens = T;
+    d.len_pending = 1;
+    d.slot_blocks = p->d_nblk;
     e = launch_decode(d, st);
     if (e != hipSuccess) return hip_fail(e, "paged extend (decode form) launch");
+    e = launch_add_lengths(len, p->slots, T, 0, p->d_nblk, p->block_log2, st);
+    if (e != hipSuccess) return hip_fail(e, "paged extend length update launch");
     for (int s = 0; s < p->slots; ++s) hl[s] += T;
     return KVATTN_OK;
   }
@@ -936,11 +999,12 @@ int kvattn_paged_extend(kvattn_paged *p, int layer, const void *q, const void *k
   a.table = p->d_table;
   a.block_log2 = p->block_log2;
   a.max_blocks = p->max_blocks;
+  a.slot_blocks = p->d_nblk;
   e = launch_extend_attention(a, st);
   if (e != hipSuccess) return hip_fail(e, "paged extend attention launch");
 
   // 3. commit: len[b] += T
-  e = launch_add_lengths(len, p->slots, T, st);
+  e = launch_add_lengths(len, p->slots, T, 0, p->d_nblk, p->block_log2, st);
   if (e != hipSuccess) return hip_fail(e, "paged extend length update launch");
   for (int s = 0; s < p->slots; ++s) hl[s] += T;
   return KVATTN_OK;
@@ -980,6 +1044,7 @@ int kvattn_paged_decode(kvattn_paged *p, int layer, const void *q, void *o, floa
   a.table = p->d_table;
   a.block_log2 = p->block_log2;
   a.max_blocks = p->max_blocks;
+  a.slot_blocks = p->d_nblk;
   hipError_t e = launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "paged decode launch");
   return KVATTN_OK;

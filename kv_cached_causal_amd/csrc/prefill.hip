@@ -153,6 +153,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void prefill_mfma_kernel(
   const T *qb = (const T *)a.q + (size_t)bh * Tn * D;
   // query row i sits at absolute position off + i and sees keys 0 .. off + i
   const int off = a.offsets ? a.offsets[b] : 0;
+  // an extend past the sequence's capacity (only on a replayed graph) is
+  // left to the copy and length kernels to skip; no output row is written
+  if (a.offsets && off + Tn > seq_capacity(a.slot_blocks, b, a.block_log2, a.max_T)) return;
   const int last_key = off + Tn - 1;
   // paged (extend over a paged cache): k/v are the block pools and a key's
   // row is found through the sequence's block table
@@ -497,6 +500,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * QW;
   const int off = a.offsets ? a.offsets[b] : 0;
+  // an extend past the sequence's capacity (only on a replayed graph) is
+  // left to the copy and length kernels to skip; no output row is written
+  if (a.offsets && off + Tn > seq_capacity(a.slot_blocks, b, a.block_log2, a.max_T)) return;
   const int dlo = (off + qw0) / BN;
   const int dhi = (off + qw0 + QW - 1) / BN;
   const int stid = tid & 255;
@@ -800,6 +806,9 @@ __global__ __launch_bounds__(64 * kF32Waves) void prefill_f32_kernel(PrefillArgs
 
   const float *qb = (const float *)a.q + (size_t)bh * Tn * D;
   const int off = a.offsets ? a.offsets[b] : 0;  // absolute position of query row 0
+  // an extend past the sequence's capacity (only on a replayed graph) is
+  // left to the copy and length kernels to skip; no output row is written
+  if (a.offsets && off + Tn > seq_capacity(a.slot_blocks, b, a.block_log2, a.max_T)) return;
   // with a block table, k/v are the paged pools and rows are looked up per key
   const float4_t *kb = (const float4_t *)a.k + (a.table ? 0 : (size_t)(b * a.kv_heads + g) * a.kv_rows * C4);
   const float4_t *vb = (const float4_t *)a.v + (a.table ? 0 : (size_t)(b * a.kv_heads + g) * a.kv_rows * C4);
