@@ -5,8 +5,8 @@ workload with 1% of K rows scaled by 8:
   * prefill: a B=1 causal prefill of an 8192-token prompt through all 32
     layers (each layer writes its K/V into the cache), then
   * decode: one decode step of a batch of 32 sequences with ragged contexts
-    drawn uniformly from [512, 4096], through all 32 layers (append one K/V
-    row, then attend the whole cache).
+    drawn uniformly from [512, 4096], through all 32 layers (one fused call
+    per layer appends the new K/V row and attends the whole cache).
 Inputs are seeded synthetic N(0,1) tensors generated on the device and
 resident in HBM before timing starts.  The same run also times a decode step
 of the 32-layer bf16 GQA workload (32 query / 8 KV heads, batch 16, context
@@ -15,9 +15,10 @@ of the 32-layer bf16 GQA workload (32 query / 8 KV heads, batch 16, context
 Printed: one JSON line.  `value` is the decode step's algorithmic HBM bytes
 per second (K and V read once per KV head, plus q, o and the appended row);
 the prefill's algorithmic TFLOP/s (4*B*H*D*T(T+1)/2 per layer) sits in
-`prefill`.  Kernel durations come from HIP events on the launch stream.
-`cpu_baseline` times the CPU fp64 oracle on a bounded sample of the same
-workload.
+`prefill`.  Kernel durations come from HIP events on the launch stream: the
+median over every timed launch, with p10 and p90.  `cpu_baseline` times the
+CPU fp64 oracle on a bounded sample of the same workload (cached decode,
+recompute-everything decode, naive prefill).
 """
 from __future__ import annotations
 
@@ -52,7 +53,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skip-gqa", action="store_true")
     p.add_argument("--only", choices=["prefill", "decode", "gqa"], default=None,
@@ -86,10 +87,10 @@ PREFILL_SOURCES = ["prefill.hip", "common.hpp"]
 CALIB_BYTES = 4 << 30
 # kernels of each measured launch, by a substring of the demangled or mangled name
 TRAFFIC_KERNELS = {
-    "decode_ragged_b32": (DECODE_SOURCES, ["decode_kernel<kvattn::TagF16, 128, 1, 6, 1, 4, false, false>",
-                                           "decode_merge_kernel<128, 1>"]),
-    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4, 4, 1, 4, false, false>",
-                                        "decode_merge_kernel<128, 4>"]),
+    "decode_ragged_b32": (DECODE_SOURCES, ["decode_kernel<kvattn::TagF16, 128, 1, 6, 1, 4, false, false, true>",
+                                           "decode_merge_kernel<128, 1, true>"]),
+    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4, 4, 1, 4, false, false, true>",
+                                        "decode_merge_kernel<128, 4, true>"]),
     "prefill_t8192": (PREFILL_SOURCES, ["prefill_pipe_kernelIDF16_Li128"]),
 }
 
@@ -242,7 +243,7 @@ def small_head_prefill(kv, dev, mceil, eceil, reps=20):
 
 def small_config_measurements(kv, dev):
     """The three small workloads, whole: prompt prefill of every layer, then every decode step
-    (append + decode per layer), timed with HIP events around the prefills and around the steps
+    (one fused append + decode call per layer), timed with HIP events around the prefills and around the steps
     (median of five runs).  Their caches (0.3-69 MB) stay in
     the 256 MB last-level cache and their launches take a few microseconds, so they are reported in
     microseconds per step (launch-bound), not as bandwidth."""
@@ -262,8 +263,7 @@ def small_config_measurements(kv, dev):
         pre = [c.bind_prefill(l, *ins[l], scale=w.scale) for l in range(L)]
         kn, vn, qd = rnd((B, Hkv, 1, D)), rnd((B, Hkv, 1, D)), rnd((B, H, 1, D))
         od = torch.empty((B, H, 1, D), dtype=dt, device=dev)
-        app = [c.bind_append(l, kn, vn) for l in range(L)]
-        dec = [c.bind_decode(l, qd, od, scale=w.scale) for l in range(L)]
+        dec = [c.bind_append_decode(l, kn, vn, qd, od, scale=w.scale) for l in range(L)]
 
         def run():
             # one event pair around all layers' prefills and one around all steps: an event
@@ -276,7 +276,6 @@ def small_config_measurements(kv, dev):
             e[1].record()
             for _ in range(w.steps):
                 for l in range(L):
-                    app[l]()
                     dec[l]()
             e[2].record()
             torch.cuda.synchronize()
@@ -347,7 +346,7 @@ def heavy_scale_(k_block: torch.Tensor, L, frac, gen: torch.Generator):
 
 
 class Timer:
-    """Per-launch HIP event pairs on the current stream."""
+    """Per-launch HIP event pairs on the current stream (the stream the library's calls are enqueued on)."""
 
     def __init__(self):
         self.pairs = []
@@ -362,8 +361,21 @@ class Timer:
         e.record()
         self.pairs.append((s, e))
 
+    def times_ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
     def mean_ms(self):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+        return float(np.mean(self.times_ms())) if self.pairs else float("nan")
+
+    def median_ms(self):
+        return float(np.median(self.times_ms())) if self.pairs else float("nan")
+
+    def spread(self):
+        """Launch count, median, p10, p90 and mean of the per-launch times (ms)."""
+        t = np.array(self.times_ms())
+        return {"launches": int(t.size), "median_ms": round(float(np.median(t)), 5),
+                "p10_ms": round(float(np.percentile(t, 10)), 5), "p90_ms": round(float(np.percentile(t, 90)), 5),
+                "mean_ms": round(float(t.mean()), 5)}
 
 
 def setup_decode(kv, w, dev, seed):
@@ -383,17 +395,36 @@ def setup_decode(kv, w, dev, seed):
     outs = [torch.empty_like(q) for q in qs]
     appends = [cache.bind_append(l, kn[l], vn[l]) for l in range(w.layers)]
     decodes = [cache.bind_decode(l, qs[l], outs[l], scale=w.scale) for l in range(w.layers)]
+    # the decode step as one call per layer: append + decode fused (kvattn_append_decode)
+    steps = [cache.bind_append_decode(l, kn[l], vn[l], qs[l], outs[l], scale=w.scale) for l in range(w.layers)]
     e = 2
     bytes_kernel = int(2 * w.kv_heads * w.head_dim * e * int(ctx.sum())   # K and V once per KV head
                        + 2 * w.batch * w.q_heads * w.head_dim * e)         # q in, o out
     bytes_step_layer = bytes_kernel + 2 * w.batch * w.kv_heads * w.head_dim * e  # + appended row
     return dict(w=w, ctx=ctx, cache=cache, q=qs, kn=kn, vn=vn, o=outs, appends=appends, decodes=decodes,
-                bytes_kernel=bytes_kernel, bytes_step=bytes_step_layer * w.layers)
+                steps=steps, bytes_kernel=bytes_kernel, bytes_step_layer=bytes_step_layer,
+                bytes_step=bytes_step_layer * w.layers)
+
+
+def reset_decode(d):
+    """Lengths back to the step's starting contexts (outside the timed region)."""
+    d["cache"].set_lengths([int(L) - 1 for L in d["ctx"]])
 
 
 def decode_step(d, timer=None):
-    w, c = d["w"], d["cache"]
-    c.set_lengths([int(L) - 1 for L in d["ctx"]])
+    """One decode step of every layer: the fused append + decode call per layer (timed per launch)."""
+    w = d["w"]
+    for layer in range(w.layers):
+        ev = timer.start() if timer else None
+        d["steps"][layer]()
+        if timer:
+            timer.stop(ev)
+
+
+def decode_step_two_calls(d, timer=None):
+    """The same step as two calls per layer (kvattn_append, then kvattn_decode; the decode timed)."""
+    w = d["w"]
+    reset_decode(d)
     for layer in range(w.layers):
         d["appends"][layer]()
         ev = timer.start() if timer else None
@@ -423,9 +454,12 @@ def setup_prefill(kv, w, dev, seed):
     return dict(w=w, T=T, cache=cache, q=q, k=k, v=v, o=o, calls=calls, flops_layer=flops)
 
 
+def reset_prefill(p):
+    p["cache"].set_lengths([0])
+
+
 def prefill_step(p, timer=None):
-    w, c = p["w"], p["cache"]
-    c.set_lengths([0])
+    w = p["w"]
     for layer in range(w.layers):
         ev = timer.start() if timer else None
         p["calls"][layer]()
@@ -620,6 +654,37 @@ def decoder_measurements(kv, dev, prompt=4096, new_tokens=128):
     return out
 
 
+def prefill_memory_and_clock(kv, pre):
+    """Peak device memory while the 32 prefills run (no T x T buffer: the prefill allocates
+    nothing beyond its inputs, outputs and the cache), and the sustained shader clock of one
+    prefill launch (workgroup 0's shader-clock and 100 MHz real-time counters)."""
+    import ctypes
+    reset_prefill(pre)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    prefill_step(pre)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated()
+    w, T = pre["w"], pre["T"]
+    sample = torch.zeros(2, dtype=torch.int64, device=pre["q"][0].device)
+    c = pre["cache"]
+    c.set_lengths([0], layer=0)
+    rc = kv.lib().kvattn_measure_prefill_clock(
+        c._handle, 0, ctypes.c_void_p(pre["q"][0].data_ptr()), ctypes.c_void_p(pre["k"][0].data_ptr()),
+        ctypes.c_void_p(pre["v"][0].data_ptr()), ctypes.c_void_p(pre["o"][0].data_ptr()), T, ctypes.c_float(w.scale),
+        1, ctypes.c_void_p(sample.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"kvattn_measure_prefill_clock failed ({rc})")
+    torch.cuda.synchronize()
+    cyc, ticks = (int(x) for x in sample.cpu().tolist())
+    clock = cyc / ticks * 0.1 if ticks > 0 else None
+    return {"peak_bytes_during_prefill": int(peak), "allocated_before_bytes": int(base),
+            "extra_bytes_during_prefill": int(peak - base),
+            "tt_scores_fp32_bytes_per_layer": int(w.q_heads * T * T * 4),
+            "sustained_clock_ghz": round(clock, 3) if clock else None}
+
+
 def timed(fn, steps, warmup):
     for _ in range(warmup):
         fn(None)
@@ -633,17 +698,32 @@ def timed(fn, steps, warmup):
     return wall, timer.mean_ms()
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline():
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+    """The oracle, as it stands, on a bounded sample of the same workload: the cached decode
+    (one layer-step of 8 sequences), the recompute-everything decode (one sequence, 4 heads:
+    every row of the history recomputed, as the uncached generation loop does) and the naive
+    prefill (2 heads at T=8192, materialising T x T)."""
     import oracle
     w = si.WORKLOADS[5]
     cores = len(os.sched_getaffinity(0))
-    threads = cores
+    blas_threads, blas = None, None
     try:
         from threadpoolctl import threadpool_info
-        info = threadpool_info()
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
         if info:
-            threads = max(i.get("num_threads", 0) for i in info)
+            blas_threads = max(i.get("num_threads", 0) for i in info)
+            blas = info[0].get("internal_api")
     except Exception:
         pass
     ctx = si.decode_contexts(w)
@@ -673,6 +753,26 @@ def cpu_baseline():
         t_dec = time.perf_counter() - t0
     dec_bytes = reps * (2 * w.kv_heads * w.head_dim * 2 * int(ctx[:n_seq].sum())
                         + 2 * n_seq * w.q_heads * w.head_dim * 2)
+    cached_us_per_seq_head = t_dec / reps / (n_seq * w.q_heads) * 1e6
+    # recompute-everything decode: sequence 0, 4 heads, every row of its L positions recomputed
+    rh = 4
+    L0 = int(ctx[0])
+    qh = si.round_to(np.random.default_rng(55).standard_normal((1, rh, L0, w.head_dim)), w.dtype)
+    qh[0, :, L0 - 1] = q[0, :rh, 0]
+    log(f"cpu baseline: recompute decode of {rh} heads at context {L0}")
+    t0 = time.perf_counter()
+    rec = oracle.decode_recompute(si.to_f64(qh, w.dtype), ck[0:1, :rh, :L0], cv[0:1, :rh, :L0], w.scale)
+    t_rec = time.perf_counter() - t0
+    ref = oracle.decode_cached(qf[0:1, :rh], ck[0:1, :rh, :L0], cv[0:1, :rh, :L0], [L0], w.scale)
+    if not np.array_equal(rec, ref):
+        raise RuntimeError("cached and recompute oracles disagree")
+    recompute_us_per_seq_head = t_rec / rh * 1e6
+    cached_one = []
+    for _ in range(20):
+        t0 = time.perf_counter()
+        oracle.decode_cached(qf[0:1, :rh], ck[0:1, :rh, :L0], cv[0:1, :rh, :L0], [L0], w.scale)
+        cached_one.append(time.perf_counter() - t0)
+    cached_one_us = statistics.median(cached_one) / rh * 1e6
     # prefill sample: whole heads of one layer at T = 8192, naive (materialises T x T)
     T = w.extra_prefill_T
     n_heads = 2
@@ -686,12 +786,17 @@ def cpu_baseline():
     t_pre = time.perf_counter() - t0
     pre_flops = 4.0 * n_heads * w.head_dim * T * (T + 1) / 2
     return {
-        "value": round(dec_bytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"decode: layer 0 of the ragged batch-32 workload, first {n_seq} sequences x 32 heads "
+        "value": round(dec_bytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+        "sample": (f"cached decode: layer 0 of the ragged batch-32 workload, first {n_seq} sequences x 32 heads "
                    f"(sum of contexts {int(ctx[:n_seq].sum())}), {reps} repetitions in {t_dec:.1f} s, fp64 NumPy; "
-                   f"prefill: {n_heads} of 32 heads of one layer at T={T}, naive fp64 in {t_pre:.1f} s"),
+                   f"recompute decode: sequence 0 (context {L0}), {rh} heads, every history row recomputed, "
+                   f"{t_rec:.1f} s; prefill: {n_heads} of 32 heads of one layer at T={T}, naive fp64 in {t_pre:.1f} s"),
+        "cpu_model": cpu_model(), "blas": blas, "blas_threads": blas_threads,
         "prefill": {"value": round(pre_flops / t_pre / 1e12, 6), "unit": "TFLOP/s"},
-        "host_cores_affinity": cores,
+        "decode_cached_us_per_seq_head": round(cached_us_per_seq_head, 2),
+        "recompute_decode": {"context": L0, "us_per_seq_head_step": round(recompute_us_per_seq_head, 1),
+                             "cached_us_per_seq_head_step": round(cached_one_us, 2),
+                             "cache_speedup": round(recompute_us_per_seq_head / cached_one_us, 1)},
     }
 
 
@@ -752,58 +857,98 @@ def main():
         if dec is not None:
             decode_step(dec, td)
 
+    def reset():
+        if pre is not None:
+            reset_prefill(pre)
+        if dec is not None:
+            reset_decode(dec)
+
     # warmup
     for _ in range(args.warmup):
+        reset()
         step(None)
     torch.cuda.synchronize()
-    tp, td = Timer(), Timer()
-    # phase clocks: events at phase boundaries of every step
+    # the timed steps: events at the phase boundaries only (an event pair per
+    # launch would add its own gap between launches); the lengths are reset
+    # between steps, outside the events
     marks = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
+        reset()
         e0 = torch.cuda.Event(enable_timing=True); e0.record()
         if pre is not None:
-            prefill_step(pre, tp)
+            prefill_step(pre)
         e1 = torch.cuda.Event(enable_timing=True); e1.record()
         if dec is not None:
-            decode_step(dec, td)
+            decode_step(dec)
         e2 = torch.cuda.Event(enable_timing=True); e2.record()
         marks.append((e0, e1, e2))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
-    pre_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in marks]))
-    dec_ms = float(np.mean([b.elapsed_time(c) for _, b, c in marks]))
+    # per-launch durations: the same steps again, an event pair around every launch
+    tp, td = Timer(), Timer()
+    for _ in range(args.steps):
+        reset()
+        if pre is not None:
+            prefill_step(pre, tp)
+        if dec is not None:
+            decode_step(dec, td)
+    torch.cuda.synchronize()
+    pre_steps = [a.elapsed_time(b) for a, b, _ in marks]
+    dec_steps = [b.elapsed_time(c) for _, b, c in marks]
+    pre_ms = float(np.median(pre_steps))
+    dec_ms = float(np.median(dec_steps))
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "f16", "data": "synthetic"}
+           "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+           "inputs": ("N(0,1) tensors drawn on the device (seeded torch generator) in HBM before timing, with the "
+                      "shapes, dtype, ragged lengths and 1% x8 heavy K rows of the seeded host recipe the tests "
+                      "and the CPU baseline use (the 64 GiB decode cache is not generated on the host)"),
+           "timing": (f"{args.warmup} warmup steps, then {args.steps} timed steps of 32 layers per phase with HIP "
+                      "events on the library's stream at the phase boundaries (phase and step figures: medians, "
+                      "p10/p90 beside them; ms_per_step is the host wall clock of the timed steps, length resets "
+                      "included), then the same steps again with an event pair around every launch (per-launch "
+                      "medians, p10/p90: the roofline figures)")}
     dec_hash = kernel_source_hash(DECODE_SOURCES)
     pre_hash = kernel_source_hash(PREFILL_SOURCES)
     if dec is not None:
-        k_ms = td.mean_ms()
-        achieved = dec["bytes_kernel"] / (k_ms * 1e-3) / 1e9
+        k_ms = td.median_ms()
+        achieved = dec["bytes_step_layer"] / (k_ms * 1e-3) / 1e9
         out["value"] = round(dec["bytes_step"] / (dec_ms * 1e-3) / 1e9, 2)
         out["unit"] = "GB/s"
         out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "traffic": traffic_from_profiles("decode_ragged_b32", dec_hash),
-                           "kernel": "kvattn_decode (split-K partial + merge) per layer",
-                           "algorithmic_bytes_per_launch": dec["bytes_kernel"],
-                           "mean_launch_ms": round(k_ms, 5)}
-        out["decode"] = {"ms_per_step": round(dec_ms, 4), "us_per_layer": round(dec_ms * 1e3 / w5.layers, 2),
+                           "kernel": "kvattn_append_decode per layer (fused append + split-K decode, and the "
+                                     "merge kernel that commits the lengths)",
+                           "algorithmic_bytes_per_launch": dec["bytes_step_layer"],
+                           "launch_ms": td.spread()}
+        out["decode"] = {"ms_per_step": round(dec_ms, 4),
+                         "ms_per_step_p10_p90": [round(float(np.percentile(dec_steps, 10)), 4),
+                                                 round(float(np.percentile(dec_steps, 90)), 4)],
+                         "us_per_layer": round(dec_ms * 1e3 / w5.layers, 2),
                          "bytes_per_step": dec["bytes_step"], "sum_contexts": int(dec["ctx"].sum())}
     if pre is not None:
-        k_ms = tp.mean_ms()
+        k_ms = tp.median_ms()
         tf = pre["flops_layer"] / (k_ms * 1e-3) / 1e12
         out["prefill"] = {"value": round(pre["flops_layer"] * w5.layers / (pre_ms * 1e-3) / 1e12, 2),
                           "unit": "TFLOP/s", "ms_per_step": round(pre_ms, 4),
+                          "ms_per_step_p10_p90": [round(float(np.percentile(pre_steps, 10)), 4),
+                                                  round(float(np.percentile(pre_steps, 90)), 4)],
                           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                                        "traffic": traffic_from_profiles("prefill_t8192", pre_hash),
                                        "kernel": "prefill_pipe_kernel<f16, D=128> (8 waves x 32 query rows, 64-key tiles, 32x32x16 MFMA)",
                                        "algorithmic_flops_per_launch": pre["flops_layer"],
-                                       "mean_launch_ms": round(k_ms, 5)}}
+                                       "launch_ms": tp.spread()}}
+        out["prefill"].update(prefill_memory_and_clock(kv, pre))
+        clk = out["prefill"]["sustained_clock_ghz"]
+        if clk:
+            # the dense peak scales with the clock (2.5 PFLOP/s at 2.4 GHz)
+            out["prefill"]["roofline"]["frac_of_peak_at_sustained_clock"] = round(
+                tf / (MFMA_F16_PEAK_TFLOPS * clk / 2.4), 4)
         if "value" not in out:
             out["value"], out["unit"] = out["prefill"]["value"], "TFLOP/s"
     out["config"] = {"workload": w5.name, "layers": w5.layers, "q_heads": w5.q_heads, "kv_heads": w5.kv_heads,
@@ -813,10 +958,20 @@ def main():
     out["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                      "cus": props.multi_processor_count}
     if dec is not None and not args.no_extras:
+        log("decode step as two calls (append, then decode)")
+        t2 = Timer()
+        for _ in range(3):
+            decode_step_two_calls(dec)
+        for _ in range(args.steps):
+            decode_step_two_calls(dec, t2)
+        torch.cuda.synchronize()
+        out["decode_two_calls"] = {"decode_launch_ms": t2.spread(),
+                                   "note": "kvattn_decode alone after a separate kvattn_append launch per layer"}
+    if dec is not None and not args.no_extras:
         log("decode under a sliding window")
-        out["decode_window"] = window_measurements(kv, w5, dec, out["roofline"]["mean_launch_ms"] * 1e3)
+        out["decode_window"] = window_measurements(kv, w5, dec, out["roofline"]["launch_ms"]["median_ms"] * 1e3)
         log("decode from a paged cache")
-        out["decode_paged"] = paged_measurements(kv, w5, dec, out["roofline"]["mean_launch_ms"] * 1e3)
+        out["decode_paged"] = paged_measurements(kv, w5, dec, out["roofline"]["launch_ms"]["median_ms"] * 1e3)
     if dec is not None and pre is not None and not args.no_extras:
         log("extend: chunked prefill and 4-token verification")
         out["extend"] = extend_measurements(kv, w5, dec, pre)
@@ -831,15 +986,36 @@ def main():
     if not args.skip_gqa and args.only in (None, "gqa"):
         log("GQA bf16 decode workload (8 GiB cache)")
         g = setup_decode(kv, w4, dev, 4)
-        wall, k_ms = timed(lambda t: decode_step(g, t), args.steps, args.warmup)
-        step_ms = wall / args.steps * 1e3
-        achieved = g["bytes_kernel"] / (k_ms * 1e-3) / 1e9
+        for _ in range(args.warmup):
+            reset_decode(g)
+            decode_step(g)
+        torch.cuda.synchronize()
+        gsteps = []
+        for _ in range(args.steps):
+            reset_decode(g)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            decode_step(g)
+            b.record()
+            gsteps.append((a, b))
+        tg = Timer()
+        for _ in range(args.steps):
+            reset_decode(g)
+            decode_step(g, tg)
+        torch.cuda.synchronize()
+        step_ms = float(np.median([a.elapsed_time(b) for a, b in gsteps]))
+        k_ms = tg.median_ms()
+        achieved = g["bytes_step_layer"] / (k_ms * 1e-3) / 1e9
+        gs = [a.elapsed_time(b) for a, b in gsteps]
         out["decode_gqa"] = {"workload": w4.name, "value": round(g["bytes_step"] / (step_ms * 1e-3) / 1e9, 2),
                              "unit": "GB/s", "ms_per_step": round(step_ms, 4),
+                             "ms_per_step_p10_p90": [round(float(np.percentile(gs, 10)), 4),
+                                                     round(float(np.percentile(gs, 90)), 4)],
                              "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                                           "traffic": traffic_from_profiles("decode_gqa_b16", dec_hash),
-                                          "mean_launch_ms": round(k_ms, 5)}}
+                                          "algorithmic_bytes_per_launch": g["bytes_step_layer"],
+                                          "launch_ms": tg.spread()}}
         g["cache"].close()
         if args.only == "gqa":
             out["value"], out["unit"] = out["decode_gqa"]["value"], "GB/s"

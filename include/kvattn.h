@@ -199,7 +199,7 @@ int kvattn_append_decode(kvattn_cache *c, int layer, const void *k_new, const vo
  * device array of KVATTN_NOALLOC_SCRATCH_BYTES inside the library instead of
  * a cache object's workspace; a shape needs
  * 4 * batch * q_heads * ceil(max_T / split) * (head_dim + 2) bytes of it
- * (split = the decode split size, 384-1024 keys by head dim and group size,
+ * (split = the decode split size, 384-2048 keys by head dim and group size,
  * doubled while max_T / split > 64), and CAPACITY is returned, with the
  * sizes in kvattn_last_error, when that exceeds the array.  The array is
  * shared by every call on a device and keeps the last call's contents:

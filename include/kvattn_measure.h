@@ -15,6 +15,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kvattn.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -61,6 +63,20 @@ int kvattn_measure_exp2(int workgroups, int iters, float *sink, void *stream);
 /* Exponentials of one such launch (0 for a non-positive argument).  Pure host
  * function. */
 double kvattn_measure_exp2_count(int workgroups, int iters);
+
+/* The sustained shader clock of a prefill: kvattn_prefill (same arguments,
+ * same kernels, same result and cache update) with one addition: when the
+ * prompt runs on the pipelined 16-bit kernel, workgroup 0 (the heaviest query
+ * tile, enqueued first) reads the shader-clock counter (s_memtime) and the
+ * 100 MHz real-time counter (s_memrealtime) when it starts and when it ends,
+ * and writes the two differences to sample[0] (shader cycles) and sample[1]
+ * (real-time ticks), a device array of two uint64.  sample[0] / sample[1] *
+ * 0.1 GHz is then the mean shader clock over that workgroup's life, which
+ * spans most of the launch.  Other prompts leave `sample` unwritten.  Returns
+ * what kvattn_prefill returns, or KVATTN_ERR_INVALID_ARG for a null sample. */
+int kvattn_measure_prefill_clock(kvattn_cache *c, int layer, const void *q, const void *k, const void *v,
+                                 void *o, int T, float scale, kvattn_dtype o_dtype, uint64_t *sample,
+                                 void *stream);
 
 #ifdef __cplusplus
 }

@@ -143,6 +143,9 @@ struct PrefillArgs {
   const int32_t *table = nullptr;
   int block_log2 = 0, max_blocks = 0;
   const int32_t *slot_blocks = nullptr;  // paged: blocks assigned to each sequence [B] (device)
+  // measurement aid: when set, workgroup 0 of the pipelined kernel records
+  // the shader-clock and real-time counters at its start and its end
+  uint64_t *clock_sample = nullptr;
 };
 
 struct ExtendCopyArgs {
@@ -192,12 +195,14 @@ constexpr int kMaxSplits = 64;
 // rather than a power of two: with 256- or 512-key splits the concurrently
 // streaming workgroups sit at aligned offsets and the ragged batch-32 decode
 // ran at 4.9 TB/s instead of 6.3 TB/s on MI355X (measured over split sizes
-// 256..576).  Groups of >= 4 query heads per KV head run best with 1024-key
-// splits: fewer, longer streams (GQA 32/8, batch 16 at 4096 keys: 512
-// workgroups, 54.7 -> 52.4 us per layer against 768-key splits; 256 to 1366
-// keys measured).
+// 256..576).  Groups of >= 4 query heads per KV head run best with fewer,
+// longer streams: 2048-key splits with 8-wave workgroups (GQA 32/8, batch
+// 16 at 4096 keys, one decode step of 32 layers: 1.552 ms against 1.573 ms
+// for 1024-key splits of 4 waves; 768, 1088, 1366 and 4096 keys, 4 or 8
+// waves, measured slower, and so was starting each split's stream at a
+// rotated offset).
 inline int decode_chunk(int head_dim, int group, int max_T) {
-  int c = head_dim <= 32 ? 512 : (group >= 4 ? 1024 : 384);
+  int c = head_dim <= 32 ? 512 : (group >= 4 ? 2048 : 384);
   while ((max_T + c - 1) / c > kMaxSplits) c *= 2;
   return c;
 }

@@ -17,6 +17,7 @@
 #include "cache.hpp"
 #include "common.hpp"
 #include "kvattn.h"
+#include "kvattn_measure.h"
 
 using namespace kvattn;
 
@@ -262,8 +263,12 @@ int kvattn_cache_get_lengths(const kvattn_cache *c, int layer, int32_t *host_len
   return KVATTN_OK;
 }
 
-int kvattn_prefill(kvattn_cache *c, int layer, const void *q, const void *k, const void *v,
-                   void *o, int T, float scale, kvattn_dtype o_dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int prefill_impl(kvattn_cache *c, int layer, const void *q, const void *k, const void *v, void *o, int T,
+                 float scale, kvattn_dtype o_dtype, void *stream, uint64_t *clock_sample) {
   int rc = check_layer(c, layer);
   if (rc) return rc;
   if (!q || !k || !v || !o) return KVATTN_ERR_INVALID_ARG;
@@ -298,10 +303,27 @@ int kvattn_prefill(kvattn_cache *c, int layer, const void *q, const void *k, con
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dt = c->dt;
   a.o_dt = o_dtype;
+  a.clock_sample = clock_sample;
   hipError_t e = launch_prefill(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   for (int b = 0; b < c->batch; ++b) c->h_len[(size_t)layer * c->batch + b] = T;
   return KVATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvattn_prefill(kvattn_cache *c, int layer, const void *q, const void *k, const void *v,
+                   void *o, int T, float scale, kvattn_dtype o_dtype, void *stream) {
+  return prefill_impl(c, layer, q, k, v, o, T, scale, o_dtype, stream, nullptr);
+}
+
+int kvattn_measure_prefill_clock(kvattn_cache *c, int layer, const void *q, const void *k, const void *v,
+                                 void *o, int T, float scale, kvattn_dtype o_dtype, uint64_t *sample,
+                                 void *stream) {
+  if (!sample) return KVATTN_ERR_INVALID_ARG;
+  return prefill_impl(c, layer, q, k, v, o, T, scale, o_dtype, stream, sample);
 }
 
 int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, const void *v, void *o,

@@ -443,7 +443,13 @@ struct PipeLds {
   static constexpr int VSTR = BN + 4;  // V^T row stride (elements)
   static constexpr int K_ELEMS = BN * KSTR;
   static constexpr int V_ELEMS = D * VSTR;
-  static constexpr size_t BYTES = (size_t)(2 * K_ELEMS + 2 * V_ELEMS) * 2;
+  static constexpr size_t STAGE_BYTES = (size_t)(2 * K_ELEMS + 2 * V_ELEMS) * 2;
+  // the output rows of the 8 waves (32 each, 16-byte padded) staged at the end
+  static constexpr size_t out_bytes(int esz) { return (size_t)8 * 32 * (D * esz + 16); }
+  static constexpr size_t bytes(int out_esz) {
+    return STAGE_BYTES > out_bytes(out_esz) ? STAGE_BYTES : out_bytes(out_esz);
+  }
+  static constexpr size_t MAX_BYTES = bytes(4);
 };
 
 typedef float float16v_t __attribute__((ext_vector_type(16)));
@@ -458,6 +464,43 @@ template <bool MAX>
 __device__ __forceinline__ float across_h(float x) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return MAX ? fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])) : __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Output of one wave of the pipelined kernel: its O^T accumulators (lane l
+// holds query l % 32, head dims 32 db + 8 g + 4 (l / 32) + i), scaled by
+// `inv` and rounded to OT, are written row-major into the wave's own region
+// of the (idle) LDS, with a 16-byte pad per row, then read back so that each
+// store instruction writes whole rows of D elements: 16-byte pieces of 32
+// different rows had each been written as a separate partial line.
+template <typename OT, int D>
+__device__ __forceinline__ void store_rows_via_lds(unsigned char *smem, int wave, int lane,
+                                                   const float16v_t (&oacc)[D / 32], float inv, OT *o,
+                                                   size_t row0, int valid) {
+  constexpr int DB = D / 32;
+  constexpr int VPC = 16 / (int)sizeof(OT);  // elements per 16-byte chunk
+  constexpr int STR = D + VPC;               // row stride (elements)
+  constexpr int CPR = D / VPC;               // chunks per row
+  constexpr int RPI = 64 / CPR;              // rows per store instruction
+  static_assert(RPI >= 1 && 64 % CPR == 0, "a row must fit one wave's chunks");
+  OT *buf = reinterpret_cast<OT *>(smem) + (size_t)wave * 32 * STR;
+  const int l32 = lane & 31, hh = lane >> 5;
+  typedef OT ot4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      ot4 x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = (OT)(oacc[db][4 * g4 + i] * inv);
+      *(ot4 *)(buf + l32 * STR + db * 32 + 8 * g4 + 4 * hh) = x;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const int r = r0 + lane / CPR;
+    const int c = lane % CPR;
+    if (r < valid) *(u32x4 *)(o + (row0 + r) * D + c * VPC) = *(const u32x4 *)(buf + r * STR + c * VPC);
+  }
 }
 
 template <typename T, int D, int BN>
@@ -485,6 +528,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
   const int G = H / a.kv_heads;
   const int n_qt = (Tn + BM - 1) / BM;
   const int BH = a.batch * H;
+  // heaviest query tiles of all heads first.  (Giving each XCD all query
+  // tiles of one head at a time, so that they share its L2, measured 3.5 %
+  // slower at T = 8192, 32 heads.)
   const int qt = n_qt - 1 - (int)(blockIdx.x / BH);
   const int bh = blockIdx.x % BH;
   const int b = bh / H;
@@ -492,6 +538,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
   const int g = h / G;
   const bool writer = (h - g * G) == 0;
 
+  uint64_t clk0 = 0, rt0 = 0;
+  if (a.clock_sample && blockIdx.x == 0 && threadIdx.x == 0) {
+    clk0 = __builtin_amdgcn_s_memtime();
+    rt0 = __builtin_amdgcn_s_memrealtime();
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -743,17 +794,21 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
     if (j + 1 < n_tiles) step(j + 1, sb, sa);
   }
 
-  // lane holds O^T[d = 32 db + 8 g + 4 hh + i][query = qw0 + l32]
+  // lane holds O^T[d = 32 db + 8 g + 4 hh + i][query = qw0 + l32]; the
+  // loop's last barrier has freed the K/V buffers, which now stage each
+  // wave's rows so that every store writes whole rows
   const float inv = 1.0f / across_h<false>(lrow);
-  const int qr = qw0 + l32;
-  if (qr < Tn) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float4_t x = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
-        store4(a.o, ((size_t)bh * Tn + qr) * D + db * 32 + 8 * g4 + 4 * hh, x, inv, a.o_dt);
-      }
+  const size_t orow0 = (size_t)bh * Tn + qw0;
+  const int valid = Tn - qw0;
+  if (a.o_dt == KVATTN_F32)
+    store_rows_via_lds<float, D>(smem_raw, wave, lane, oacc, inv, (float *)a.o, orow0, valid);
+  else
+    store_rows_via_lds<T, D>(smem_raw, wave, lane, oacc, inv, (T *)a.o, orow0, valid);
+  if (a.clock_sample && blockIdx.x == 0 && tid == 0) {
+    const uint64_t clk1 = __builtin_amdgcn_s_memtime();
+    const uint64_t rt1 = __builtin_amdgcn_s_memrealtime();
+    a.clock_sample[0] = clk1 - clk0;
+    a.clock_sample[1] = rt1 - rt0;
   }
 }
 
@@ -969,17 +1024,18 @@ struct PrefillConfig {
 };
 
 // Launch with `lds` bytes of dynamic LDS.  The kernel's maximum dynamic LDS
-// attribute is set once per device (bit d of `attr_done`; always for device
-// ids past 63).
+// attribute (`lds_max`, or `lds` when 0) is set once per device (bit d of
+// `attr_done`; always for device ids past 63).
 template <typename KernelT>
 static hipError_t launch_with_lds(KernelT kern, dim3 grid, int threads, size_t lds, hipStream_t s,
-                                  std::atomic<uint64_t> &attr_done, const PrefillArgs &a) {
+                                  std::atomic<uint64_t> &attr_done, const PrefillArgs &a, size_t lds_max = 0) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
   if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(lds_max ? lds_max : lds));
     if (e != hipSuccess) return e;
     attr_done.fetch_or(bit, std::memory_order_release);
   }
@@ -1001,8 +1057,9 @@ static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
     // the plain kernel takes the window mask, and prompts whose K/V slab does
     // not fit the 32-bit range of the pipelined kernel's buffer loads
     if (a.window > 0 || (size_t)a.T * D * sizeof(T) >= ((size_t)1 << 31)) return launch_extend_mfma<T, D>(a, s);
-    return launch_with_lds(prefill_pipe_kernel<T, D, C::BN>, grid, C::NW * 64, PipeLds<D, C::BN>::BYTES, s,
-                           attr_done, a);
+    return launch_with_lds(prefill_pipe_kernel<T, D, C::BN>, grid, C::NW * 64,
+                           PipeLds<D, C::BN>::bytes(a.o_dt == KVATTN_F32 ? 4 : 2), s, attr_done, a,
+                           PipeLds<D, C::BN>::MAX_BYTES);
   } else {
     return launch_with_lds(prefill_mfma_kernel<T, D, C::QW, C::BN, C::NW>, grid, C::NW * 64,
                            PrefillLds<D, C::BN>::BYTES, s, attr_done, a);
@@ -1030,8 +1087,9 @@ static hipError_t launch_extend_mfma(const PrefillArgs &a, hipStream_t s) {
       constexpr int PBM = C::NW * C::QW;
       const dim3 pgrid((unsigned)((a.T + PBM - 1) / PBM) * a.batch * a.q_heads);
       static std::atomic<uint64_t> attr_pipe{0};
-      return launch_with_lds(prefill_pipe_kernel<T, D, C::BN>, pgrid, C::NW * 64, PipeLds<D, C::BN>::BYTES, s,
-                             attr_pipe, a);
+      return launch_with_lds(prefill_pipe_kernel<T, D, C::BN>, pgrid, C::NW * 64,
+                             PipeLds<D, C::BN>::bytes(a.o_dt == KVATTN_F32 ? 4 : 2), s, attr_pipe, a,
+                             PipeLds<D, C::BN>::MAX_BYTES);
     }
   }
   constexpr int NW = 4, QW = 32, BN = D == 32 ? 128 : 64, BM = NW * QW;

@@ -256,7 +256,7 @@ def test_noalloc_decode_validates_on_the_host():
     the sizes in the error text."""
     lib = kv.lib()
     p = 0x1000  # never dereferenced: every case is rejected on the host
-    # B = 1024, H = 32, D = 128, 4096 keys in 4 splits of 1024: 4*1024*32*4*130 B = 68 MB > 16 MiB
+    # B = 1024, H = 32, D = 128, 4096 keys in 2 splits of 2048: 4*1024*32*2*130 B = 34 MB > 16 MiB
     assert lib.kvattn_decode_noalloc(p, p, p, 1024, 32, 8, 128, 4096, 1, p, p, 0.125, 1, None) == -3
     assert b"scratch" in lib.kvattn_last_error()
     assert kv.NOALLOC_SCRATCH_BYTES == 16 << 20

@@ -25,8 +25,9 @@ def _rand(shape, dtype, seed):
 
 @pytest.mark.parametrize("dtype,D", [("f16", 128), ("bf16", 64)])
 def test_decode_at_131072_keys(dtype, D):
-    """Capacity 131072: the split size doubles to 2048 so that a full sequence
-    has 64 splits (the split cap).  One sequence exactly full, one not."""
+    """Capacity 131072: the split size is 2048 (grown from the head dim's
+    default until a full sequence has at most 64 splits, the cap), so a full
+    sequence has 64 splits.  One sequence exactly full, one not."""
     kv = _kv()
     B, H, Hkv, max_T = 2, 8, 2, 131072
     lens = [max_T, 65537]

@@ -72,7 +72,7 @@ def test_noalloc_decode_matches_decode_twice_second_smaller():
 
 def test_noalloc_decode_rejects_a_shape_beyond_its_array():
     import kv_cached_causal_amd as kv
-    # 4 * B * H * splits * (D + 2) bytes: B = 1024, H = 32, D = 128, 4096 keys in 4 splits: 68 MB > 16 MiB
+    # 4 * B * H * splits * (D + 2) bytes: B = 1024, H = 32, D = 128, 4096 keys in 2 splits: 34 MB > 16 MiB
     B, H, Hkv, D, max_T = 1024, 32, 8, 128, 4096
     lib = kv.lib()
     dummy = torch.zeros(16, dtype=torch.float16, device="cuda")
