@@ -22,6 +22,8 @@ struct kvattn_cache {
   std::vector<int> window, sink;  // per layer: sliding window (0: none), sink positions
   float *d_ws;            // decode split-K workspace (device)
   int32_t *d_cnt;         // fused decode step: [B][kStepSlots] (counter, attended count)
+  float *d_pws;           // prefill split workspace (null when no prompt up to max_T splits)
+  int32_t *d_pcnt;        // prefill split counters, zero between calls
   int chunk, n_splits;
   int device;
 };

@@ -72,6 +72,37 @@ struct DecodeArgs {
 // ints per sequence of the fused decode step's device record (counter, count)
 constexpr int kStepSlots = 2;
 
+// Prompts whose per-sequence grid (query tiles x heads) fills between half
+// a round and one round of the pipelined prefill kernel (128 to 256
+// workgroups, one per CU) split their heavier half of query tiles in two
+// (see PrefillArgs): the heaviest tile then no longer sets the time of the
+// round.  A function of T and H only, so that a sequence's result does not
+// depend on the batch it is in.  Measured on MI355X: 16 heads of D = 32 at
+// T = 4096 (256 tiles) 62.5 -> 50.5 us; a batch of 4 sequences of 12 heads
+// of D = 64 at T = 2048 (96 tiles each, 1.5 rounds together) 57 -> 68 us
+// when split, so grids under half a round stay whole.
+constexpr int kMaxPrefillQt = 64;                       // query tiles of 256 rows
+constexpr int kMaxPrefillItems = kMaxPrefillQt * 3 / 2;
+inline int prefill_split_tiles(int T, int q_heads) {
+  const int n_qt = (T + 255) / 256;
+  if (n_qt < 8 || n_qt > kMaxPrefillQt || n_qt * q_heads < 128 || n_qt * q_heads > 256) return 0;
+  return n_qt / 2;
+}
+// floats of one half's partial state (8 waves x 64 lanes x (m, l and the
+// lane's D / 2 accumulator elements))
+constexpr size_t prefill_split_half_floats(int head_dim) { return (size_t)8 * 64 * (2 + head_dim / 2); }
+// the most query tiles split for any prompt of up to max_T positions (the
+// split workspace and counters are sized for it)
+inline int prefill_split_tiles_max(int max_T, int q_heads) {
+  int best = 0;
+  const int top = max_T < kMaxPrefillQt * 256 ? max_T : kMaxPrefillQt * 256;
+  for (int T = 256; T < top + 256; T += 256) {
+    const int n = prefill_split_tiles(T < top ? T : top, q_heads);
+    best = n > best ? n : best;
+  }
+  return best;
+}
+
 // the longest extend served by the decode kernels (its workspace is sized
 // for this many query positions per head)
 constexpr int kMaxVerifyTokens = 8;
@@ -146,6 +177,15 @@ struct PrefillArgs {
   // measurement aid: when set, workgroup 0 of the pipelined kernel records
   // the shader-clock and real-time counters at its start and its end
   uint64_t *clock_sample = nullptr;
+  // split query tiles (pipelined kernel, prompts): the n_split heaviest query
+  // tiles run as two workgroups each, over the first and the second half of
+  // their key tiles, and the second to finish merges the two partial
+  // results.  Workgroup i takes item i / (B * H) of the table (query tile,
+  // part: 0 whole, 1 first half, 2 second half), heaviest items first.
+  int n_split = 0, n_items = 0;
+  uint8_t item_qt[kMaxPrefillItems], item_part[kMaxPrefillItems];
+  float *split_ws = nullptr;     // [n_split][B * H][2 halves][prefill_split_half_floats(D)]
+  int32_t *split_cnt = nullptr;  // [n_split][B * H], zero between calls
 };
 
 struct ExtendCopyArgs {
@@ -180,6 +220,9 @@ hipError_t launch_set_lengths(int32_t *dst, int layers, int batch, const int32_t
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+// whether prompts of this dtype and head dim run on the pipelined kernel,
+// which can split heavy query tiles (and needs the split workspace)
+bool prefill_uses_split(kvattn_dtype dt, int head_dim);
 hipError_t launch_extend_attention(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_extend_copy(const ExtendCopyArgs &a, hipStream_t s);
 hipError_t launch_add_lengths(int32_t *len, int batch, int T, int max_T, const int32_t *slot_blocks,

@@ -171,11 +171,19 @@ int kvattn_cache_alloc(kvattn_cache **out, int layers, int batch, int q_heads, i
   // kernels (up to kMaxVerifyTokens query positions per head)
   const size_t ws_bytes = sizeof(float) * (size_t)batch * q_heads * kMaxVerifyTokens * c->n_splits * (head_dim + 2);
   const size_t cnt_bytes = sizeof(int32_t) * (size_t)batch * kStepSlots;
+  // prefill split of heavy query tiles: partials and counters for the
+  // largest split any prompt up to max_T takes
+  const int split_max = prefill_uses_split(dt, head_dim) ? prefill_split_tiles_max(max_T, q_heads) : 0;
+  const size_t pws_bytes = sizeof(float) * (size_t)split_max * batch * q_heads * 2 * prefill_split_half_floats(head_dim);
+  const size_t pcnt_bytes = sizeof(int32_t) * (size_t)split_max * batch * q_heads;
   e = hipMalloc((void **)&c->d_len, len_bytes);
   if (e == hipSuccess) e = hipMalloc((void **)&c->d_ws, ws_bytes);
   if (e == hipSuccess) e = hipMalloc((void **)&c->d_cnt, cnt_bytes);
+  if (e == hipSuccess && split_max) e = hipMalloc((void **)&c->d_pws, pws_bytes);
+  if (e == hipSuccess && split_max) e = hipMalloc((void **)&c->d_pcnt, pcnt_bytes);
   if (e == hipSuccess) e = hipMemset(c->d_len, 0, len_bytes);
   if (e == hipSuccess) e = hipMemset(c->d_cnt, 0, cnt_bytes);
+  if (e == hipSuccess && split_max) e = hipMemset(c->d_pcnt, 0, pcnt_bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     int rc = hip_fail(e, "cache side buffers");
@@ -183,6 +191,8 @@ int kvattn_cache_alloc(kvattn_cache **out, int layers, int batch, int q_heads, i
     if (c->d_len) (void)hipFree(c->d_len);
     if (c->d_ws) (void)hipFree(c->d_ws);
     if (c->d_cnt) (void)hipFree(c->d_cnt);
+    if (c->d_pws) (void)hipFree(c->d_pws);
+    if (c->d_pcnt) (void)hipFree(c->d_pcnt);
     if (c->owns_base) (void)hipFree(c->base);
     delete c;
     return e == hipErrorOutOfMemory ? KVATTN_ERR_OOM : rc;
@@ -197,12 +207,16 @@ int kvattn_cache_free(kvattn_cache *c) {
   hipError_t e1 = hipFree(c->d_len);
   hipError_t e2 = hipFree(c->d_ws);
   hipError_t e4 = hipFree(c->d_cnt);
+  hipError_t e5 = c->d_pws ? hipFree(c->d_pws) : hipSuccess;
+  hipError_t e6 = c->d_pcnt ? hipFree(c->d_pcnt) : hipSuccess;
   hipError_t e3 = c->owns_base ? hipFree(c->base) : hipSuccess;
   delete c;
   if (e != hipSuccess) return hip_fail(e, "kvattn_cache_free sync");
   if (e1 != hipSuccess) return hip_fail(e1, "hipFree(lengths)");
   if (e2 != hipSuccess) return hip_fail(e2, "hipFree(workspace)");
   if (e4 != hipSuccess) return hip_fail(e4, "hipFree(split counters)");
+  if (e5 != hipSuccess) return hip_fail(e5, "hipFree(prefill split workspace)");
+  if (e6 != hipSuccess) return hip_fail(e6, "hipFree(prefill split counters)");
   if (e3 != hipSuccess) return hip_fail(e3, "hipFree(payload)");
   return KVATTN_OK;
 }
@@ -304,6 +318,8 @@ int prefill_impl(kvattn_cache *c, int layer, const void *q, const void *k, const
   a.dt = c->dt;
   a.o_dt = o_dtype;
   a.clock_sample = clock_sample;
+  a.split_ws = c->d_pws;
+  a.split_cnt = c->d_pcnt;
   hipError_t e = launch_prefill(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   for (int b = 0; b < c->batch; ++b) c->h_len[(size_t)layer * c->batch + b] = T;

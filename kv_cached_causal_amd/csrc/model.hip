@@ -644,6 +644,8 @@ int kvattn_model_prefill(kvattn_model *m, const int32_t *tokens, int T, float *l
     a.scale_log2 = (float)(1.0 / std::sqrt((double)D)) * 1.4426950408889634f;
     a.dt = KVATTN_F16;
     a.o_dt = KVATTN_F16;
+    a.split_ws = c->d_pws;
+    a.split_cnt = c->d_pcnt;
     e = launch_prefill(a, s);
     if (e != hipSuccess) break;
     merge_heads_kernel<<<dim3((unsigned)R, (d + 255) / 256), 256, 0, s>>>(m->po, m->pflat, T, H, D);

@@ -25,6 +25,7 @@
 // store that K/V tile into the cache from the registers it was loaded into.
 //
 // F32 takes a plain vector-ALU kernel (four lanes per query row).
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -503,7 +504,10 @@ __device__ __forceinline__ void store_rows_via_lds(unsigned char *smem, int wave
   }
 }
 
-template <typename T, int D, int BN>
+// SPLIT: the grid runs the item table of a prompt whose heavier query tiles
+// are split (a separate instance, so that other prompts keep the registers
+// of the plain schedule).
+template <typename T, int D, int BN, bool SPLIT = false>
 __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
   typedef typename Mfma<T>::vec vec8;
   constexpr bool SPL = Mfma<T>::kSplitP;
@@ -528,10 +532,13 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
   const int G = H / a.kv_heads;
   const int n_qt = (Tn + BM - 1) / BM;
   const int BH = a.batch * H;
-  // heaviest query tiles of all heads first.  (Giving each XCD all query
-  // tiles of one head at a time, so that they share its L2, measured 3.5 %
-  // slower at T = 8192, 32 heads.)
-  const int qt = n_qt - 1 - (int)(blockIdx.x / BH);
+  // heaviest query tiles of all heads first (from the item table when heavy
+  // tiles are split).  (Giving each XCD all query tiles of one head at a
+  // time, so that they share its L2, measured 3.5 % slower at T = 8192, 32
+  // heads.)
+  const int item = (int)(blockIdx.x / BH);
+  const int qt = SPLIT ? (int)a.item_qt[item] : n_qt - 1 - item;
+  const int part = SPLIT ? (int)a.item_part[item] : 0;
   const int bh = blockIdx.x % BH;
   const int b = bh / H;
   const int h = bh - b * H;
@@ -583,6 +590,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
 
   const int kv_end = off + min(q0 + BM, Tn);
   const int n_tiles = (kv_end + BN - 1) / BN;
+  // key tiles [t0, t1) of this workgroup: all, or one half of a split tile
+  // (the first half lies below every query row of the tile, so only the
+  // second holds diagonal tiles)
+  const int t0 = part == 2 ? n_tiles / 2 : 0;
+  const int t1 = part == 1 ? n_tiles / 2 : n_tiles;
 
   u32x4 sreg[4];
   const int v_kg = stid % (BN / 4);
@@ -735,23 +747,24 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
     }
   };
 
-  load_k(0);
-  load_v(0);
-  store_k(0, 0);
-  store_v(0, 0);
-  if (n_tiles > 1) {
-    load_k(1);
-    store_k(1, 1);
+  // LDS slot of key tile t: its parity counted from t0
+  load_k(t0);
+  load_v(t0);
+  store_k(t0, 0);
+  store_v(t0, 0);
+  if (t0 + 1 < t1) {
+    load_k(t0 + 1);
+    store_k(t0 + 1, 1);
   }
   __syncthreads();
 
   float16v_t sa[KB], sb[KB];
   scores(0, sa);
-  if (dlo == 0) mask(0, sa);
+  if (t0 >= dlo && t0 <= dhi) mask(t0, sa);
 
   auto step = [&](int j, float16v_t (&cur)[KB], float16v_t (&nxt)[KB]) {
-    if (j + 2 < n_tiles) load_k(j + 2);
-    if (j + 1 < n_tiles) load_v(j + 1);
+    if (j + 2 < t1) load_k(j + 2);
+    if (j + 1 < t1) load_v(j + 1);
     __builtin_amdgcn_sched_barrier(0);
     if (j <= dhi) {
       vec8 pb[PS];
@@ -759,7 +772,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
       float al;
       __builtin_amdgcn_s_setprio(2);
       const bool any_resc = stats(cur, al);
-      scores((j + 1) & 1, nxt);
+      scores((j + 1 - t0) & 1, nxt);
       expo(cur, pb, pl, al);
       {
         constexpr int NMF = KB * KS;
@@ -777,7 +790,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] *= al;
       }
-      pv(j & 1, pb, pl);
+      pv((j - t0) & 1, pb, pl);
       if (j + 1 >= dlo && j + 1 <= dhi) {
         int t = j + 1;
         asm volatile("" : "+v"(t));
@@ -785,19 +798,76 @@ __global__ __launch_bounds__(512, 1) void prefill_pipe_kernel(PrefillArgs a) {
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    if (j + 2 < n_tiles) store_k(j + 2, j & 1);
-    if (j + 1 < n_tiles) store_v(j + 1, (j + 1) & 1);
+    if (j + 2 < t1) store_k(j + 2, (j - t0) & 1);
+    if (j + 1 < t1) store_v(j + 1, (j + 1 - t0) & 1);
     __syncthreads();
   };
-  for (int j = 0; j < n_tiles; j += 2) {
+  for (int j = t0; j < t1; j += 2) {
     step(j, sa, sb);
-    if (j + 1 < n_tiles) step(j + 1, sb, sa);
+    if (j + 1 < t1) step(j + 1, sb, sa);
   }
 
-  // lane holds O^T[d = 32 db + 8 g + 4 hh + i][query = qw0 + l32]; the
-  // loop's last barrier has freed the K/V buffers, which now stage each
+  // lane holds O^T[d = 32 db + 8 g + 4 hh + i][query = qw0 + l32]
+  float lsum = across_h<false>(lrow);
+  if (SPLIT && part != 0) {
+    // one half of a split tile: publish this half's (m, l, O) rows, count it
+    // in, and let the second half to finish merge the two.  The L2 is per
+    // XCD, so the partials are written with device-scope stores (written
+    // through to the level every XCD shares) and read back with device-scope
+    // loads; each thread waits for its stores before the barrier after
+    // which the half is counted (a device-scope atomic).
+    const int si = qt - (n_qt - a.n_split);
+    const size_t pair = (size_t)si * BH + bh;
+    // each half's partial: per wave, NVAL values per lane (m, l, then the
+    // lane's 16 DB accumulator elements), stored value-major so that a wave
+    // writes (and the merging workgroup, whose lanes hold the same rows and
+    // head dims, reads) 256 contiguous bytes per instruction
+    constexpr int NVAL = 2 + 16 * DB;
+    static_assert((size_t)NW * 64 * NVAL == prefill_split_half_floats(D), "workspace layout");
+    float *mine = a.split_ws + ((pair * 2 + (part - 1)) * NW + wave) * NVAL * 64 + lane;
+    const float *other = a.split_ws + ((pair * 2 + (2 - part)) * NW + wave) * NVAL * 64 + lane;
+    __hip_atomic_store(mine, mrow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(mine + 64, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int k4 = 0; k4 < 16; ++k4)
+        __hip_atomic_store(mine + (2 + db * 16 + k4) * 64, oacc[db][k4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    __shared__ int s_last;
+    if (tid == 0) {
+      int32_t *cnt = a.split_cnt + pair;
+      const int last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1;
+      if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // both halves hold a finite reference point (every wave visits at least
+    // one key tile in each).  The two are combined in a fixed order, first
+    // half then second, whichever finished last, so that the result does
+    // not depend on the order the halves finished in.
+    const bool first = part == 1;
+    const float mo = __hip_atomic_load(other, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float lo = __hip_atomic_load(other + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float m1 = first ? mrow : mo, m2 = first ? mo : mrow;
+    const float l1 = first ? lsum : lo, l2 = first ? lo : lsum;
+    const float mn = fmaxf(m1, m2);
+    const float a1 = fast_exp2(m1 - mn), a2 = fast_exp2(m2 - mn);
+    lsum = fmaf(l1, a1, l2 * a2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int k4 = 0; k4 < 16; ++k4) {
+        const float uo = __hip_atomic_load(other + (2 + db * 16 + k4) * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float u1 = first ? oacc[db][k4] : uo, u2 = first ? uo : oacc[db][k4];
+        oacc[db][k4] = fmaf(u1, a1, u2 * a2);
+      }
+  }
+  // the loop's last barrier has freed the K/V buffers, which now stage each
   // wave's rows so that every store writes whole rows
-  const float inv = 1.0f / across_h<false>(lrow);
+  const float inv = 1.0f / lsum;
   const size_t orow0 = (size_t)bh * Tn + qw0;
   const int valid = Tn - qw0;
   if (a.o_dt == KVATTN_F32)
@@ -1046,24 +1116,70 @@ static hipError_t launch_with_lds(KernelT kern, dim3 grid, int threads, size_t l
 template <typename T, int D>
 static hipError_t launch_extend_mfma(const PrefillArgs &a, hipStream_t s);
 
+// The pipelined kernel's items for a prompt whose heavier query tiles are
+// split (prefill_split_tiles): every query tile whole, except the n_split
+// heaviest, each as its first and second half of key tiles; ordered by
+// their key-tile counts, largest first (ties: later query tile first).
+// Returns the item count (0: no split).
+static int plan_split(PrefillArgs &a, int BM, int BN) {
+  a.n_items = 0;
+  a.n_split = 0;
+  if (!a.split_ws || !a.split_cnt || a.offsets || a.window > 0) return 0;
+  const int ns = prefill_split_tiles(a.T, a.q_heads);
+  if (ns == 0) return 0;
+  const int n_qt = (a.T + BM - 1) / BM;
+  int size[kMaxPrefillItems], n = 0;
+  for (int qt = n_qt - 1; qt >= 0; --qt) {
+    const int nt = (min((qt + 1) * BM, a.T) + BN - 1) / BN;
+    if (qt >= n_qt - ns) {
+      a.item_qt[n] = (uint8_t)qt, a.item_part[n] = 2, size[n++] = nt - nt / 2;
+      a.item_qt[n] = (uint8_t)qt, a.item_part[n] = 1, size[n++] = nt / 2;
+    } else {
+      a.item_qt[n] = (uint8_t)qt, a.item_part[n] = 0, size[n++] = nt;
+    }
+  }
+  // insertion sort, stable: equal sizes keep the later query tile first
+  for (int i = 1; i < n; ++i)
+    for (int j = i; j > 0 && size[j] > size[j - 1]; --j) {
+      std::swap(size[j], size[j - 1]);
+      std::swap(a.item_qt[j], a.item_qt[j - 1]);
+      std::swap(a.item_part[j], a.item_part[j - 1]);
+    }
+  a.n_split = ns;
+  a.n_items = n;
+  return n;
+}
+
 template <typename T, int D>
-static hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
+static hipError_t launch_mfma(const PrefillArgs &a_in, hipStream_t s) {
   typedef PrefillConfig<T, D> C;
   constexpr int BM = C::NW * C::QW;
-  const int n_qt = (a.T + BM - 1) / BM;
-  const dim3 grid((unsigned)n_qt * a.batch * a.q_heads);
+  const int n_qt = (a_in.T + BM - 1) / BM;
+  const dim3 grid((unsigned)n_qt * a_in.batch * a_in.q_heads);
   static std::atomic<uint64_t> attr_done{0};
   if constexpr (C::kPipe) {
     // the plain kernel takes the window mask, and prompts whose K/V slab does
     // not fit the 32-bit range of the pipelined kernel's buffer loads
-    if (a.window > 0 || (size_t)a.T * D * sizeof(T) >= ((size_t)1 << 31)) return launch_extend_mfma<T, D>(a, s);
+    if (a_in.window > 0 || (size_t)a_in.T * D * sizeof(T) >= ((size_t)1 << 31)) return launch_extend_mfma<T, D>(a_in, s);
+    PrefillArgs a = a_in;
+    const int items = plan_split(a, BM, C::BN);
+    if (items) {
+      static std::atomic<uint64_t> attr_split{0};
+      return launch_with_lds(prefill_pipe_kernel<T, D, C::BN, true>, dim3((unsigned)items * a.batch * a.q_heads),
+                             C::NW * 64, PipeLds<D, C::BN>::bytes(a.o_dt == KVATTN_F32 ? 4 : 2), s, attr_split, a,
+                             PipeLds<D, C::BN>::MAX_BYTES);
+    }
     return launch_with_lds(prefill_pipe_kernel<T, D, C::BN>, grid, C::NW * 64,
                            PipeLds<D, C::BN>::bytes(a.o_dt == KVATTN_F32 ? 4 : 2), s, attr_done, a,
                            PipeLds<D, C::BN>::MAX_BYTES);
   } else {
     return launch_with_lds(prefill_mfma_kernel<T, D, C::QW, C::BN, C::NW>, grid, C::NW * 64,
-                           PrefillLds<D, C::BN>::BYTES, s, attr_done, a);
+                           PrefillLds<D, C::BN>::BYTES, s, attr_done, a_in);
   }
+}
+
+bool prefill_uses_split(kvattn_dtype dt, int head_dim) {
+  return dt == KVATTN_F16 || (dt == KVATTN_BF16 && head_dim != 32);
 }
 
 template <int D>
