@@ -43,8 +43,7 @@ size_t kvattn_model_weight_elems(int layers, int d_model, int vocab, int max_T, 
  * the caller's packed fp16 weights (device; they must outlive the model).
  * d_model / heads must be 32, 64 or 128 and d_model a multiple of 512, at
  * most 1024 (UNSUPPORTED otherwise).  Allocates the model's KV cache
- * (kvattn_cache_alloc), activation buffers, a rocBLAS handle for the
- * prompt's projections and a stream for generation. */
+ * (kvattn_cache_alloc), activation buffers and a stream for generation. */
 int kvattn_model_create(kvattn_model **out, int layers, int d_model, int heads, int vocab, int max_T,
                         int mlp_mult, int batch, const void *weights);
 
@@ -61,9 +60,9 @@ int kvattn_model_positions(const kvattn_model *m, int32_t *host_pos);
  * Fills every layer's cache (STATE unless the caches are empty; CAPACITY if
  * T > max_T).  Writes the last position's logits (device fp32, batch x
  * vocab; may be NULL) and their argmax (device int32, batch; lowest index on
- * ties).  The projections run as rocBLAS GEMMs with fp16 inputs and fp32
- * accumulation, the attention as kvattn_prefill.  Token ids outside [0,
- * vocab) are clamped into it. */
+ * ties).  The projections run on the library's own matrix-core GEMM (fp16
+ * inputs, fp32 accumulation), the attention as kvattn_prefill.  Token ids
+ * outside [0, vocab) are clamped into it. */
 int kvattn_model_prefill(kvattn_model *m, const int32_t *tokens, int T, float *logits, int32_t *next,
                          void *stream);
 

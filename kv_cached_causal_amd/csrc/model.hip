@@ -14,7 +14,6 @@
 // accumulation; the residual stream stays fp32 through beta = 1 updates); the
 // attention is the library's prefill kernel, which also fills the cache.
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
 
 #include <cmath>
 #include <cstdio>
@@ -261,7 +260,6 @@ struct kvattn_model {
   size_t prompt_rows;
   float *px;
   half_t *ph, *pqkv, *pq, *pk, *pv, *po, *pflat, *pup;
-  rocblas_handle blas;
   hipStream_t gs;  // generation stream, ordered after the caller's by events
   hipEvent_t ev_in, ev_out;
   int device;
@@ -304,16 +302,105 @@ hipError_t launch_gemv(int epi, bool norm, const GemvArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// C (M x N, row-major) = A (M x K, row-major) * W^T, W (N x K, row-major):
-// column-major C^T = W^T(op) * A^T with no copies.  fp16 inputs, fp32
-// accumulation; C fp16, or fp32 with C = beta * C + A W^T.
-rocblas_status gemm_rows(rocblas_handle h, const half_t *A, const half_t *W, void *C, int M, int N, int K,
-                         bool c_f32, float beta) {
-  const float alpha = 1.f;
-  const rocblas_datatype ct = c_f32 ? rocblas_datatype_f32_r : rocblas_datatype_f16_r;
-  return rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &alpha, W,
-                         rocblas_datatype_f16_r, K, A, rocblas_datatype_f16_r, K, &beta, C, ct, N, C, ct, N,
-                         rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+// C (M x N, row-major) = A (M x K, row-major) * W^T, W (N x K, row-major),
+// fp16 inputs, fp32 accumulation; C fp16, or fp32 with C += A W^T
+// (the residual add).  Both operands are contiguous along K, which is what
+// the matrix instruction's operands hold per lane (8 consecutive k of one
+// row of A, and of one row of W = one column of W^T), so tiles are staged
+// row-major.  A workgroup of 4 waves computes a 128 x 128 block of C, each
+// wave 64 x 64 as 2 x 2 v_mfma_f32_32x32x16_f16 blocks; K advances 32 at a
+// time through two LDS buffers, the next step's global loads in flight
+// during this step's matrix work.  N must be a multiple of 128 and K of 32
+// (the model's widths are multiples of 512); rows past M are clamped on load
+// and not stored.
+constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 32;
+constexpr int kGemmStr = kGemmBK + 8;  // LDS row stride (elements): conflict-free 16-byte fragment reads
+typedef float gemm_acc_t __attribute__((ext_vector_type(16)));
+
+template <bool C_F32>
+__global__ __launch_bounds__(256) void gemm_rows_kernel(const half_t *__restrict__ A, const half_t *__restrict__ W,
+                                                        void *C, int M, int N, int K) {
+  __shared__ __align__(16) half_t As[2][kGemmBM * kGemmStr];
+  __shared__ __align__(16) half_t Ws[2][kGemmBN * kGemmStr];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int m0 = blockIdx.y * kGemmBM, n0 = blockIdx.x * kGemmBN;
+  // staging: 512 16-byte chunks of each 128 x 32 tile, two per thread
+  u32x4 ra[2], rw[2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * 256 + tid, r = c >> 2, kc = (c & 3) * 8;
+      const int am = min(m0 + r, M - 1);
+      ra[i] = *(const u32x4 *)(A + (size_t)am * K + k0 + kc);
+      rw[i] = *(const u32x4 *)(W + (size_t)(n0 + r) * K + k0 + kc);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * 256 + tid, r = c >> 2, kc = (c & 3) * 8;
+      *(u32x4 *)(&As[buf][r * kGemmStr + kc]) = ra[i];
+      *(u32x4 *)(&Ws[buf][r * kGemmStr + kc]) = rw[i];
+    }
+  };
+  gemm_acc_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int nk = K / kGemmBK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load((kt + 1) * kGemmBK);
+#pragma unroll
+    for (int ks = 0; ks < kGemmBK / 16; ++ks) {
+      half8_t fa[2], fw[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[i] = *(const half8_t *)(&As[buf][(wm + 32 * i + l32) * kGemmStr + 16 * ks + 8 * hh]);
+        fw[i] = *(const half8_t *)(&Ws[buf][(wn + 32 * i + l32) * kGemmStr + 16 * ks + 8 * hh]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fw[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+  // lane holds C[wm + 32 i + 8 (v / 4) + 4 hh + v % 4][wn + 32 j + l32]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm + 32 * i + 8 * (v / 4) + 4 * hh + v % 4;
+        const int n = n0 + wn + 32 * j + l32;
+        if (m < M) {
+          if constexpr (C_F32)
+            ((float *)C)[(size_t)m * N + n] += acc[i][j][v];
+          else
+            ((half_t *)C)[(size_t)m * N + n] = (half_t)acc[i][j][v];
+        }
+      }
+}
+
+hipError_t gemm_rows(hipStream_t s, const half_t *A, const half_t *W, void *C, int M, int N, int K, bool c_f32) {
+  if (M <= 0 || N % kGemmBN != 0 || K % kGemmBK != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(N / kGemmBN), (unsigned)((M + kGemmBM - 1) / kGemmBM));
+  if (c_f32)
+    gemm_rows_kernel<true><<<grid, 256, 0, s>>>(A, W, C, M, N, K);
+  else
+    gemm_rows_kernel<false><<<grid, 256, 0, s>>>(A, W, C, M, N, K);
+  return hipGetLastError();
 }
 
 template <typename P>
@@ -394,22 +481,8 @@ hipError_t enqueue_step(kvattn_model *m, const int32_t *tokens, float *logits, i
     e = launch_gemv(EPI_QKV, true, g, s);
     if (e != hipSuccess) break;
 
-    AppendArgs ap;
-    ap.k_layer = cache_layer_k(c, l);
-    ap.v_layer = cache_layer_v(c, l);
-    ap.k_new = (const char *)m->k;
-    ap.v_new = (const char *)m->v;
-    ap.len = c->d_len + (size_t)l * B;
-    ap.batch = B;
-    ap.kv_heads = m->heads;
-    ap.max_T = m->max_T;
-    ap.row_bytes = m->D * 2;
-    ap.table = nullptr;
-    ap.block_log2 = 0;
-    ap.max_blocks = 0;
-    e = launch_append(ap, s);
-    if (e != hipSuccess) break;
-
+    // append this position's K/V and attend the layer's cache: one fused
+    // decode step (the merge kernel, with several splits, commits the length)
     DecodeArgs da;
     da.k_layer = cache_layer_k(c, l);
     da.v_layer = cache_layer_v(c, l);
@@ -432,7 +505,13 @@ hipError_t enqueue_step(kvattn_model *m, const int32_t *tokens, float *logits, i
     da.table = nullptr;
     da.block_log2 = 0;
     da.max_blocks = 0;
-    e = launch_decode(da, s);
+    da.k_new = m->k;
+    da.v_new = m->v;
+    da.k_cache_rw = cache_layer_k(c, l);
+    da.v_cache_rw = cache_layer_v(c, l);
+    da.len_rw = c->d_len + (size_t)l * B;
+    da.counters = c->d_cnt;
+    e = launch_decode_step(da, s);
     if (e != hipSuccess) break;
 
     GemvArgs go{};
@@ -562,8 +641,8 @@ int kvattn_model_create(kvattn_model **out, int layers, int d_model, int heads, 
   if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_in, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_out, hipEventDisableTiming);
   if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (e != hipSuccess || rocblas_create_handle(&m->blas) != rocblas_status_success) {
-    int r = e != hipSuccess ? model_hip_fail(e, "model buffers") : KVATTN_ERR_HIP;
+  if (e != hipSuccess) {
+    int r = model_hip_fail(e, "model buffers");
     kvattn_model_free(m);
     return e == hipErrorOutOfMemory ? KVATTN_ERR_OOM : r;
   }
@@ -574,7 +653,6 @@ int kvattn_model_create(kvattn_model **out, int layers, int d_model, int heads, 
 int kvattn_model_free(kvattn_model *m) {
   if (!m) return KVATTN_ERR_INVALID_ARG;
   hipError_t e = hipDeviceSynchronize();
-  if (m->blas) (void)rocblas_destroy_handle(m->blas);
   free_prompt_buffers(m);
   for (void *p : {(void *)m->x, (void *)m->att, (void *)m->hid, (void *)m->logits, (void *)m->q, (void *)m->k,
                   (void *)m->v, (void *)m->tok, (void *)m->gen_out, (void *)m->step_ctr})
@@ -613,14 +691,13 @@ int kvattn_model_prefill(kvattn_model *m, const int32_t *tokens, int T, float *l
   const size_t R = (size_t)B * T;
   hipError_t e = ensure_prompt_buffers(m, R);
   if (e != hipSuccess) return e == hipErrorOutOfMemory ? KVATTN_ERR_OOM : model_hip_fail(e, "prompt buffers");
-  if (rocblas_set_stream(m->blas, s) != rocblas_status_success) return KVATTN_ERR_HIP;
 
   embed_kernel<<<dim3(T, B), 256, 0, s>>>(tokens, nullptr, m->tok_emb, m->pos_emb, m->px, T, d, m->vocab);
   e = hipGetLastError();
   for (int l = 0; l < m->layers && e == hipSuccess; ++l) {
     rmsnorm_rows_kernel<<<dim3((unsigned)R), 256, 0, s>>>(m->px, m->ln1[l], m->ph, d);
-    if (gemm_rows(m->blas, m->ph, m->wqkv[l], m->pqkv, (int)R, 3 * d, d, false, 0.f) != rocblas_status_success)
-      return KVATTN_ERR_HIP;
+    e = gemm_rows(s, m->ph, m->wqkv[l], m->pqkv, (int)R, 3 * d, d, false);
+    if (e != hipSuccess) break;
     split_qkv_kernel<<<dim3((unsigned)R, (3 * d + 255) / 256), 256, 0, s>>>(m->pqkv, m->pq, m->pk, m->pv, T, H, D);
     PrefillArgs a;
     a.q = m->pq;
@@ -649,15 +726,15 @@ int kvattn_model_prefill(kvattn_model *m, const int32_t *tokens, int T, float *l
     e = launch_prefill(a, s);
     if (e != hipSuccess) break;
     merge_heads_kernel<<<dim3((unsigned)R, (d + 255) / 256), 256, 0, s>>>(m->po, m->pflat, T, H, D);
-    if (gemm_rows(m->blas, m->pflat, m->wo[l], m->px, (int)R, d, d, true, 1.f) != rocblas_status_success)
-      return KVATTN_ERR_HIP;
+    e = gemm_rows(s, m->pflat, m->wo[l], m->px, (int)R, d, d, true);
+    if (e != hipSuccess) break;
     rmsnorm_rows_kernel<<<dim3((unsigned)R), 256, 0, s>>>(m->px, m->ln2[l], m->ph, d);
-    if (gemm_rows(m->blas, m->ph, m->wup[l], m->pup, (int)R, m->mlp, d, false, 0.f) != rocblas_status_success)
-      return KVATTN_ERR_HIP;
+    e = gemm_rows(s, m->ph, m->wup[l], m->pup, (int)R, m->mlp, d, false);
+    if (e != hipSuccess) break;
     const size_t n_up = R * (size_t)m->mlp;
     gelu_half_kernel<<<dim3((unsigned)((n_up + 255) / 256)), 256, 0, s>>>(m->pup, n_up);
-    if (gemm_rows(m->blas, m->pup, m->wdown[l], m->px, (int)R, d, m->mlp, true, 1.f) != rocblas_status_success)
-      return KVATTN_ERR_HIP;
+    e = gemm_rows(s, m->pup, m->wdown[l], m->px, (int)R, d, m->mlp, true);
+    if (e != hipSuccess) break;
     e = hipGetLastError();
   }
   if (e == hipSuccess) {

@@ -266,3 +266,13 @@ def test_noalloc_decode_validates_on_the_host():
     assert lib.kvattn_decode_noalloc(p, p, p, 2, 4, 4, 64, 64, 1, p, p, 0.125, 2, None) == -2
     assert lib.kvattn_decode_noalloc(p, p, p, 2, 4, 4, 64, 64, 1, p, p, -1.0, 1, None) == -1
     assert lib.kvattn_decode_noalloc(p, p, p, 0, 4, 4, 64, 64, 1, p, p, 0.125, 1, None) == -1
+
+
+def test_library_links_no_vendor_blas():
+    """Every kernel of the path, the decoder's prompt GEMMs included, is the
+    library's own: libkvattn.so needs no BLAS library."""
+    import subprocess
+    out = subprocess.run(["ldd", kv.LIB_PATH], capture_output=True, text=True).stdout.lower()
+    assert "libamdhip64" in out
+    for vendor in ("rocblas", "hipblas", "hipblaslt", "miopen"):
+        assert vendor not in out, f"libkvattn.so links {vendor}"
