@@ -153,9 +153,14 @@ int kvattn_append(kvattn_cache *c, int layer, const void *k_new, const void *v_n
 int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, const void *v, void *o,
                   int T, float scale, kvattn_dtype o_dtype, void *stream);
 
-/* Decode of one layer: query q[b,h] (B,H,1,D) sits at position len[b]-1 and
- * attends all len[b] cached keys of its KV head (the causal mask aligned to
- * the bottom right); o (B,H,1,D) in o_dtype (cache dtype or F32).  Lengths are
+/* Decode of one layer (inference chapter, section 9.3: decode appends one
+ * position and reads the whole cache; section 9.1: that read of the cached
+ * history makes decode memory-bandwidth bound; roadmap page, project 11: the
+ * new query attends the past keys concatenated with its own, and project 12:
+ * query heads that share a KV head read it once): query q[b,h] (B,H,1,D) sits
+ * at position len[b]-1 and attends all len[b] cached keys of its KV head (the
+ * causal mask aligned to the bottom right); o (B,H,1,D) in o_dtype (cache
+ * dtype or F32).  Lengths are
  * read from device memory, so the call needs no host synchronisation after an
  * append.  STATE if any len[b] == 0.  Long contexts are split across
  * workgroups and merged by log-sum-exp; the split depends only on len[b],

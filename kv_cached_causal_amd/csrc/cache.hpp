@@ -1,8 +1,10 @@
-// The contiguous cache object behind the opaque kvattn_cache handle, shared by
-// the C ABI (kvattn.hip) and the decoder that drives it (model.hip).
+// The cache objects behind the opaque kvattn_cache and kvattn_paged handles,
+// shared by the C ABI (kvattn.hip), its host-side validation (validate.hpp)
+// and the decoder that drives the contiguous cache (model.hip).  Plain host
+// structs: device memory appears only as pointers.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include <vector>
@@ -24,6 +26,29 @@ struct kvattn_cache {
   int32_t *d_cnt;         // fused decode step: [B][kStepSlots] (counter, attended count)
   float *d_pws;           // prefill split workspace (null when no prompt up to max_T splits)
   int32_t *d_pcnt;        // prefill split counters, zero between calls
+  int chunk, n_splits;
+  int device;
+};
+
+// The block-paged cache: one pool allocation laid out
+// [layer][K|V][num_blocks][Hkv][block_size][D]; one block table per slot
+// (device, [slots][max_blocks], the same for every layer); lengths
+// [layer][slots] on the device with a host mirror.
+struct kvattn_paged {
+  int layers, slots, q_heads, kv_heads, head_dim;
+  int num_blocks, block_size, block_log2, max_blocks;
+  kvattn_dtype dt;
+  int elem;
+  size_t payload_bytes, layer_bytes;
+  char *base;
+  bool owns_base;
+  int32_t *d_len;              // [layers][slots]
+  std::vector<int32_t> h_len;  // host mirror
+  int32_t *d_table;            // [slots][max_blocks]
+  int32_t *d_nblk;             // [slots] blocks assigned per slot (device copy of h_nblk)
+  std::vector<int> h_nblk;     // table entries set per slot
+  std::vector<int> window, sink;  // per layer; window 0 = none
+  float *d_ws;
   int chunk, n_splits;
   int device;
 };

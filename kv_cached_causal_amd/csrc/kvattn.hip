@@ -18,6 +18,7 @@
 #include "common.hpp"
 #include "kvattn.h"
 #include "kvattn_measure.h"
+#include "validate.hpp"
 
 using namespace kvattn;
 
@@ -29,25 +30,6 @@ thread_local char g_last_error[256] = "";
 int hip_fail(hipError_t e, const char *where) {
   std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", where, hipGetErrorString(e));
   return KVATTN_ERR_HIP;
-}
-
-int elem_bytes(kvattn_dtype dt) {
-  switch (dt) {
-    case KVATTN_F32: return 4;
-    case KVATTN_F16: return 2;
-    case KVATTN_BF16: return 2;
-  }
-  return 0;
-}
-
-bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
-
-bool valid_out_dtype(const kvattn_cache *c, kvattn_dtype o) { return o == c->dt || o == KVATTN_F32; }
-
-int check_layer(const kvattn_cache *c, int layer) {
-  if (!c) return KVATTN_ERR_INVALID_ARG;
-  if (layer < 0 || layer >= c->layers) return KVATTN_ERR_INVALID_ARG;
-  return KVATTN_OK;
 }
 
 int check_device(const kvattn_cache *c) {
@@ -231,26 +213,22 @@ int kvattn_cache_kv_ptr(const kvattn_cache *c, int layer, void **k, void **v) {
 }
 
 int kvattn_cache_set_lengths(kvattn_cache *c, int layer, const int32_t *host_lens, void *stream) {
-  if (!c || !host_lens) return KVATTN_ERR_INVALID_ARG;
-  if (layer != -1 && (layer < 0 || layer >= c->layers)) return KVATTN_ERR_INVALID_ARG;
-  for (int b = 0; b < c->batch; ++b)
-    if (host_lens[b] < 0 || host_lens[b] > c->max_T) return KVATTN_ERR_CAPACITY;
-  int rc = check_device(c);
+  int rc = validate_set_lengths(c, layer, host_lens);
+  if (rc) return rc;
+  rc = check_device(c);
   if (rc) return rc;
   const int first = layer < 0 ? 0 : layer;
   const int count = layer < 0 ? c->layers : 1;
   hipError_t e = launch_set_lengths(c->d_len + (size_t)first * c->batch, count, c->batch, host_lens,
                                     (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "set_lengths launch");
-  for (int l = first; l < first + count; ++l)
-    std::memcpy(&c->h_len[(size_t)l * c->batch], host_lens, sizeof(int32_t) * c->batch);
+  mirror_copy(c, layer, host_lens);
   return KVATTN_OK;
 }
 
 int kvattn_cache_set_window(kvattn_cache *c, int layer, int window, int sink) {
-  if (!c) return KVATTN_ERR_INVALID_ARG;
-  if (layer != -1 && (layer < 0 || layer >= c->layers)) return KVATTN_ERR_INVALID_ARG;
-  if (window < 0 || sink < 0) return KVATTN_ERR_INVALID_ARG;
+  int rc = validate_set_window(c, layer, window, sink);
+  if (rc) return rc;
   const int first = layer < 0 ? 0 : layer;
   const int count = layer < 0 ? c->layers : 1;
   for (int l = first; l < first + count; ++l) {
@@ -283,15 +261,8 @@ namespace {
 
 int prefill_impl(kvattn_cache *c, int layer, const void *q, const void *k, const void *v, void *o, int T,
                  float scale, kvattn_dtype o_dtype, void *stream, uint64_t *clock_sample) {
-  int rc = check_layer(c, layer);
+  int rc = validate_prefill(c, layer, q, k, v, o, T, scale, o_dtype);
   if (rc) return rc;
-  if (!q || !k || !v || !o) return KVATTN_ERR_INVALID_ARG;
-  if (T <= 0 || !(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
-  if (!valid_out_dtype(c, o_dtype)) return KVATTN_ERR_UNSUPPORTED;
-  if (T > c->max_T) return KVATTN_ERR_CAPACITY;
-  const int32_t *hl = &c->h_len[(size_t)layer * c->batch];
-  for (int b = 0; b < c->batch; ++b)
-    if (hl[b] != 0) return KVATTN_ERR_STATE;
   rc = check_device(c);
   if (rc) return rc;
 
@@ -322,7 +293,7 @@ int prefill_impl(kvattn_cache *c, int layer, const void *q, const void *k, const
   a.split_cnt = c->d_pcnt;
   hipError_t e = launch_prefill(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
-  for (int b = 0; b < c->batch; ++b) c->h_len[(size_t)layer * c->batch + b] = T;
+  mirror_set(c, layer, T);
   return KVATTN_OK;
 }
 
@@ -344,14 +315,8 @@ int kvattn_measure_prefill_clock(kvattn_cache *c, int layer, const void *q, cons
 
 int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, const void *v, void *o,
                   int T, float scale, kvattn_dtype o_dtype, void *stream) {
-  int rc = check_layer(c, layer);
+  int rc = validate_extend(c, layer, q, k, v, o, T, scale, o_dtype);
   if (rc) return rc;
-  if (!q || !k || !v || !o) return KVATTN_ERR_INVALID_ARG;
-  if (T <= 0 || !(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
-  if (!valid_out_dtype(c, o_dtype)) return KVATTN_ERR_UNSUPPORTED;
-  int32_t *hl = &c->h_len[(size_t)layer * c->batch];
-  for (int b = 0; b < c->batch; ++b)
-    if (hl[b] > c->max_T - T) return KVATTN_ERR_CAPACITY;
   rc = check_device(c);
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
@@ -406,7 +371,7 @@ int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, cons
     if (e != hipSuccess) return hip_fail(e, "extend (decode form) launch");
     e = launch_add_lengths(len, c->batch, T, c->max_T, nullptr, 0, st);
     if (e != hipSuccess) return hip_fail(e, "extend length update launch");
-    for (int b = 0; b < c->batch; ++b) hl[b] += T;
+    mirror_add(c, layer, T);
     return KVATTN_OK;
   }
 
@@ -439,17 +404,13 @@ int kvattn_extend(kvattn_cache *c, int layer, const void *q, const void *k, cons
   // 3. commit: len[b] += T
   e = launch_add_lengths(len, c->batch, T, c->max_T, nullptr, 0, st);
   if (e != hipSuccess) return hip_fail(e, "extend length update launch");
-  for (int b = 0; b < c->batch; ++b) hl[b] += T;
+  mirror_add(c, layer, T);
   return KVATTN_OK;
 }
 
 int kvattn_append(kvattn_cache *c, int layer, const void *k_new, const void *v_new, void *stream) {
-  int rc = check_layer(c, layer);
+  int rc = validate_append(c, layer, k_new, v_new);
   if (rc) return rc;
-  if (!k_new || !v_new) return KVATTN_ERR_INVALID_ARG;
-  int32_t *hl = &c->h_len[(size_t)layer * c->batch];
-  for (int b = 0; b < c->batch; ++b)
-    if (hl[b] >= c->max_T) return KVATTN_ERR_CAPACITY;
   rc = check_device(c);
   if (rc) return rc;
   AppendArgs a;
@@ -467,7 +428,7 @@ int kvattn_append(kvattn_cache *c, int layer, const void *k_new, const void *v_n
   a.max_blocks = 0;
   hipError_t e = launch_append(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "append launch");
-  for (int b = 0; b < c->batch; ++b) hl[b] += 1;
+  mirror_add(c, layer, 1);
   return KVATTN_OK;
 }
 
@@ -507,14 +468,8 @@ extern "C" {
 
 int kvattn_append_decode(kvattn_cache *c, int layer, const void *k_new, const void *v_new, const void *q, void *o,
                          float scale, kvattn_dtype o_dtype, void *stream) {
-  int rc = check_layer(c, layer);
+  int rc = validate_append_decode(c, layer, k_new, v_new, q, o, scale, o_dtype);
   if (rc) return rc;
-  if (!k_new || !v_new || !q || !o) return KVATTN_ERR_INVALID_ARG;
-  if (!(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
-  if (!valid_out_dtype(c, o_dtype)) return KVATTN_ERR_UNSUPPORTED;
-  int32_t *hl = &c->h_len[(size_t)layer * c->batch];
-  for (int b = 0; b < c->batch; ++b)
-    if (hl[b] >= c->max_T) return KVATTN_ERR_CAPACITY;
   rc = check_device(c);
   if (rc) return rc;
   DecodeArgs a = cache_decode_args(c, layer, q, o, scale, o_dtype);
@@ -526,20 +481,14 @@ int kvattn_append_decode(kvattn_cache *c, int layer, const void *k_new, const vo
   a.counters = c->d_cnt;
   hipError_t e = launch_decode_step(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode step launch");
-  for (int b = 0; b < c->batch; ++b) hl[b] += 1;
+  mirror_add(c, layer, 1);
   return KVATTN_OK;
 }
 
 int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scale,
                   kvattn_dtype o_dtype, void *stream) {
-  int rc = check_layer(c, layer);
+  int rc = validate_decode(c, layer, q, o, scale, o_dtype);
   if (rc) return rc;
-  if (!q || !o) return KVATTN_ERR_INVALID_ARG;
-  if (!(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
-  if (!valid_out_dtype(c, o_dtype)) return KVATTN_ERR_UNSUPPORTED;
-  const int32_t *hl = &c->h_len[(size_t)layer * c->batch];
-  for (int b = 0; b < c->batch; ++b)
-    if (hl[b] <= 0) return KVATTN_ERR_STATE;
   rc = check_device(c);
   if (rc) return rc;
   DecodeArgs a = cache_decode_args(c, layer, q, o, scale, o_dtype);
@@ -553,7 +502,7 @@ int kvattn_decode_noalloc(const void *k_cache, const void *v_cache, const int32_
                           void *o, float scale, kvattn_dtype o_dtype, void *stream) {
   if (!k_cache || !v_cache || !lengths || !q || !o) return KVATTN_ERR_INVALID_ARG;
   if (batch <= 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 || max_T <= 0) return KVATTN_ERR_INVALID_ARG;
-  if (!(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return KVATTN_ERR_INVALID_ARG;
   if (elem_bytes(dt) == 0 || !supported_dim(head_dim) || q_heads % kv_heads != 0) return KVATTN_ERR_UNSUPPORTED;
   if (o_dtype != dt && o_dtype != KVATTN_F32) return KVATTN_ERR_UNSUPPORTED;
   // split-K partials (m, l, u[D]) of every (sequence, query head, split);
@@ -606,31 +555,8 @@ int kvattn_decode_noalloc(const void *k_cache, const void *v_cache, const int32_
 
 }  // extern "C"
 
-struct kvattn_paged {
-  int layers, slots, q_heads, kv_heads, head_dim;
-  int num_blocks, block_size, block_log2, max_blocks;
-  kvattn_dtype dt;
-  int elem;
-  size_t payload_bytes, layer_bytes;
-  char *base;
-  bool owns_base;
-  int32_t *d_len;              // [layers][slots]
-  std::vector<int32_t> h_len;  // host mirror
-  int32_t *d_table;            // [slots][max_blocks]
-  int32_t *d_nblk;             // [slots] blocks assigned per slot (device copy of h_nblk)
-  std::vector<int> h_nblk;     // table entries set per slot
-  std::vector<int> window, sink;  // per layer; window 0 = none
-  float *d_ws;
-  int chunk, n_splits;
-  int device;
-};
 
 namespace {
-
-int paged_check_layer(const kvattn_paged *p, int layer) {
-  if (!p || layer < 0 || layer >= p->layers) return KVATTN_ERR_INVALID_ARG;
-  return KVATTN_OK;
-}
 
 int paged_check_device(const kvattn_paged *p) {
   int dev = -1;
@@ -646,7 +572,6 @@ int paged_check_device(const kvattn_paged *p) {
 
 char *paged_k(const kvattn_paged *p, int layer) { return p->base + (size_t)layer * p->layer_bytes; }
 char *paged_v(const kvattn_paged *p, int layer) { return paged_k(p, layer) + p->layer_bytes / 2; }
-int paged_capacity(const kvattn_paged *p, int slot) { return p->h_nblk[slot] * p->block_size; }
 
 }  // namespace
 
@@ -775,14 +700,9 @@ int kvattn_paged_kv_ptr(const kvattn_paged *p, int layer, void **k, void **v) {
 
 int kvattn_paged_set_blocks(kvattn_paged *p, int slot, const int32_t *host_block_ids, int n_blocks,
                             void *stream) {
-  if (!p || slot < 0 || slot >= p->slots || n_blocks < 0 || n_blocks > p->max_blocks)
-    return KVATTN_ERR_INVALID_ARG;
-  if (n_blocks > 0 && !host_block_ids) return KVATTN_ERR_INVALID_ARG;
-  for (int i = 0; i < n_blocks; ++i)
-    if (host_block_ids[i] < 0 || host_block_ids[i] >= p->num_blocks) return KVATTN_ERR_INVALID_ARG;
-  for (int l = 0; l < p->layers; ++l)
-    if (p->h_len[(size_t)l * p->slots + slot] > n_blocks * p->block_size) return KVATTN_ERR_CAPACITY;
-  int rc = paged_check_device(p);
+  int rc = validate_paged_set_blocks(p, slot, host_block_ids, n_blocks);
+  if (rc) return rc;
+  rc = paged_check_device(p);
   if (rc) return rc;
   if (n_blocks > 0) {
     hipError_t e = launch_set_lengths(p->d_table + (size_t)slot * p->max_blocks, 1, n_blocks, host_block_ids,
@@ -799,11 +719,9 @@ int kvattn_paged_set_blocks(kvattn_paged *p, int slot, const int32_t *host_block
 }
 
 int kvattn_paged_set_lengths(kvattn_paged *p, int layer, const int32_t *host_lens, void *stream) {
-  if (!p || !host_lens) return KVATTN_ERR_INVALID_ARG;
-  if (layer != -1 && (layer < 0 || layer >= p->layers)) return KVATTN_ERR_INVALID_ARG;
-  for (int s = 0; s < p->slots; ++s)
-    if (host_lens[s] < 0 || host_lens[s] > paged_capacity(p, s)) return KVATTN_ERR_CAPACITY;
-  int rc = paged_check_device(p);
+  int rc = validate_paged_set_lengths(p, layer, host_lens);
+  if (rc) return rc;
+  rc = paged_check_device(p);
   if (rc) return rc;
   const int first = layer < 0 ? 0 : layer;
   const int count = layer < 0 ? p->layers : 1;
@@ -849,16 +767,8 @@ int kvattn_paged_get_window(const kvattn_paged *p, int layer, int *window, int *
 
 int kvattn_paged_prefill(kvattn_paged *p, int layer, const void *q, const void *k, const void *v, void *o,
                          int T, float scale, kvattn_dtype o_dtype, void *stream) {
-  int rc = paged_check_layer(p, layer);
+  int rc = validate_paged_prefill(p, layer, q, k, v, o, T, scale, o_dtype);
   if (rc) return rc;
-  if (!q || !k || !v || !o) return KVATTN_ERR_INVALID_ARG;
-  if (T <= 0 || !(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
-  if (o_dtype != p->dt && o_dtype != KVATTN_F32) return KVATTN_ERR_UNSUPPORTED;
-  const int32_t *hl = &p->h_len[(size_t)layer * p->slots];
-  for (int s = 0; s < p->slots; ++s)
-    if (hl[s] != 0) return KVATTN_ERR_STATE;
-  for (int s = 0; s < p->slots; ++s)
-    if (T > paged_capacity(p, s)) return KVATTN_ERR_CAPACITY;
   rc = paged_check_device(p);
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
@@ -907,17 +817,13 @@ int kvattn_paged_prefill(kvattn_paged *p, int layer, const void *q, const void *
   w.slot_blocks = p->d_nblk;
   e = launch_paged_write(w, st);
   if (e != hipSuccess) return hip_fail(e, "paged prefill write launch");
-  for (int s = 0; s < p->slots; ++s) p->h_len[(size_t)layer * p->slots + s] = T;
+  paged_mirror_set(p, layer, T);
   return KVATTN_OK;
 }
 
 int kvattn_paged_append(kvattn_paged *p, int layer, const void *k_new, const void *v_new, void *stream) {
-  int rc = paged_check_layer(p, layer);
+  int rc = validate_paged_append(p, layer, k_new, v_new);
   if (rc) return rc;
-  if (!k_new || !v_new) return KVATTN_ERR_INVALID_ARG;
-  int32_t *hl = &p->h_len[(size_t)layer * p->slots];
-  for (int s = 0; s < p->slots; ++s)
-    if (hl[s] >= paged_capacity(p, s)) return KVATTN_ERR_CAPACITY;
   rc = paged_check_device(p);
   if (rc) return rc;
   AppendArgs a;
@@ -936,20 +842,14 @@ int kvattn_paged_append(kvattn_paged *p, int layer, const void *k_new, const voi
   a.slot_blocks = p->d_nblk;
   hipError_t e = launch_append(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "paged append launch");
-  for (int s = 0; s < p->slots; ++s) hl[s] += 1;
+  paged_mirror_add(p, layer, 1);
   return KVATTN_OK;
 }
 
 int kvattn_paged_extend(kvattn_paged *p, int layer, const void *q, const void *k, const void *v, void *o, int T,
                         float scale, kvattn_dtype o_dtype, void *stream) {
-  int rc = paged_check_layer(p, layer);
+  int rc = validate_paged_extend(p, layer, q, k, v, o, T, scale, o_dtype);
   if (rc) return rc;
-  if (!q || !k || !v || !o) return KVATTN_ERR_INVALID_ARG;
-  if (T <= 0 || !(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
-  if (o_dtype != p->dt && o_dtype != KVATTN_F32) return KVATTN_ERR_UNSUPPORTED;
-  int32_t *hl = &p->h_len[(size_t)layer * p->slots];
-  for (int s = 0; s < p->slots; ++s)
-    if (hl[s] > paged_capacity(p, s) - T) return KVATTN_ERR_CAPACITY;
   rc = paged_check_device(p);
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
@@ -1006,7 +906,7 @@ int kvattn_paged_extend(kvattn_paged *p, int layer, const void *q, const void *k
     if (e != hipSuccess) return hip_fail(e, "paged extend (decode form) launch");
     e = launch_add_lengths(len, p->slots, T, 0, p->d_nblk, p->block_log2, st);
     if (e != hipSuccess) return hip_fail(e, "paged extend length update launch");
-    for (int s = 0; s < p->slots; ++s) hl[s] += T;
+    paged_mirror_add(p, layer, T);
     return KVATTN_OK;
   }
 
@@ -1044,20 +944,14 @@ int kvattn_paged_extend(kvattn_paged *p, int layer, const void *q, const void *k
   // 3. commit: len[b] += T
   e = launch_add_lengths(len, p->slots, T, 0, p->d_nblk, p->block_log2, st);
   if (e != hipSuccess) return hip_fail(e, "paged extend length update launch");
-  for (int s = 0; s < p->slots; ++s) hl[s] += T;
+  paged_mirror_add(p, layer, T);
   return KVATTN_OK;
 }
 
 int kvattn_paged_decode(kvattn_paged *p, int layer, const void *q, void *o, float scale, kvattn_dtype o_dtype,
                         void *stream) {
-  int rc = paged_check_layer(p, layer);
+  int rc = validate_paged_decode(p, layer, q, o, scale, o_dtype);
   if (rc) return rc;
-  if (!q || !o) return KVATTN_ERR_INVALID_ARG;
-  if (!(scale > 0.f) || scale == INFINITY) return KVATTN_ERR_INVALID_ARG;
-  if (o_dtype != p->dt && o_dtype != KVATTN_F32) return KVATTN_ERR_UNSUPPORTED;
-  const int32_t *hl = &p->h_len[(size_t)layer * p->slots];
-  for (int s = 0; s < p->slots; ++s)
-    if (hl[s] <= 0) return KVATTN_ERR_STATE;
   rc = paged_check_device(p);
   if (rc) return rc;
   DecodeArgs a;
