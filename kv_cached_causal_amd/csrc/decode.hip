@@ -479,16 +479,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 }
 
 // query heads per decode workgroup for G query heads per KV head: the
-// largest of 8, 4, 3, 2 that divides G (1 otherwise)
+// largest of 8 .. 1 that divides G.  Each K/V byte is read once for G <= 8
+// and G / group_tile(G) times for larger groups (the G accumulators of a
+// lane would not fit its registers).
 inline int group_tile(int G) {
-  return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 3 == 0) ? 3 : (G % 2 == 0) ? 2 : 1;
+  for (int t = 8; t > 1; --t)
+    if (G % t == 0) return t;
+  return 1;
 }
 
 // threads of the merge kernel: one per output element up to 256, else a
 // block size that divides the GT * D outputs evenly
 template <int D, int GT>
 constexpr int merge_threads() {
-  return GT * D <= 256 ? GT * D : (GT * D % 256 == 0 ? 256 : 128);
+  return GT * D <= 256 ? GT * D
+                       : (GT * D % 256 == 0 ? 256 : GT * D % 128 == 0 ? 128 : GT * D % 64 == 0 ? 64 : 32);
 }
 
 // grid (Hkv * G/GT, B): log-sum-exp merge of the non-empty splits of one
@@ -630,6 +635,9 @@ static hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
   }
   switch (group_tile(G)) {
     case 8: return launch_gt<Tag, D, 8>(a, s);
+    case 7: return launch_gt<Tag, D, 7>(a, s);
+    case 6: return launch_gt<Tag, D, 6>(a, s);
+    case 5: return launch_gt<Tag, D, 5>(a, s);
     case 4: return launch_gt<Tag, D, 4>(a, s);
     case 3: return launch_gt<Tag, D, 3>(a, s);
     case 2: return launch_gt<Tag, D, 2>(a, s);
@@ -641,6 +649,9 @@ template <class Tag, int D>
 static hipError_t launch_step_typed(const DecodeArgs &a, hipStream_t s) {
   switch (group_tile(a.q_heads / a.kv_heads)) {
     case 8: return launch_gt_step<Tag, D, 8>(a, s);
+    case 7: return launch_gt_step<Tag, D, 7>(a, s);
+    case 6: return launch_gt_step<Tag, D, 6>(a, s);
+    case 5: return launch_gt_step<Tag, D, 5>(a, s);
     case 4: return launch_gt_step<Tag, D, 4>(a, s);
     case 3: return launch_gt_step<Tag, D, 3>(a, s);
     case 2: return launch_gt_step<Tag, D, 2>(a, s);

@@ -119,7 +119,8 @@ DECODE_LENS = [1, 7, 256, 257, 700, 1100]
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("D", [32, 64, 128])
-@pytest.mark.parametrize("heads", HEADS + [(8, 1), (12, 4), (6, 2)], ids=lambda x: f"H{x[0]}kv{x[1]}")
+@pytest.mark.parametrize("heads", HEADS + [(8, 1), (12, 4), (6, 2), (10, 2), (12, 2), (14, 2), (16, 1)],
+                         ids=lambda x: f"H{x[0]}kv{x[1]}")
 def test_decode_matches_oracle(dtype, D, heads):
     """Ragged contexts across split boundaries; stale slots poisoned with NaN."""
     kv = _kv()
