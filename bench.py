@@ -56,8 +56,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skip-gqa", action="store_true")
-    p.add_argument("--only", choices=["prefill", "decode", "gqa"], default=None,
-                   help="time one phase only (for profiling runs)")
+    p.add_argument("--only", choices=["prefill", "decode", "gqa", "prefill_d32"], default=None,
+                   help="time one phase only (for profiling runs); prefill_d32: the 8-layer model's D=32 "
+                        "prompts at T=4096 and T=8192")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the windowed, paged and extend measurements (profiling runs: their launches "
                         "share kernel names with the headline ones)")
@@ -89,7 +90,7 @@ CALIB_BYTES = 4 << 30
 TRAFFIC_KERNELS = {
     "decode_ragged_b32": (DECODE_SOURCES, ["decode_kernel<kvattn::TagF16, 128, 1, 6, 1, 4, false, false, true>",
                                            "decode_merge_kernel<128, 1, true>"]),
-    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4, 4, 1, 4, false, false, true>",
+    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4, 4, 1, 8, false, false, true>",
                                         "decode_merge_kernel<128, 4, true>"]),
     "prefill_t8192": (PREFILL_SOURCES, ["prefill_pipe_kernelIDF16_Li128"]),
 }
@@ -205,11 +206,11 @@ def measure_exp_ceiling(kv, dev, workgroups=4096, iters=5000, reps=5):
     return n / (a.elapsed_time(b) / reps * 1e-3)
 
 
-def small_head_prefill(kv, dev, mceil, eceil, reps=20):
-    """The 8-layer x 512-wide model's attention prefill at T=8192 (B=1, 16 heads of D=32, fp16):
+def small_head_prefill(kv, dev, mceil, eceil, reps=20, T=8192):
+    """The 8-layer x 512-wide model's attention prefill at T (B=1, 16 heads of D=32, fp16):
     per-launch time against the MFMA peak and against the exponential ceiling (one exp2 per
     unmasked score: at D=32 a score costs only 128 MFMA flops)."""
-    T, H, D = 8192, 16, 32
+    H, D = 16, 32
     gen = torch.Generator(device=dev)
     gen.manual_seed(32)
     dt = torch.float16
@@ -233,7 +234,7 @@ def small_head_prefill(kv, dev, mceil, eceil, reps=20):
     med = statistics.median(times) * 1e-3
     flops = 4.0 * H * D * T * (T + 1) / 2
     exps = H * T * (T + 1) / 2
-    return {"workload": "T=8192 causal prefill, B=1, H=16, D=32, fp16 (the 8L x 512d model's attention)",
+    return {"workload": f"T={T} causal prefill, B=1, H=16, D=32, fp16 (the 8L x 512d model's attention)",
             "us_per_layer": round(med * 1e6, 1), "value": round(flops / med / 1e12, 1), "unit": "TFLOP/s",
             "frac_of_mfma_peak": round(flops / med / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
             "mfma_bound_us": round(flops / (mceil * 1e12) * 1e6, 1),
@@ -838,6 +839,15 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+    if args.only == "prefill_d32":
+        # the D=32 prompts alone (profiling runs): T=4096 (split query tiles) and T=8192
+        mceil, eceil = MFMA_F16_PEAK_TFLOPS * 0.968, 18.9e12  # nominal, for the bound columns only
+        res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+               "prefill_d32_t4096": small_head_prefill(kv, dev, mceil, eceil, reps=args.steps, T=4096),
+               "prefill_d32": small_head_prefill(kv, dev, mceil, eceil, reps=args.steps, T=8192)}
+        res["value"], res["unit"] = res["prefill_d32"]["value"], "TFLOP/s"
+        print(json.dumps(res), flush=True)
+        return
     w5, w4 = si.WORKLOADS[5], si.WORKLOADS[4]
     res = {}
 
@@ -1042,7 +1052,8 @@ def main():
         eceil = measure_exp_ceiling(kv, dev)
         out["exp2_ceiling"] = {"value": round(eceil / 1e12, 3), "unit": "T exp2/s", "kernel": "kvattn_measure_exp2"}
         if not args.no_extras:
-            log("small-head prefill (T=8192, 16 heads of D=32)")
+            log("small-head prefill (T=4096 and T=8192, 16 heads of D=32)")
+            out["prefill_d32_t4096"] = small_head_prefill(kv, dev, mceil, eceil, T=4096)
             out["prefill_d32"] = small_head_prefill(kv, dev, mceil, eceil)
     if args.only is None and not args.no_extras:
         log("small workloads (configs 1-3), whole")
