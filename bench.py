@@ -63,7 +63,7 @@ def parse():
                    help="skip the windowed, paged and extend measurements (profiling runs: their launches "
                         "share kernel names with the headline ones)")
     p.add_argument("--calibrate", action="store_true",
-                   help="also run a plain 4 GiB read and a 4 GiB fill, whose FETCH_SIZE / WRITE_SIZE counter "
+                   help="also run a plain 4 GiB read and a plain 4 GiB write, whose FETCH_SIZE / WRITE_SIZE counter "
                         "readings calibrate the counters (for the --pmc runs that produce profiles/traffic.json)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="read the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE rocprofv3 run of "
@@ -122,9 +122,10 @@ def write_traffic(fetch_dir, write_dir):
         return hits[0]
 
     f_scale = CALIB_BYTES / 1024.0 / pick(fetch, "stream_read_kernel")
-    w_scale = CALIB_BYTES / 1024.0 / pick(write, "FillFunctor<c10::Half>")
+    w_scale = CALIB_BYTES / 1024.0 / pick(write, "stream_write_kernel")
     out = {"calibration": {"bytes": CALIB_BYTES, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-                           "note": "FETCH_SIZE scaled by a plain streaming read, WRITE_SIZE by a fill, same run"}}
+                           "note": "FETCH_SIZE scaled by a plain streaming read, WRITE_SIZE by a plain streaming "
+                                   "write, same run"}}
     for key, (sources, kernels) in TRAFFIC_KERNELS.items():
         fb = sum(pick(fetch, k) for k in kernels) * 1024.0 * f_scale
         wb = sum(pick(write, k) for k in kernels) * 1024.0 * w_scale
@@ -299,16 +300,18 @@ def small_config_measurements(kv, dev):
 
 
 def calibration_kernels(kv, dev):
-    """A plain read and a fill of CALIB_BYTES each (run under --pmc to calibrate the HBM counters)."""
+    """A plain read and a plain write of CALIB_BYTES each (run under --pmc to calibrate the HBM
+    counters): the library's streaming kernels, 16-byte words per lane, coalesced."""
     import ctypes
     buf = torch.empty(CALIB_BYTES // 2, dtype=torch.float16, device=dev)
     sink = torch.zeros(8192, dtype=torch.int32, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     for _ in range(3):
+        if kv.lib().kvattn_measure_stream_write(ctypes.c_void_p(buf.data_ptr()), CALIB_BYTES, 8192, stream) != 0:
+            raise RuntimeError("kvattn_measure_stream_write failed")
         if kv.lib().kvattn_measure_stream_read(ctypes.c_void_p(buf.data_ptr()), CALIB_BYTES, 8192,
                                                ctypes.c_void_p(sink.data_ptr()), stream) != 0:
             raise RuntimeError("kvattn_measure_stream_read failed")
-        buf.fill_(1.5)
     torch.cuda.synchronize()
     del buf, sink
     torch.cuda.empty_cache()

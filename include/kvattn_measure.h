@@ -32,6 +32,16 @@ extern "C" {
 int kvattn_measure_stream_read(const void *buf, size_t bytes, int workgroups, uint32_t *sink,
                                void *stream);
 
+/* Enqueue on `stream` one write of the `bytes` bytes at device address `buf`
+ * (bytes > 0 and a multiple of 16; buf 16-byte aligned) by `workgroups`
+ * workgroups of 256 threads, each lane storing whole 16-byte words with a grid
+ * stride (word j holds j, j ^ 0x55555555, j + 1 and ~j in its four uint32, j
+ * taken mod 2^32).  Plain coalesced stores, like the attention kernels' output
+ * and cache rows: the memory counters' reading for it calibrates their reading
+ * for those kernels.  Returns 0, KVATTN_ERR_INVALID_ARG (-1) for a bad
+ * argument, or KVATTN_ERR_HIP (-6) if the launch fails. */
+int kvattn_measure_stream_write(void *buf, size_t bytes, int workgroups, void *stream);
+
 /* Enqueue on `stream` a plain matrix-core loop: `workgroups` workgroups of four
  * waves, each wave running `iters` rounds of eight independent chains of
  * v_mfma_f32_16x16x32_f16 (fp16 inputs, fp32 accumulation) on register

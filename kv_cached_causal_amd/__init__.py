@@ -96,6 +96,7 @@ _SIGS = {
     "kvattn_measure_exp2_count": (ctypes.c_double, [ctypes.c_int, ctypes.c_int]),
     "kvattn_measure_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                                   ctypes.c_void_p]),
+    "kvattn_measure_stream_write": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]),
     "kvattn_measure_prefill_clock": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 4
                                      + [ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
                                         ctypes.c_void_p]),

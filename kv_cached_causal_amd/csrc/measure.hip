@@ -1,5 +1,6 @@
 // Measurement aids: a plain streaming-read kernel, used to report the HBM read
 // rate the device sustains next to the decode kernels' rate; a plain
+// streaming-write kernel, whose byte count calibrates the write counters; a plain
 // matrix-core loop, used to report the fp16 MFMA rate it sustains next to the
 // prefill kernel's rate; and a plain exp2 loop, used to report the rate of the
 // exponentials (one per score) that bound prefill at small head dims.
@@ -26,6 +27,21 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restric
     for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
+}
+
+// Writes n 16-byte words, each lane storing whole words with a grid stride
+// (plain coalesced stores, as the attention kernels' output and cache rows).
+__global__ __launch_bounds__(256) void stream_write_kernel(u32x4 *__restrict__ p, size_t n) {
+  constexpr int U = 4;
+  const size_t stride = (size_t)gridDim.x * 256 * U;
+  for (size_t i = (size_t)blockIdx.x * 256 * U + threadIdx.x; i < n; i += stride) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t j = i + (size_t)u * 256;
+      const uint32_t w = (uint32_t)j;
+      if (j < n) p[j] = u32x4{w, w ^ 0x55555555u, w + 1u, ~w};
+    }
+  }
 }
 
 // Each wave runs `iters` rounds of NCH independent accumulation chains of
@@ -95,6 +111,14 @@ extern "C" int kvattn_measure_mfma_f16(int workgroups, int iters, float *sink, v
 extern "C" double kvattn_measure_mfma_f16_flops(int workgroups, int iters) {
   if (workgroups <= 0 || iters <= 0) return 0.0;
   return (double)workgroups * 4 /* waves */ * iters * kvattn::kMfmaChains * (16.0 * 16.0 * 32.0 * 2.0);
+}
+
+extern "C" int kvattn_measure_stream_write(void *buf, size_t bytes, int workgroups, void *stream) {
+  if (!buf || bytes == 0 || bytes % 16 != 0 || ((uintptr_t)buf & 15u) != 0 || workgroups <= 0)
+    return KVATTN_ERR_INVALID_ARG;
+  kvattn::stream_write_kernel<<<dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream>>>(
+      (kvattn::u32x4 *)buf, bytes / 16);
+  return hipGetLastError() == hipSuccess ? KVATTN_OK : KVATTN_ERR_HIP;
 }
 
 extern "C" int kvattn_measure_stream_read(const void *buf, size_t bytes, int workgroups, uint32_t *sink,

@@ -150,6 +150,16 @@ def test_measure_stream_read_validates_on_host():
     assert lib.kvattn_measure_stream_read(fake, 1 << 20, 64, None, None) == -1
 
 
+def test_measure_stream_write_validates_on_host():
+    lib = kv.lib()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation first
+    assert lib.kvattn_measure_stream_write(None, 1 << 20, 64, None) == -1
+    assert lib.kvattn_measure_stream_write(fake, 0, 64, None) == -1
+    assert lib.kvattn_measure_stream_write(fake, 100, 64, None) == -1      # not a multiple of 16
+    assert lib.kvattn_measure_stream_write(ctypes.c_void_p((1 << 20) + 4), 1 << 20, 64, None) == -1
+    assert lib.kvattn_measure_stream_write(fake, 1 << 20, 0, None) == -1
+
+
 def test_extend_rejects_null_cache_without_a_device():
     lib = kv.lib()
     assert lib.kvattn_extend(None, 0, None, None, None, None, 4, 0.1, 1, None) == -1

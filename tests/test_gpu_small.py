@@ -292,3 +292,13 @@ def test_measurement_aids_run():
     torch.cuda.synchronize()
     assert int(sink_u.abs().sum()) == 0 and float(sink_f.abs().sum()) == 0.0
     assert lib.kvattn_measure_exp2_count(64, 50) == 64 * 256 * 50 * 32
+    # the streaming write: word j of a 16-byte-word buffer holds j, j ^ 0x55555555, j + 1, ~j
+    n_words = 3 * 64 * 256 * 4 + 37  # past a whole number of grid strides, with a ragged tail
+    wbuf = torch.zeros(n_words * 4 + 4, dtype=torch.int32, device="cuda")
+    say("measurement aid: stream write")
+    assert lib.kvattn_measure_stream_write(ctypes.c_void_p(wbuf.data_ptr()), n_words * 16, 64, stream) == 0
+    torch.cuda.synchronize()
+    got = wbuf.cpu().numpy().view(np.uint32)
+    j = np.arange(n_words, dtype=np.uint32)
+    want = np.stack([j, j ^ np.uint32(0x55555555), j + np.uint32(1), ~j], axis=1).reshape(-1)
+    assert np.array_equal(got[:4 * n_words], want) and got[4 * n_words:].tolist() == [0, 0, 0, 0]
