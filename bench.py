@@ -56,9 +56,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skip-gqa", action="store_true")
-    p.add_argument("--only", choices=["prefill", "decode", "gqa", "prefill_d32"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "gqa", "prefill_d32", "small"], default=None,
                    help="time one phase only (for profiling runs); prefill_d32: the 8-layer model's D=32 "
-                        "prompts at T=4096 and T=8192")
+                        "prompts at T=4096 and T=8192; small: the three small workloads")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the windowed, paged and extend measurements (profiling runs: their launches "
                         "share kernel names with the headline ones)")
@@ -88,10 +88,10 @@ PREFILL_SOURCES = ["prefill.hip", "common.hpp"]
 CALIB_BYTES = 4 << 30
 # kernels of each measured launch, by a substring of the demangled or mangled name
 TRAFFIC_KERNELS = {
-    "decode_ragged_b32": (DECODE_SOURCES, ["decode_kernel<kvattn::TagF16, 128, 1, 6, 1, 4, false, false, true>",
+    "decode_ragged_b32": (DECODE_SOURCES, ["decode_kernel<kvattn::TagF16, 128, 1, 6, 1, 4, false, false, true, false>",
                                            "decode_merge_kernel<128, 1, true>"]),
-    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4, 4, 1, 8, false, false, true>",
-                                        "decode_merge_kernel<128, 4, true>"]),
+    # 256 workgroups: the splits are merged inside the decode launch
+    "decode_gqa_b16": (DECODE_SOURCES, ["decode_kernel<kvattn::TagBF16, 128, 4, 4, 1, 8, false, false, true, true>"]),
     "prefill_t8192": (PREFILL_SOURCES, ["prefill_pipe_kernelIDF16_Li128"]),
 }
 
@@ -842,6 +842,10 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+    if args.only == "small":
+        res = {"metric": METRIC, "n_gpus": 1, "small_configs": small_config_measurements(kv, dev)}
+        print(json.dumps(res), flush=True)
+        return
     if args.only == "prefill_d32":
         # the D=32 prompts alone (profiling runs): T=4096 (split query tiles) and T=8192
         mceil, eceil = MFMA_F16_PEAK_TFLOPS * 0.968, 18.9e12  # nominal, for the bound columns only

@@ -61,8 +61,10 @@ struct DecodeArgs {
   const int32_t *slot_blocks = nullptr;  // paged: blocks assigned to each sequence [B] (device)
   // the fused decode step (append + decode, contiguous cache): the new rows
   // (B, Hkv, 1, D), writable views of the layer's K/V blocks and lengths, and
-  // per sequence kStepSlots ints: a counter that is zero between calls, and
-  // the attended count recorded for the merge kernel
+  // step_counter_ints(B, H) ints: per sequence kStepSlots (a counter that is
+  // zero between calls, and the attended count recorded for the merge
+  // kernel), then per (sequence, unit of query heads) a merge counter, zero
+  // between calls
   const void *k_new = nullptr, *v_new = nullptr;
   void *k_cache_rw = nullptr, *v_cache_rw = nullptr;
   int32_t *len_rw = nullptr;
@@ -71,6 +73,11 @@ struct DecodeArgs {
 
 // ints per sequence of the fused decode step's device record (counter, count)
 constexpr int kStepSlots = 2;
+inline size_t step_counter_ints(int batch, int q_heads) { return (size_t)batch * (kStepSlots + q_heads); }
+// fused decode steps over several splits whose grid has at most this many
+// workgroups (a fraction of one round on 256 CUs) merge the splits inside the
+// decode kernel: at that size a second launch costs more than it saves
+constexpr size_t kInKernelMergeMaxWorkgroups = 256;
 
 // Prompts whose per-sequence grid (query tiles x heads) fills between half
 // a round and one round of the pipelined prefill kernel (128 to 256

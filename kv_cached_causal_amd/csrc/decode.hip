@@ -115,6 +115,81 @@ __device__ inline int attended_keys(const DecodeArgs &a, int b, int len_in) {
   return min(len_in, cap);
 }
 
+// Log-sum-exp merge of the ns non-empty splits of one unit (sequence b, GT
+// query rows from h0): THREADS threads each own whole output elements.  Per
+// element the splits are folded in rounds of eight (their m, l and u loaded
+// together: one dependent round trip per round), in split order, so the
+// result does not depend on which workgroup runs it.  COHERENT: the partials
+// were written in the same launch by workgroups on other XCDs and are read
+// with device-scope loads.
+template <int D, int GT, int THREADS, bool COHERENT>
+__device__ void merge_unit(const DecodeArgs &a, int b, int h0, int ns) {
+  constexpr int SB = 8;  // splits per round of loads
+  const int RS = a.q_heads * a.tokens;
+  const float *ws_unit = a.ws + (size_t)(b * RS + h0) * a.n_splits * (D + 2);
+  auto ld = [](const float *p) -> float {
+    if constexpr (COHERENT)
+      return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      return *p;
+  };
+  // E elements per thread per pass, their loads issued together
+  constexpr int E = GT * D >= THREADS ? GT * D / THREADS : 1;
+  for (int t0 = 0; t0 < GT * D; t0 += E * THREADS) {
+    float M[E], num[E], den[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      M[e] = -INFINITY;
+      num[e] = 0.f;
+      den[e] = 0.f;
+    }
+    for (int s0 = 0; s0 < ns; s0 += SB) {
+      float ms[E][SB], ls[E][SB], us[E][SB];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        // elements past the unit's GT * D are clamped to its last (in bounds, never stored)
+        const int t = min(t0 + e * THREADS + (int)threadIdx.x, GT * D - 1);
+        const int g = t / D;
+        const int d = t - g * D;
+#pragma unroll
+        for (int i = 0; i < SB; ++i) {
+          // clamped (always in bounds) and masked below
+          const float *st = ws_unit + ((size_t)g * a.n_splits + min(s0 + i, ns - 1)) * (D + 2);
+          ms[e][i] = ld(st);
+          ls[e][i] = ld(st + 1);
+          us[e][i] = ld(st + 2 + d);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float mx = M[e];
+#pragma unroll
+        for (int i = 0; i < SB; ++i) mx = fmaxf(mx, s0 + i < ns ? ms[e][i] : -INFINITY);
+        // split 0 holds at least one visible key, so mx is finite from the first round on
+        const float f = fast_exp2(M[e] - mx);
+        num[e] *= f;
+        den[e] *= f;
+#pragma unroll
+        for (int i = 0; i < SB; ++i) {
+          const float w = s0 + i < ns ? fast_exp2(ms[e][i] - mx) : 0.f;
+          num[e] = fmaf(w, us[e][i], num[e]);
+          den[e] = fmaf(w, ls[e][i], den[e]);
+        }
+        M[e] = mx;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int t = t0 + e * THREADS + (int)threadIdx.x;
+      if (t < GT * D) {
+        const int g = t / D;
+        const int d = t - g * D;
+        store_out(a.o, (size_t)(b * RS + h0 + g) * D + d, num[e] / den[e], a.o_dt);
+      }
+    }
+  }
+}
+
 // grid (n_splits, Hkv * G/GT, B), 256 threads.  A workgroup owns one split of
 // `chunk` keys of one KV head, for GT query heads of its group.  LPR lanes
 // share one key row, each holding NV 16-byte slices of it (columns cl + v *
@@ -132,10 +207,17 @@ __device__ inline int attended_keys(const DecodeArgs &a, int b, int len_in) {
 // the cache.  This kernel only reads len[b]; the advanced length is written
 // after every workgroup of the sequence has read it: by the merge kernel
 // (from the attended count this kernel records) when the cache has several
-// splits, else by the last of the sequence's workgroups to count itself in
-// on an atomic counter.
-template <class Tag, int D, int GT, int U, int NV, int NW, bool PAGED, bool VER = false, bool FUSED = false>
+// splits and the grid is large, else by the last of the sequence's
+// workgroups to count itself in on an atomic counter.
+//
+// INM (with FUSED, for grids too small to fill the device, where a second
+// launch costs more than it saves): the splits are merged in this kernel by
+// the last of a unit's workgroups to finish, with the merge kernel's
+// arithmetic (merge_unit), so the result is the same bits either way.
+template <class Tag, int D, int GT, int U, int NV, int NW, bool PAGED, bool VER = false, bool FUSED = false,
+          bool INM = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
+  static_assert(!INM || (FUSED && !PAGED && !VER), "in-kernel merge: fused decode step only");
   constexpr int EPL = Tag::EPL;
   constexpr int LPR = D / (EPL * NV);  // lanes that share one key row
   constexpr int RPW = 64 / LPR;        // key rows per wave per load instruction
@@ -154,32 +236,46 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int kvh = unit / subs;
   const int h0 = kvh * RK + (unit - kvh * subs) * GT;  // first query row
   const int tid = threadIdx.x;
-  // splits run over the visible keys (all L, or the sink and window ones)
-  const int len_in = a.len[b];
+  // splits run over the visible keys (all L, or the sink and window ones).
+  // FUSED: one thread reads len[b] (the workgroup takes it from LDS), so
+  // that once that thread has counted the workgroup in below, no thread of
+  // it reads len[b] any more
+  __shared__ int s_len;
+  if constexpr (FUSED) {
+    if (tid == 0) s_len = a.len[b];
+    __syncthreads();
+  }
+  const int len_in = FUSED ? s_len : a.len[b];
   // FUSED: a full sequence is left as it is (cache, length, output); every
   // workgroup of the sequence reads the same len_in, so they all skip it
   const bool full = FUSED && len_in >= a.max_T;
   int32_t *const step_b = FUSED ? a.counters + (size_t)b * kStepSlots : nullptr;
-  // several splits: the attended count (or -1: skipped) for the merge kernel,
-  // which commits it as the new length
-  if (FUSED && a.n_splits > 1 && split == 0 && blockIdx.y == 0 && tid == 0) step_b[1] = full ? -1 : len_in + 1;
+  // several splits merged by the merge kernel: the attended count (or -1:
+  // skipped) for it, which commits it as the new length
+  if (FUSED && !INM && a.n_splits > 1 && split == 0 && blockIdx.y == 0 && tid == 0)
+    step_b[1] = full ? -1 : len_in + 1;
   if (full) return;
   const int L = FUSED ? len_in + 1 : attended_keys(a, b, len_in);
   if (L < 0) return;  // an extend past the sequence's capacity: skipped
-  const VisibleKeys vk = visible_keys(L, a.window, a.sink);
-  const int kb = split * a.chunk;  // first visible index of this split
-  if (kb >= vk.count) return;  // empty split (never with FUSED and a single split)
-  // one split: every workgroup of the sequence counts itself in (after its
-  // read of len[b]); the last one advances len[b] and clears the counter
+  // one split, or the in-kernel merge: every workgroup of the sequence
+  // (empty splits included) counts itself in after its read of len[b]; the
+  // last one advances len[b] and clears the counter
+  constexpr bool kCount = FUSED;
+  const bool counted = kCount && (INM || a.n_splits == 1);
   int len_ticket = 0;
-  if (FUSED && a.n_splits == 1 && tid == 0)
-    len_ticket = __hip_atomic_fetch_add(step_b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (counted && tid == 0) len_ticket = __hip_atomic_fetch_add(step_b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   auto finish_len = [&]() {
-    if (FUSED && a.n_splits == 1 && tid == 0 && len_ticket == (int)gridDim.y - 1) {
+    if (counted && tid == 0 && len_ticket == (int)(gridDim.x * gridDim.y) - 1) {
       __hip_atomic_store(step_b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       a.len_rw[b] = len_in + 1;
     }
   };
+  const VisibleKeys vk = visible_keys(L, a.window, a.sink);
+  const int kb = split * a.chunk;  // first visible index of this split
+  if (kb >= vk.count) {  // empty split (never with FUSED and a single split)
+    finish_len();
+    return;
+  }
   const int rows = min(a.chunk, vk.count - kb);
   const int n_valid = (vk.count + a.chunk - 1) / a.chunk;
   // FUSED: the split holding the last visible key holds the new row, which
@@ -453,6 +549,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   }
 
   // write this split's (m, l, u) for the GT heads; decode_merge combines them
+  // (INM: device-scope stores, written through to the level every XCD shares,
+  // then read back by this unit's last workgroup with device-scope loads)
+  auto put = [&](float *p, float x) {
+    if constexpr (INM)
+      __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *p = x;
+  };
   for (int t = tid; t < GT * D; t += NW * 64) {
     const int g = t / D;
     const int d = t - g * D;
@@ -470,11 +574,26 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       den = fmaf(al, s_l[w][g], den);
     }
     float *dst = a.ws + ((size_t)(b * RS + h0 + g) * a.n_splits + split) * (D + 2);
-    dst[2 + d] = num;
+    put(dst + 2 + d, num);
     if (d == 0) {
-      dst[0] = M;
-      dst[1] = den;
+      put(dst, M);
+      put(dst + 1, den);
     }
+  }
+  if constexpr (INM) {
+    // count this split in; the unit's last one to finish merges all of them
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    __shared__ int s_last;
+    if (tid == 0) {
+      int32_t *cu = a.counters + (size_t)a.batch * kStepSlots + (size_t)b * a.q_heads + unit;
+      const int last = __hip_atomic_fetch_add(cu, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_valid - 1;
+      if (last) __hip_atomic_store(cu, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (s_last) merge_unit<D, GT, NW * 64, true>(a, b, h0, n_valid);
+    finish_len();
   }
 }
 
@@ -510,11 +629,8 @@ constexpr int merge_threads() {
 template <int D, int GT, bool STEP = false>
 __global__ __launch_bounds__((merge_threads<D, GT>())) void decode_merge_kernel(DecodeArgs a) {
   constexpr int THREADS = merge_threads<D, GT>();
-  constexpr int E = GT * D / THREADS;  // outputs per thread
-  static_assert(E * THREADS == GT * D, "outputs split evenly");
-  constexpr int SB = 8;                // splits per round of loads
+  static_assert(GT * D % THREADS == 0, "outputs split evenly");
   const int b = blockIdx.y;
-  const int RS = a.q_heads * a.tokens;                 // query rows per sequence
   const int RK = (a.q_heads / a.kv_heads) * a.tokens;  // query rows per KV head
   const int subs = RK / GT;
   const int unit = blockIdx.x;
@@ -525,56 +641,7 @@ __global__ __launch_bounds__((merge_threads<D, GT>())) void decode_merge_kernel(
   if (STEP && unit == 0 && threadIdx.x == 0) a.len_rw[b] = L;
   const int ns = (visible_keys(L, a.window, a.sink).count + a.chunk - 1) / a.chunk;
   if (ns <= 1) return;
-  const float *ws_unit = a.ws + (size_t)(b * RS + h0) * a.n_splits * (D + 2);
-
-  float M[E], num[E], den[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    M[e] = -INFINITY;
-    num[e] = 0.f;
-    den[e] = 0.f;
-  }
-  for (int s0 = 0; s0 < ns; s0 += SB) {
-    float ms[E][SB], ls[E][SB], us[E][SB];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int t = e * THREADS + (int)threadIdx.x;
-      const int g = t / D;
-      const int d = t - g * D;
-#pragma unroll
-      for (int i = 0; i < SB; ++i) {
-        // clamped (always in bounds) and masked below
-        const float *st = ws_unit + ((size_t)g * a.n_splits + min(s0 + i, ns - 1)) * (D + 2);
-        ms[e][i] = st[0];
-        ls[e][i] = st[1];
-        us[e][i] = st[2 + d];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float mx = M[e];
-#pragma unroll
-      for (int i = 0; i < SB; ++i) mx = fmaxf(mx, s0 + i < ns ? ms[e][i] : -INFINITY);
-      // split 0 holds at least one visible key, so mx is finite from the first round on
-      const float f = fast_exp2(M[e] - mx);
-      num[e] *= f;
-      den[e] *= f;
-#pragma unroll
-      for (int i = 0; i < SB; ++i) {
-        const float w = s0 + i < ns ? fast_exp2(ms[e][i] - mx) : 0.f;
-        num[e] = fmaf(w, us[e][i], num[e]);
-        den[e] = fmaf(w, ls[e][i], den[e]);
-      }
-      M[e] = mx;
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int t = e * THREADS + (int)threadIdx.x;
-    const int g = t / D;
-    const int d = t - g * D;
-    store_out(a.o, (size_t)(b * RS + h0 + g) * D + d, num[e] / den[e], a.o_dt);
-  }
+  merge_unit<D, GT, THREADS, false>(a, b, h0, ns);
 }
 
 template <class Tag, int D, int GT, bool PAGED, bool VER>
@@ -607,7 +674,12 @@ static hipError_t launch_gt_step(const DecodeArgs &a, hipStream_t s) {
   constexpr int NV = 1, NW = GT >= 4 ? 8 : 4;
   constexpr int U = GT >= 4 ? 4 : 6;
   const int units = a.q_heads / GT;
-  decode_kernel<Tag, D, GT, U, NV, NW, false, false, true><<<dim3(a.n_splits, units, a.batch), NW * 64, 0, s>>>(a);
+  const dim3 grid(a.n_splits, units, a.batch);
+  if (a.n_splits > 1 && (size_t)a.n_splits * units * a.batch <= kInKernelMergeMaxWorkgroups) {
+    decode_kernel<Tag, D, GT, U, NV, NW, false, false, true, true><<<grid, NW * 64, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  decode_kernel<Tag, D, GT, U, NV, NW, false, false, true><<<grid, NW * 64, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
   decode_merge_kernel<D, GT, true><<<dim3(units, a.batch), merge_threads<D, GT>(), 0, s>>>(a);

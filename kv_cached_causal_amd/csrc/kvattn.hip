@@ -152,7 +152,7 @@ int kvattn_cache_alloc(kvattn_cache **out, int layers, int batch, int q_heads, i
   // split-K workspace for decode and for the short extends run on the decode
   // kernels (up to kMaxVerifyTokens query positions per head)
   const size_t ws_bytes = sizeof(float) * (size_t)batch * q_heads * kMaxVerifyTokens * c->n_splits * (head_dim + 2);
-  const size_t cnt_bytes = sizeof(int32_t) * (size_t)batch * kStepSlots;
+  const size_t cnt_bytes = sizeof(int32_t) * step_counter_ints(batch, q_heads);
   // prefill split of heavy query tiles: partials and counters for the
   // largest split any prompt up to max_T takes
   const int split_max = prefill_uses_split(dt, head_dim) ? prefill_split_tiles_max(max_T, q_heads) : 0;

@@ -1,9 +1,10 @@
 """The fused decode step (kvattn_append_decode): append + decode in one launch.
 
 The new K/V row of each sequence is stored into the cache bit for bit at
-position len[b] and attended from the registers it was loaded into; the
-splits are merged inside the launch and the length advanced by the last
-workgroup of each sequence.  Compared with the CPU oracle on seeded inputs:
+position len[b] and attended from the registers it was loaded into.  The
+splits are merged inside the launch when the grid is small (the last
+workgroup of a unit merges, the last of a sequence advances its length), else
+by a second launch that also commits the lengths; both give the same bits.  Compared with the CPU oracle on seeded inputs:
 small shapes over every dtype, head dim and head layout with lengths across
 split boundaries (stale slots NaN-poisoned, including the new row's slot),
 consecutive steps over several layers, windows, the host capacity check,
@@ -343,3 +344,49 @@ def test_batched_long_context_step(cfg):
         assert d <= 2e-3
         cp.close()
     free_gpu()
+
+
+def test_in_kernel_and_separate_merge_give_the_same_bits():
+    """One sequence stepped alone (88 workgroups: merged inside the decode
+    launch) and as sequence 0 of a batch of three (264 workgroups: merged by the
+    merge kernel) gives the same output bits, cache rows and lengths."""
+    kv = _kv()
+    dtype, D, H, max_T = "f16", 64, 8, 4000
+    scale = float(np.float32(1 / np.sqrt(D)))
+    lens = [3001, 2500, 3999 - 8]
+    hk = _rand((3, H, max_T, D), dtype, 41)
+    hv = _rand((3, H, max_T, D), dtype, 42)
+    outs, caches = [], []
+    for B in (1, 3):
+        say(f"merge paths: B={B}, 11 splits x {H} heads")
+        c = _poisoned_cache(kv, 1, B, H, H, D, max_T, dtype)
+        for b in range(B):
+            c.k_view(0)[b, :, :lens[b]] = to_dev(hk[b, :, :lens[b]], dtype)
+            c.v_view(0)[b, :, :lens[b]] = to_dev(hv[b, :, :lens[b]], dtype)
+        c.set_lengths(lens[:B])
+        steps = []
+        for t in range(3):
+            q = _rand((3, H, 1, D), dtype, 50 + t)[:B]
+            kn = _rand((3, H, 1, D), dtype, 60 + t)[:B]
+            vn = _rand((3, H, 1, D), dtype, 70 + t)[:B]
+            o = c.append_decode(0, to_dev(kn, dtype), to_dev(vn, dtype), to_dev(q, dtype), scale=scale,
+                                out_dtype=torch.float32)
+            steps.append(host_bits(o)[0].copy())
+        torch.cuda.synchronize()
+        assert c.lengths(0) == [n + 3 for n in lens[:B]]
+        outs.append(steps)
+        caches.append((host_bits(c.k_view(0))[0, :, :lens[0] + 3].copy(), host_bits(c.v_view(0))[0, :, :lens[0] + 3].copy()))
+        if B == 1:
+            # the first step also against the oracle
+            q0 = _rand((3, H, 1, D), dtype, 50)[:1]
+            kk = np.concatenate([hk[:1, :, :lens[0]], _rand((3, H, 1, D), dtype, 60)[:1]], axis=2)
+            vv = np.concatenate([hv[:1, :, :lens[0]], _rand((3, H, 1, D), dtype, 70)[:1]], axis=2)
+            ref = oracle.decode_cached(si.to_f64(q0[:, :, 0], dtype), si.to_f64(kk, dtype), si.to_f64(vv, dtype),
+                                       [lens[0] + 1], scale)
+            got = steps[0].view(np.float32).astype(np.float64).reshape(ref.shape)
+            assert np.abs(got - ref).max() <= 2e-3
+        c.close()
+        free_gpu()
+    for t in range(3):
+        assert np.array_equal(outs[0][t], outs[1][t]), f"step {t}: merge paths differ"
+    assert np.array_equal(caches[0][0], caches[1][0]) and np.array_equal(caches[0][1], caches[1][1])
