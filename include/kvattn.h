@@ -177,9 +177,11 @@ int kvattn_decode(kvattn_cache *c, int layer, const void *q, void *o, float scal
  * row included, within the layer's window and sink if set); o (B,H,1,D) in
  * o_dtype (cache dtype or F32); then len[b] += 1.  The result equals that of
  * the two calls.  The new row is taken from k_new/v_new for the attention and
- * stored into the cache by the same kernel; the splits of each sequence are
- * merged by log-sum-exp inside the launch, and the last of a sequence's
- * workgroups advances its length, so the call needs no host synchronisation
+ * stored into the cache by the same kernel.  The splits of each sequence are
+ * merged by log-sum-exp: inside the launch when its grid has at most 256
+ * workgroups (the last of a sequence's workgroups then advances its length),
+ * else by a second kernel on the same stream, which also advances the
+ * lengths; both give the same bits.  The call needs no host synchronisation
  * and may be captured in a HIP graph.  CAPACITY if any len[b] == max_T
  * (checked on the host against its copy of the lengths); on a replayed graph
  * a sequence found full on the device is left unchanged, cache, length and

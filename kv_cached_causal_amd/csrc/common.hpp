@@ -250,9 +250,13 @@ constexpr int kMaxSplits = 64;
 // 16 at 4096 keys, one decode step of 32 layers: 1.552 ms against 1.573 ms
 // for 1024-key splits of 4 waves; 768, 1088, 1366 and 4096 keys, 4 or 8
 // waves, measured slower, and so was starting each split's stream at a
-// rotated offset).
+// rotated offset).  At D = 32 a 768-key split is two batches of the
+// workgroup's loads, and contexts up to 6144 keys take at most eight splits
+// (one round of the merge's loads): the 8-layer, 16-head step at 4096-4224
+// keys took 61.8 us against 67.7 us with 512-key splits (nine splits), 68.0
+// with 1024 (three batches) and 71.5 with 1536.
 inline int decode_chunk(int head_dim, int group, int max_T) {
-  int c = head_dim <= 32 ? 512 : (group >= 4 ? 2048 : 384);
+  int c = head_dim <= 32 ? 768 : (group >= 4 ? 2048 : 384);
   while ((max_T + c - 1) / c > kMaxSplits) c *= 2;
   return c;
 }

@@ -35,8 +35,8 @@ def _rand(shape, dtype, seed):
 
 HEADS = [(4, 4), (4, 2), (4, 1), (8, 1), (12, 4), (6, 2), (10, 2), (14, 2), (16, 1)]
 # lengths before the step (the query then sees len + 1 keys): empty, one key,
-# and around the 384-, 512-, 1024- and 2048-key split sizes
-LENS_BEFORE = [0, 1, 383, 384, 511, 1023, 1024, 2047, 2048]
+# and around the 384-, 768-, 1024- and 2048-key split sizes and their multiples
+LENS_BEFORE = [0, 1, 383, 384, 767, 768, 1023, 1024, 1535, 2047, 2048]
 
 
 def _poisoned_cache(kv, layers, B, H, Hkv, D, max_T, dtype):
