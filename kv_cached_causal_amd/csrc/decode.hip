@@ -260,8 +260,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // one split, or the in-kernel merge: every workgroup of the sequence
   // (empty splits included) counts itself in after its read of len[b]; the
   // last one advances len[b] and clears the counter
-  constexpr bool kCount = FUSED;
-  const bool counted = kCount && (INM || a.n_splits == 1);
+  const bool counted = FUSED && (INM || a.n_splits == 1);
   int len_ticket = 0;
   if (counted && tid == 0) len_ticket = __hip_atomic_fetch_add(step_b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   auto finish_len = [&]() {
