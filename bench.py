@@ -56,9 +56,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skip-gqa", action="store_true")
-    p.add_argument("--only", choices=["prefill", "decode", "gqa", "prefill_d32", "small"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "gqa", "prefill_d32", "small", "sweep"], default=None,
                    help="time one phase only (for profiling runs); prefill_d32: the 8-layer model's D=32 "
-                        "prompts at T=4096 and T=8192; small: the three small workloads")
+                        "prompts at T=4096 and T=8192; small: the three small workloads; sweep: B=1 fp16 "
+                        "prefill per layer at T = 512 ... 16384 for 16 heads of D=32 and 32 heads of D=128")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the windowed, paged and extend measurements (profiling runs: their launches "
                         "share kernel names with the headline ones)")
@@ -207,11 +208,10 @@ def measure_exp_ceiling(kv, dev, workgroups=4096, iters=5000, reps=5):
     return n / (a.elapsed_time(b) / reps * 1e-3)
 
 
-def small_head_prefill(kv, dev, mceil, eceil, reps=20, T=8192):
-    """The 8-layer x 512-wide model's attention prefill at T (B=1, 16 heads of D=32, fp16):
-    per-launch time against the MFMA peak and against the exponential ceiling (one exp2 per
-    unmasked score: at D=32 a score costs only 128 MFMA flops)."""
-    H, D = 16, 32
+def small_head_prefill(kv, dev, mceil, eceil, reps=20, T=8192, H=16, D=32):
+    """The 8-layer x 512-wide model's attention prefill at T (B=1, 16 heads of D=32, fp16; other
+    head counts and dims for the sweep): per-launch time against the MFMA peak and against the
+    exponential ceiling (one exp2 per unmasked score: at D=32 a score costs only 128 MFMA flops)."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(32)
     dt = torch.float16
@@ -235,7 +235,8 @@ def small_head_prefill(kv, dev, mceil, eceil, reps=20, T=8192):
     med = statistics.median(times) * 1e-3
     flops = 4.0 * H * D * T * (T + 1) / 2
     exps = H * T * (T + 1) / 2
-    return {"workload": f"T={T} causal prefill, B=1, H=16, D=32, fp16 (the 8L x 512d model's attention)",
+    what = " (the 8L x 512d model's attention)" if (H, D) == (16, 32) else ""
+    return {"workload": f"T={T} causal prefill, B=1, H={H}, D={D}, fp16{what}",
             "us_per_layer": round(med * 1e6, 1), "value": round(flops / med / 1e12, 1), "unit": "TFLOP/s",
             "frac_of_mfma_peak": round(flops / med / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
             "mfma_bound_us": round(flops / (mceil * 1e12) * 1e6, 1),
@@ -842,6 +843,17 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+    if args.only == "sweep":
+        mceil, eceil = MFMA_F16_PEAK_TFLOPS * 0.968, 18.9e12  # nominal, for the bound columns only
+        rows = []
+        for H, D in ((16, 32), (32, 128)):
+            for T in (512, 1024, 2048, 4096, 8192, 16384):
+                r = small_head_prefill(kv, dev, mceil, eceil, reps=args.steps, T=T, H=H, D=D)
+                rows.append({"H": H, "D": D, "T": T, "us_per_layer": r["us_per_layer"], "tflops": r["value"],
+                             "frac_of_mfma_peak": r["frac_of_mfma_peak"]})
+                log(f"sweep H={H} D={D} T={T}: {r['us_per_layer']} us, {r['value']} TFLOP/s")
+        print(json.dumps({"metric": METRIC, "n_gpus": 1, "steps": args.steps, "prefill_sweep": rows}), flush=True)
+        return
     if args.only == "small":
         res = {"metric": METRIC, "n_gpus": 1, "small_configs": small_config_measurements(kv, dev)}
         print(json.dumps(res), flush=True)
